@@ -1,0 +1,113 @@
+"""CPU oracle for the Mamba-2 SSD scan and single-token step.
+
+TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check and the benchmark's CPU
+baseline leg may import this package.  The GPU library neither imports nor
+links anything here, and nothing here imports the GPU library.
+
+Contents
+  scan(...)         token-by-token fp64 recurrence (C, OpenMP over (b, h))
+  step(...)         the same recurrence run for one token from a given state
+  dual_form.py      dense quadratic "dual form" materialisation (numpy, fp64)
+  chunked.py        chunked SSD algorithm written step by step (numpy, fp64)
+  brute.py          the recurrence at 50 significant digits (mpmath)
+
+The source is "Compiler-First State Space Duality and Portable O(1)
+Autoregressive Caching" (Background, Eq. 1-3; SSD properties; O(1) cache).
+The recurrence is what the chunked method computes faster; the other three are
+independent formulations used to pin it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        path = _build.build(force=False)
+        lib = ctypes.CDLL(path)
+        lib.ssd_oracle_scan.restype = ctypes.c_int
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.ssd_oracle_scan.argtypes = [i64] * 6 + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
+                                                           ctypes.c_double, vp, vp, ctypes.c_int]
+        lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().ssd_oracle_max_threads())
+
+
+def _f32(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor: exact upcast (bf16 -> f32 is exact)
+        import torch
+        a = a.detach().to("cpu", torch.float32).contiguous().numpy()
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _f64(a) -> Optional[np.ndarray]:
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        import torch
+        a = a.detach().to("cpu", torch.float64).contiguous().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, dt_softplus: bool = True,
+         dt_min: float = 1e-4, dt_max: float = 0.5, nthreads: int = 0
+         ) -> Tuple[np.ndarray, np.ndarray]:
+    """Run the fp64 token-by-token recurrence.
+
+    Shapes: x [Bt,T,H,P], dt [Bt,T,H], A/D/dt_bias [H], B/C [Bt,T,G,N],
+    h0 [Bt,H,P,N] (None means zeros).  Float inputs are taken as float32
+    values (bf16 tensors upcast exactly); h0 is taken in float64.
+    dt_min/dt_max are compared in double against d, after rounding them to
+    float32 as the C-ABI receives them.
+    Returns (y [Bt,T,H,P], final_state [Bt,H,P,N]), both float64.
+    """
+    x, dt, A, B, C = _f32(x), _f32(dt), _f32(A), _f32(B), _f32(C)
+    D, dt_bias, h0 = _f32(D), _f32(dt_bias), _f64(h0)
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dt.shape == (Bt, T, H) and A.shape == (H,)
+    assert B.shape == (Bt, T, G, N) and C.shape == (Bt, T, G, N)
+    assert D is None or D.shape == (H,)
+    assert dt_bias is None or dt_bias.shape == (H,)
+    assert h0 is None or h0.shape == (Bt, H, P, N)
+    y = np.empty((Bt, T, H, P), dtype=np.float64)
+    fin = np.empty((Bt, H, P, N), dtype=np.float64)
+    lo = float(np.float32(dt_min))
+    hi = float(np.float32(dt_max))
+    rc = _load().ssd_oracle_scan(Bt, T, H, P, N, G, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                 _ptr(B), _ptr(C), _ptr(D), _ptr(h0), int(bool(dt_softplus)),
+                                 lo, hi, _ptr(y), _ptr(fin), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_scan failed with code {rc}")
+    return y, fin
+
+
+def step(state, x_t, dt_t, A, B_t, C_t, D=None, dt_bias=None, *, dt_softplus: bool = True,
+         dt_min: float = 1e-4, dt_max: float = 0.5) -> Tuple[np.ndarray, np.ndarray]:
+    """One recurrence step: state [Bt,H,P,N], x_t [Bt,H,P], dt_t [Bt,H],
+    B_t/C_t [Bt,G,N].  Returns (y_t [Bt,H,P], new_state), both float64."""
+    x_t, dt_t, B_t, C_t = _f32(x_t), _f32(dt_t), _f32(B_t), _f32(C_t)
+    y, fin = scan(x_t[:, None], dt_t[:, None], A, B_t[:, None], C_t[:, None], D, dt_bias,
+                  state, dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max)
+    return y[:, 0], fin

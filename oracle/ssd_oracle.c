@@ -1,0 +1,118 @@
+/*
+ * CPU oracle for the Mamba-2 SSD scan: the token-by-token recurrence in fp64.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, includes or calls it, and it shares no code with the GPU library.
+ *
+ * What it computes ("Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching", Background, Eq. 1 and Eq. 2, and the O(1) cache
+ * section): a diagonal-per-head discrete SSM whose input matrix B, output
+ * matrix C and step size Delta depend on the token (Mamba-2 selectivity, same
+ * section), run one token at a time:
+ *
+ *   z_t   = dt[b,t,h] + dt_bias[h]
+ *   d_t   = clip(softplus(z_t), dt_min, dt_max)   (softplus optional)
+ *   abar  = exp(d_t * A[h])                         (A[h] < 0, scalar per head)
+ *   h_t[p,n] = abar * h_{t-1}[p,n] + d_t * x[b,t,h,p] * B[b,t,g,n]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] * h_t[p,n] + D[h] * x[b,t,h,p]
+ *
+ * with g = h / (H/G) the B/C group of head h and h_{-1} = h0 (or zeros).
+ * The page states zero-order-hold discretisation but its equation was lost;
+ * the reading taken here is Abar = exp(Delta*A) and Bbar = Delta*B, the form
+ * whose unrolled kernel is the decay-only lower-triangular matrix of the dual
+ * form (Eq. 3 and the "diagonal state matrix" property).
+ *
+ * Every input is a float32 array (bfloat16 inputs are upcast exactly before
+ * the call); every operation is carried out in double.  Layouts are dense,
+ * row-major: x,y [Bt,T,H,P]; dt [Bt,T,H]; A, D, dt_bias [H];
+ * B, C [Bt,T,G,N]; h0, final [Bt,H,P,N].
+ *
+ * Independent (b,h) pairs run in parallel with OpenMP; each pair runs serially
+ * in token order, so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double softplus_exact(double z) {
+  /* log(1 + e^z) written so that neither branch overflows */
+  return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+}
+
+int ssd_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Returns 0 on success, 1 on a bad argument, 2 when scratch allocation fails. */
+int ssd_oracle_scan(int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
+                    const float* x, const float* dt, const float* dt_bias,
+                    const float* A, const float* Bm, const float* Cm, const float* D,
+                    const double* h0, int dt_softplus, double dt_min, double dt_max,
+                    double* y, double* final_state, int nthreads) {
+  if (Bt < 0 || T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return 1;
+  if (!A || (T > 0 && (!x || !dt || !Bm || !Cm || !y))) return 1;
+  const int64_t heads_per_group = H / G;
+  const int64_t npairs = Bt * H;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double* S = (double*)malloc(sizeof(double) * (size_t)(P * N));
+    if (!S) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int64_t pair = 0; pair < npairs; ++pair) {
+      if (!S) continue;
+      const int64_t b = pair / H, h = pair % H, g = h / heads_per_group;
+      if (h0)
+        memcpy(S, h0 + (size_t)((b * H + h) * P * N), sizeof(double) * (size_t)(P * N));
+      else
+        memset(S, 0, sizeof(double) * (size_t)(P * N));
+      const double Ah = (double)A[h];
+      const double Dh = D ? (double)D[h] : 0.0;
+      const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        double z = (double)dt[(b * T + t) * H + h] + bias;
+        double d = dt_softplus ? softplus_exact(z) : z;
+        if (d < dt_min) d = dt_min;
+        if (d > dt_max) d = dt_max;
+        const double abar = exp(d * Ah);
+        const float* xt = x + (size_t)(((b * T + t) * H + h) * P);
+        const float* Bt_ = Bm + (size_t)(((b * T + t) * G + g) * N);
+        const float* Ct_ = Cm + (size_t)(((b * T + t) * G + g) * N);
+        double* yt = y + (size_t)(((b * T + t) * H + h) * P);
+        for (int64_t p = 0; p < P; ++p) {
+          const double dx = d * (double)xt[p];
+          double* Sp = S + p * N;
+          double acc = 0.0;
+          for (int64_t n = 0; n < N; ++n) {
+            Sp[n] = abar * Sp[n] + dx * (double)Bt_[n];
+            acc += (double)Ct_[n] * Sp[n];
+          }
+          yt[p] = acc + Dh * (double)xt[p];
+        }
+      }
+      if (final_state)
+        memcpy(final_state + (size_t)((b * H + h) * P * N), S, sizeof(double) * (size_t)(P * N));
+    }
+    free(S);
+  }
+  return failed ? 2 : 0;
+}
