@@ -1,0 +1,287 @@
+"""Benchmark of the MI355X SSD library: chunked-scan prefill and cached decode.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                [--decode-batch B] [--no-cpu-baseline]
+
+One step is one ssd_chunk_scan over the workload's whole batch (the prefill
+path: Delta preparation, per-chunk prefix sum, decay matrix, C B^T, the
+intra-chunk product, chunk states, the inter-chunk recurrence and the
+state-to-output term).  The cached-decode path (ssd_step) is timed in the same
+run and reported in the "decode" object.  Inputs are seeded synthetic
+activations resident in device memory before timing starts; K steps are
+timed between two device synchronisations.  Input/output sets are rotated so
+that their total exceeds the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  Algorithmic work counts (what the method must do: the
+causal half of each L x L block, C B^T once per group):
+  FLOP/token = H[(L+1)P + 4NP + 2PN/L] + G(L+1)N
+  decode bytes/token = 8HPN (state read + write) + HP(s_x + s_y) + 4H + 2GN s_BC
+Peaks are MI355X's published dense figures (fp32 MFMA 157.3 TFLOP/s, bf16
+2.5 PFLOP/s, HBM3E 8 TB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("SSD prefill tokens/s (% MFMA peak); cached decode tokens/s (% HBM GB/s peak)")
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "m130_f32"
+
+
+def prefill_flops_per_token(w):
+    H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    return H * ((L + 1) * P + 4 * N * P + 2 * P * N / L) + G * (L + 1) * N
+
+
+def phase_flops_per_token(w):
+    """Algorithmic FLOP/token of each kernel of the scan."""
+    H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    return {
+        "chunk_state": H * 2 * N * P,                                   # chunk summary states
+        "state_pass": H * 2 * P * N / L,                                # inter-chunk recurrence
+        "chunk_out": H * ((L + 1) * P + 2 * N * P) + G * (L + 1) * N,   # decay, C B^T, products
+    }
+
+
+def prefill_bytes_per_token(w, T):
+    s = 2 if w.io_dtype == "bf16" else 4
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    return H * P * (s + s) + 4 * H + 2 * G * N * s + 4 * H * P * N / T
+
+
+def decode_bytes_per_token(H, P, N, G, s):
+    return 8 * H * P * N + H * P * 2 * s + 4 * H + 2 * G * N * s
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def bench_prefill(ssd, torch, w, steps, warmup):
+    from ssd_inputs import make_inputs
+    inp = make_inputs(w)
+    dev = torch.device("cuda")
+    shared = {k: inp[k].to(dev) for k in ("A", "D", "dt_bias")}
+    Bt, T, H, P = inp["x"].shape
+    N = inp["B"].shape[3]
+    x0 = inp["x"].to(dev)
+    B0 = inp["B"].to(dev)
+    ws_bytes = ssd.ssd_chunk_scan_workspace_bytes(x0, B0, w.chunk)
+    es = x0.element_size()
+    set_bytes = (2 * x0.numel() * es + inp["dt"].numel() * 4 + 2 * B0.numel() * es
+                 + Bt * H * P * N * 4 + ws_bytes)
+    nsets = max(1, min(16, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for _ in range(nsets):
+        s = {"x": x0.clone(), "dt": inp["dt"].to(dev), "B": B0.clone(), "C": inp["C"].to(dev),
+             "y": torch.empty_like(x0),
+             "fin": torch.empty(Bt, H, P, N, device=dev, dtype=torch.float32),
+             "ws": torch.empty(ws_bytes, device=dev, dtype=torch.uint8)}
+        sets.append(s)
+
+    def run(i, events=None):
+        s = sets[i % nsets]
+        ssd.ssd_chunk_scan(s["x"], s["dt"], shared["A"], s["B"], s["C"], shared["D"],
+                           chunk=w.chunk, dt_bias=shared["dt_bias"], dt_limit=(w.dt_min, w.dt_max),
+                           y=s["y"], final_state=s["fin"], workspace=s["ws"], phase_events=events)
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    # per-kernel durations, HIP events on the stream the kernels run on
+    nph = ssd.SSD_SCAN_PHASES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(steps)]
+    for i in range(steps):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    names = ["chunk_state", "state_pass", "chunk_out"]
+    phase_ms = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
+                for k, n in enumerate(names)}
+    return {"ms": ms, "wall_ms": wall * 1e3 / steps, "phase_ms": phase_ms, "nsets": nsets,
+            "set_bytes": set_bytes, "tokens": Bt * T}
+
+
+def bench_decode(ssd, torch, batch, steps_n, warmup):
+    """2.7B-shaped decode (H=80, P=64, N=128, bf16 x/B/C, fp32 state): steps
+    captured in one HIP graph; states rotated over >= 512 MB (one state per
+    layer-like buffer) so that the state streams from HBM, not the cache."""
+    from ssd_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["m2p7_decode"].with_(batch=batch, seqlen=steps_n)
+    inp = make_inputs(w)
+    dev = torch.device("cuda")
+    H, P, N, G = w.nheads, w.headdim, w.dstate, w.ngroups
+    xs = inp["x"].transpose(0, 1).contiguous().to(dev)     # [steps, b, H, P]
+    dts = inp["dt"].transpose(0, 1).contiguous().to(dev)   # [steps, b, H]
+    Bs = inp["B"].transpose(0, 1).contiguous().to(dev)     # [steps, b, G, N]
+    Cs = inp["C"].transpose(0, 1).contiguous().to(dev)
+    A, D, bias = inp["A"].to(dev), inp["D"].to(dev), inp["dt_bias"].to(dev)
+    state_bytes = batch * H * P * N * 4
+    nstates = max(1, math.ceil(2 * MALL_BYTES / state_bytes))
+    states = [torch.randn(batch, H, P, N, device=dev) * 0.1 for _ in range(nstates)]
+    ys = torch.empty(steps_n, batch, H, P, device=dev, dtype=xs.dtype)
+
+    def body():
+        for t in range(steps_n):
+            ssd.ssd_step(states[t % nstates], xs[t], dts[t], A, Bs[t], Cs[t], D, dt_bias=bias,
+                         y_t=ys[t])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(max(1, warmup)):
+            body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (reps * steps_n)
+    s_io = xs.element_size()
+    bpt = decode_bytes_per_token(H, P, N, G, s_io)
+    achieved = bpt * batch / (ms_step * 1e-3) / 1e9
+    return {"batch": batch, "steps": steps_n, "graph_replays": reps, "ms_per_step": ms_step,
+            "tokens_per_s": batch / (ms_step * 1e-3), "state_buffers": nstates,
+            "state_bytes_each": state_bytes,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+            "bytes_per_token": bpt}
+
+
+def cpu_baseline(w, target_s=10.0):
+    """The fp64 oracle on the host cores, on a bounded sample of the workload."""
+    import oracle
+    from ssd_inputs import make_inputs
+    threads = oracle.max_threads()
+    inp = make_inputs(w)
+    Bt, H = w.batch, w.nheads
+    pairs_full = Bt * H
+    # sample: batch row 0, the first k heads (k = all heads if they fit ~2 rounds of threads)
+    k = H if (Bt == 1 and H <= 4 * threads) else min(H, 2 * threads)
+    sl = {kk: v for kk, v in inp.items()}
+    if k < H or Bt > 1:
+        sl = {"x": inp["x"][:1, :, :k], "dt": inp["dt"][:1, :, :k], "A": inp["A"][:k],
+              "B": inp["B"][:1], "C": inp["C"][:1], "D": inp["D"][:k], "dt_bias": inp["dt_bias"][:k]}
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        oracle.scan(sl["x"], sl["dt"], sl["A"], sl["B"], sl["C"], sl["D"], sl["dt_bias"], None,
+                    dt_min=w.dt_min, dt_max=w.dt_max)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el * (reps + 1) / reps > 3 * target_s:
+            break
+    per_rep = el / reps
+    scale = pairs_full / k          # the full workload has this many times the (b, h) pairs
+    full_s = per_rep * scale
+    return {"value": Bt * w.seqlen / full_s, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"fp64 recurrence on {k} of {pairs_full} (batch, head) sequences of "
+                       f"{w.seqlen} tokens, {reps} repetition(s) in {el:.1f} s, scaled by "
+                       f"{scale:g} to the whole workload; host CPU: {cpu_model()}")}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(batch and heads shard with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import state_space_model_amd as ssd
+    from ssd_inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    if args.chunk:
+        w = w.with_(chunk=args.chunk)
+    print(f"[bench] prefill {w.name} L={w.chunk} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    pf = bench_prefill(ssd, torch, w, args.steps, args.warmup)
+    tokens_s = pf["tokens"] / (pf["ms"] * 1e-3)
+    fpt = prefill_flops_per_token(w)
+    per = phase_flops_per_token(w)
+    dom = max(pf["phase_ms"], key=pf["phase_ms"].get)
+    dom_flops = per[dom] * pf["tokens"]
+    dom_ms = pf["phase_ms"][dom]
+    peak = PEAK_TFLOPS[w.io_dtype]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": pf["ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.io_dtype, "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk, "io_dtype": w.io_dtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "flops_per_launch": dom_flops, "avg_launch_ms": dom_ms},
+        "prefill": {"algorithmic_tflops": fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12,
+                    "mfma_peak_frac": fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12 / peak,
+                    "flops_per_token": fpt,
+                    "bytes_per_token": prefill_bytes_per_token(w, w.seqlen),
+                    "hbm_gbs_algorithmic": prefill_bytes_per_token(w, w.seqlen) * tokens_s / 1e9,
+                    "phase_ms": pf["phase_ms"], "wall_ms_per_step": pf["wall_ms"],
+                    "rotated_sets": pf["nsets"]},
+    }
+    if not args.no_decode:
+        print(f"[bench] decode b={args.decode_batch} steps={args.decode_steps}", file=sys.stderr,
+              flush=True)
+        out["decode"] = bench_decode(ssd, torch, args.decode_batch, args.decode_steps,
+                                     args.warmup)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

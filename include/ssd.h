@@ -1,0 +1,184 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD library (libssd.so).
+ *
+ * Two operations, following "Compiler-First State Space Duality and Portable
+ * O(1) Autoregressive Caching" (arXiv 2603.09555):
+ *
+ *   ssd_chunk_scan  the chunked state-space-duality scan over a whole
+ *                   sequence (prefill): Background, Eq. 3 and the inter-chunk
+ *                   recurrence described after it; SSD properties "diagonal
+ *                   state matrix", "chunked recurrence", "static control flow".
+ *   ssd_step        one token of the recurrence from a fixed-size state held
+ *                   on the device (decode): the O(1) cache section.
+ *
+ * Both compute, for every batch row b and head h (g = h / (H/G) is the B/C
+ * group of head h), the selective diagonal SSM
+ *
+ *   d_t      = clip(softplus(dt[b,t,h] + dt_bias[h]), dt_min, dt_max)
+ *              (softplus skipped when dt_softplus == 0; dt_bias NULL -> 0)
+ *   h_t[p,n] = exp(d_t * A[h]) * h_{t-1}[p,n] + d_t * x[b,t,h,p] * B[b,t,g,n]
+ *   y[b,t,h,p] = sum_n C[b,t,g,n] * h_t[p,n] + D[h] * x[b,t,h,p]
+ *
+ * i.e. Abar = exp(Delta*A), Bbar = Delta*B (Background, Eq. 2; the page names
+ * zero-order hold but its equation is lost, and this is the form whose
+ * unrolled kernel is the decay-only lower-triangular matrix of Eq. 3).
+ * A[h] is the (negative) decay itself, not its logarithm: a caller holding
+ * log-space decay parameters (Implementation, precision management) passes
+ * -exp(A_log) computed in float32.
+ *
+ * Conventions shared by every call
+ *  - Pointers are DEVICE pointers (hipMalloc'd or equivalent) except the
+ *    descriptor, which is a host pointer read during the call only.
+ *  - Tensors are dense, contiguous, row-major, in the layouts listed per call.
+ *    x, B, C, y and every state (and the workspace) must be 16-byte aligned;
+ *    dt, dt_bias, A and D 4-byte aligned.
+ *  - x, B, C and y share one dtype (desc->io_dtype: SSD_F32 or SSD_BF16);
+ *    dt, dt_bias, A, D and every state are float32.  All arithmetic inside is
+ *    float32 (decay, exponentials, states, accumulation); bfloat16 appears
+ *    only as matrix-core operands and at the output store (round to nearest
+ *    even).
+ *  - The caller owns every buffer, including the workspace.  The library never
+ *    allocates, frees or synchronises; calls are asynchronous on `stream`
+ *    (0 = the null stream) and results are valid once the stream has reached
+ *    them.  The library keeps no mutable global state.
+ *  - Errors: arguments are validated before anything is launched; on any error
+ *    other than SSD_ERR_HIP nothing has been written.  SSD_ERR_HIP means a
+ *    launch failed (hipGetLastError); outputs are then undefined.  No C++
+ *    exception crosses this interface.
+ *  - Shapes supported by the compiled gfx950 kernels: headdim P in
+ *    {16, 32, 64, 128}, dstate N in {16, 32, 64, 128} (N = 16 with float32
+ *    io only), chunk L a multiple of 32 in [32, 512] with P*L <= 32768
+ *    (ssd_step: the same P, and N for either dtype).  Other positive shapes
+ *    return SSD_ERR_UNSUPPORTED.  seqlen need not be a multiple of the
+ *    chunk: the last chunk may be shorter.  batch == 0 or seqlen == 0 is valid.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1, /* NULL required pointer, NaN/inverted dt limits, aliasing */
+  SSD_ERR_SHAPE = 2,       /* non-positive size, heads not a multiple of groups */
+  SSD_ERR_DTYPE = 3,       /* io_dtype not one of ssd_dtype */
+  SSD_ERR_ALIGNMENT = 4,   /* a device pointer below its required alignment */
+  SSD_ERR_UNSUPPORTED = 5, /* valid shape without a compiled gfx950 variant */
+  SSD_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than the query returned */
+  SSD_ERR_HIP = 7          /* a HIP launch failed */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Problem description of a chunked scan (prefill). */
+typedef struct {
+  int64_t batch;     /* Bt >= 0 */
+  int64_t seqlen;    /* T >= 0 */
+  int64_t nheads;    /* H >= 1, a multiple of ngroups */
+  int64_t headdim;   /* P */
+  int64_t dstate;    /* N */
+  int64_t ngroups;   /* G >= 1: heads h share B/C group h / (H/G) */
+  int64_t chunk;     /* L: tokens per chunk of the dual form */
+  int32_t io_dtype;  /* ssd_dtype of x, B, C and y */
+  int32_t dt_softplus; /* 1: d = softplus(dt + dt_bias) before clipping; 0: d = dt + dt_bias */
+  float dt_min, dt_max; /* clip limits of d, dt_min <= dt_max (e.g. 1e-4 and 0.5) */
+} ssd_scan_desc;
+
+/* Problem description of one decode step. */
+typedef struct {
+  int64_t batch, nheads, headdim, dstate, ngroups;
+  int32_t io_dtype;
+  int32_t dt_softplus;
+  float dt_min, dt_max;
+} ssd_step_desc;
+
+/*
+ * Workspace bytes ssd_chunk_scan needs for `desc` (0 if desc is invalid).
+ * It holds one float32 P x N state per (batch, head, chunk) plus one float32
+ * decay per (batch, head, chunk): about 4*Bt*H*ceil(T/L)*(P*N+1) bytes.
+ */
+size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc);
+
+/*
+ * Chunked SSD scan over a whole sequence (prefill).
+ *
+ * Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
+ * Caching", Background (Eq. 3: within a chunk of L tokens, y = (L o C B^T) X
+ * with L the lower-triangular matrix of exponentiated segment sums of A*Delta;
+ * across chunks, a sequential recurrence over chunk summary states) and the
+ * O(1) cache section (prefill hands its final state to the decode cache).
+ *
+ *   x   [Bt,T,H,P] io_dtype     dt  [Bt,T,H] f32 (pre-activation)
+ *   A   [H] f32 (A < 0)         dt_bias [H] f32 or NULL
+ *   B,C [Bt,T,G,N] io_dtype     D   [H] f32 or NULL (no skip term)
+ *   initial_state [Bt,H,P,N] f32 or NULL (zeros)
+ *   y   [Bt,T,H,P] io_dtype (written)
+ *   final_state [Bt,H,P,N] f32 (written) or NULL (not returned)
+ *   workspace: device buffer of at least ssd_chunk_scan_workspace_bytes(desc)
+ *
+ * y and final_state must not overlap any input or each other.  The result does
+ * not depend on the run (no atomics in any reduction): repeated calls on the
+ * same inputs are bitwise identical.
+ */
+ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float* dt,
+                          const float* dt_bias, const float* A, const void* B, const void* C,
+                          const float* D, const float* initial_state, void* y,
+                          float* final_state, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
+ * ssd_chunk_scan with timing instrumentation: when `phase_events` is not NULL
+ * it must hold `n_events` created HIP events; event k is recorded on `stream`
+ * before phase k and event n_phases after the last one (n_phases =
+ * SSD_SCAN_PHASES).  Used by the benchmark to time each kernel of the scan on
+ * the stream it runs on.  n_events < SSD_SCAN_PHASES + 1 is SSD_ERR_INVALID_ARG.
+ * Phases: 0 chunk states, 1 state passing, 2 chunk outputs.
+ */
+#define SSD_SCAN_PHASES 3
+ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const float* dt,
+                                const float* dt_bias, const float* A, const void* B,
+                                const void* C, const float* D, const float* initial_state,
+                                void* y, float* final_state, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* phase_events, int n_events);
+
+/*
+ * One decode step of the recurrence, the state updated in place.
+ *
+ * Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
+ * Caching", O(1) cache section: the fixed-size state (B,H,P,N) summarises the
+ * prefix, and the next token needs one recurrence step h_t = Abar h_{t-1} +
+ * Bbar x_t, O(1) in the prefix length; Results: each decode step reads and
+ * writes the same state whatever the prefix length.
+ *
+ *   state [Bt,H,P,N] f32, read and overwritten with the new state
+ *   x_t   [Bt,H,P] io_dtype        dt_t [Bt,H] f32 (pre-activation)
+ *   A [H] f32, dt_bias [H] f32 or NULL, D [H] f32 or NULL
+ *   B_t, C_t [Bt,G,N] io_dtype
+ *   y_t   [Bt,H,P] io_dtype (written; must not overlap the state or inputs)
+ *
+ * Each state element is read once and written once.
+ */
+ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x_t, const float* dt_t,
+                    const float* dt_bias, const float* A, const void* B_t, const void* C_t,
+                    const float* D, void* y_t, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* ssd_status_string(ssd_status status);
+
+/* SSD_ABI_VERSION of the built library. */
+int32_t ssd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_MI355X_H */

@@ -1,0 +1,217 @@
+"""Python binding of libssd, the gfx950 Mamba-2 SSD library.
+
+Argument marshalling only: every step of the scan and of the decode step runs
+in the HIP kernels behind the C ABI declared in include/ssd.h.  PyTorch is
+used for device memory and for the current HIP stream; there is no CPU or
+PyTorch fallback -- if libssd.so is missing, importing this package raises.
+
+  ssd_chunk_scan(x, dt, A, B, C, D=None, *, chunk=256, ...) -> (y, final_state)
+  ssd_step(state, x_t, dt_t, A, B_t, C_t, D=None, ...)      -> y_t  (state updated in place)
+  ssd_chunk_scan_workspace_bytes(...)                        -> int
+
+Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
+Caching" (Background, Eq. 2-3; O(1) cache).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_OK = 0
+SSD_F32 = 0
+SSD_BF16 = 1
+SSD_SCAN_PHASES = 3
+STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
+                4: "SSD_ERR_ALIGNMENT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE",
+                7: "SSD_ERR_HIP"}
+EXPORTED = ("ssd_chunk_scan", "ssd_chunk_scan_timed", "ssd_chunk_scan_workspace_bytes",
+            "ssd_step", "ssd_status_string", "ssd_abi_version")
+
+
+class ScanDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("dt_softplus", ctypes.c_int32), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float)]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64),
+                ("ngroups", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("dt_softplus", ctypes.c_int32), ("dt_min", ctypes.c_float),
+                ("dt_max", ctypes.c_float)]
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = int(status)
+        msg = lib.ssd_status_string(self.status).decode()
+        super().__init__(f"{where}: {msg}" if where else msg)
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build the gfx950 library first "
+            "(python -c 'import __graft_entry__ as g; g.build()' or "
+            "python state_space_model_amd/build.py). There is no CPU fallback.")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.ssd_chunk_scan.restype = i32
+    L.ssd_chunk_scan.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 11 + [sz, vp]
+    L.ssd_chunk_scan_timed.restype = i32
+    L.ssd_chunk_scan_timed.argtypes = ([ctypes.POINTER(ScanDesc)] + [vp] * 11 + [sz, vp]
+                                       + [ctypes.POINTER(vp), ctypes.c_int])
+    L.ssd_chunk_scan_workspace_bytes.restype = sz
+    L.ssd_chunk_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
+    L.ssd_step.restype = i32
+    L.ssd_step.argtypes = [ctypes.POINTER(StepDesc)] + [vp] * 9 + [vp]
+    L.ssd_status_string.restype = ctypes.c_char_p
+    L.ssd_status_string.argtypes = [i32]
+    L.ssd_abi_version.restype = i32
+    L.ssd_abi_version.argtypes = []
+    return L
+
+
+lib = _load()
+
+
+def _io_code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
+        return SSD_F32
+    if dtype == torch.bfloat16:
+        return SSD_BF16
+    raise TypeError(f"x, B, C must be float32 or bfloat16, got {dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor (got {t.device}); there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def scan_desc(x: torch.Tensor, B: torch.Tensor, chunk: int, dt_softplus: bool,
+              dt_limit: Sequence[float]) -> ScanDesc:
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return ScanDesc(Bt, T, H, P, N, G, int(chunk), _io_code(x.dtype), int(bool(dt_softplus)),
+                    float(dt_limit[0]), float(dt_limit[1]))
+
+
+def ssd_chunk_scan_workspace_bytes(x: torch.Tensor, B: torch.Tensor, chunk: int = 256) -> int:
+    d = scan_desc(x, B, chunk, True, (1e-4, 0.5))
+    return int(lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d)))
+
+
+def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                   C: torch.Tensor, D: Optional[torch.Tensor] = None, *, chunk: int = 256,
+                   dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True,
+                   dt_limit: Sequence[float] = (1e-4, 0.5),
+                   initial_state: Optional[torch.Tensor] = None,
+                   return_final_state: bool = True,
+                   y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   phase_events: Optional[Sequence[torch.cuda.Event]] = None
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked SSD scan (prefill) on the current stream.
+
+    x [Bt,T,H,P], B/C [Bt,T,G,N] in float32 or bfloat16 (same dtype);
+    dt [Bt,T,H], A/D/dt_bias [H], initial_state [Bt,H,P,N] float32.
+    Returns (y [Bt,T,H,P] in x's dtype, final_state [Bt,H,P,N] float32 or None).
+    Output and workspace tensors may be passed in to avoid allocation.
+    `phase_events`: optional SSD_SCAN_PHASES+1 torch.cuda.Event objects
+    (created with enable_timing=True) recorded around the scan's kernels.
+    """
+    if x.dim() != 4 or B.dim() != 4 or C.shape != B.shape:
+        raise ValueError("x must be [Bt,T,H,P] and B, C [Bt,T,G,N]")
+    for t, n, dt_ in ((x, "x", None), (B, "B", x.dtype), (C, "C", x.dtype), (dt, "dt", torch.float32),
+                      (A, "A", torch.float32), (D, "D", torch.float32),
+                      (dt_bias, "dt_bias", torch.float32),
+                      (initial_state, "initial_state", torch.float32)):
+        _check(t, n, dt_)
+    desc = scan_desc(x, B, chunk, dt_softplus, dt_limit)
+    Bt, T, H, P = x.shape
+    N = B.shape[3]
+    dev = x.device
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+    _check(y, "y", x.dtype)
+    _check(final_state, "final_state", torch.float32)
+    need = int(lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace")
+    wbytes = workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
+            ctypes.c_size_t(wbytes), _stream(dev))
+    if phase_events is None:
+        st = lib.ssd_chunk_scan(*args)
+    else:
+        evs = (ctypes.c_void_p * len(phase_events))(*[ctypes.c_void_p(e.cuda_event)
+                                                      for e in phase_events])
+        st = lib.ssd_chunk_scan_timed(*args, evs, len(phase_events))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_scan")
+    return y, final_state
+
+
+def step_desc(state: torch.Tensor, x_t: torch.Tensor, B_t: torch.Tensor, dt_softplus: bool,
+              dt_limit: Sequence[float]) -> StepDesc:
+    Bt, H, P, N = state.shape
+    return StepDesc(Bt, H, P, N, B_t.shape[1], _io_code(x_t.dtype), int(bool(dt_softplus)),
+                    float(dt_limit[0]), float(dt_limit[1]))
+
+
+def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torch.Tensor,
+             B_t: torch.Tensor, C_t: torch.Tensor, D: Optional[torch.Tensor] = None, *,
+             dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True,
+             dt_limit: Sequence[float] = (1e-4, 0.5),
+             y_t: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step on the current stream; `state` [Bt,H,P,N] float32 is
+    updated in place.  x_t [Bt,H,P], B_t/C_t [Bt,G,N] (float32 or bfloat16),
+    dt_t [Bt,H] float32.  Returns y_t [Bt,H,P] in x_t's dtype."""
+    if state.dim() != 4 or x_t.dim() != 3 or B_t.dim() != 3 or C_t.shape != B_t.shape:
+        raise ValueError("state [Bt,H,P,N], x_t [Bt,H,P], B_t/C_t [Bt,G,N]")
+    for t, n, dt_ in ((state, "state", torch.float32), (x_t, "x_t", None),
+                      (B_t, "B_t", x_t.dtype), (C_t, "C_t", x_t.dtype),
+                      (dt_t, "dt_t", torch.float32), (A, "A", torch.float32),
+                      (D, "D", torch.float32), (dt_bias, "dt_bias", torch.float32)):
+        _check(t, n, dt_)
+    desc = step_desc(state, x_t, B_t, dt_softplus, dt_limit)
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    _check(y_t, "y_t", x_t.dtype)
+    st = lib.ssd_step(ctypes.byref(desc), _ptr(state), _ptr(x_t), _ptr(dt_t), _ptr(dt_bias),
+                      _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D), _ptr(y_t), _stream(state.device))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_step")
+    return y_t
+
+
+def abi_version() -> int:
+    return int(lib.ssd_abi_version())

@@ -1,0 +1,250 @@
+// C ABI of libssd: argument validation, workspace layout and dispatch to the
+// gfx950 kernels.  Declarations and the contract are in include/ssd.h.
+//
+// Everything here runs on the host.  Validation is complete before the first
+// launch, so an invalid call writes nothing.  No allocation, no
+// synchronisation, no global mutable state.
+#include "ssd.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "ssd_launch.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+inline size_t io_size(int32_t dt) { return dt == SSD_BF16 ? 2 : 4; }
+
+// Checked product of non-negative int64 values; false on overflow.
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+inline Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)bytes};
+}
+
+inline bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+inline bool limits_ok(float lo, float hi) { return !isnan(lo) && !isnan(hi) && lo <= hi; }
+
+struct ScanSizes {
+  int64_t Nc = 0;
+  int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0;  // element counts
+  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_total = 0;
+};
+
+ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
+      d->ngroups <= 0 || d->chunk <= 0)
+    return SSD_ERR_SHAPE;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_SHAPE;
+  if (!limits_ok(d->dt_min, d->dt_max)) return SSD_ERR_INVALID_ARG;
+  if (!ssd::scan_shape_supported(d->headdim, d->dstate, d->chunk, d->io_dtype == SSD_BF16))
+    return SSD_ERR_UNSUPPORTED;
+  const int64_t Nc = (d->seqlen + d->chunk - 1) / d->chunk;
+  int64_t bt = 0, bth = 0, bh = 0, pn = 0, tmp = 0;
+  if (!mul_ok(d->batch, d->seqlen, &bt) || !mul_ok(bt, d->nheads, &bth) ||
+      !mul_ok(bth, d->headdim, &s->n_x) || !mul_ok(bt, d->ngroups, &tmp) ||
+      !mul_ok(tmp, d->dstate, &s->n_bc) || !mul_ok(d->batch, d->nheads, &bh) ||
+      !mul_ok(d->headdim, d->dstate, &pn) || !mul_ok(bh, pn, &s->n_state))
+    return SSD_ERR_UNSUPPORTED;
+  s->n_dt = bth;
+  s->Nc = Nc;
+  int64_t units = 0, ws_elems = 0;
+  if (!mul_ok(bh, Nc, &units) || !mul_ok(units, pn, &ws_elems) || !mul_ok(ws_elems, 4, &tmp))
+    return SSD_ERR_UNSUPPORTED;
+  // one workgroup per (batch, chunk, head): the grid must fit a 32-bit x-dimension
+  if (units > INT32_MAX || s->n_x > (INT64_MAX / 8)) return SSD_ERR_UNSUPPORTED;
+  s->ws_state_bytes = round_up((size_t)ws_elems * 4, kAlign);
+  s->ws_alpha_bytes = round_up((size_t)units * 4, kAlign);
+  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes;
+  return SSD_OK;
+}
+
+ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
+                     const float* dt_bias, const float* A, const void* B, const void* C,
+                     const float* D, const float* initial_state, void* y, float* final_state,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream,
+                     hipEvent_t* events, int n_events) {
+  ScanSizes s;
+  ssd_status st = check_scan_desc(desc, &s);
+  if (st != SSD_OK) return st;
+  if (events && n_events < SSD_SCAN_PHASES + 1) return SSD_ERR_INVALID_ARG;
+  const bool work = desc->batch > 0 && desc->seqlen > 0;
+  if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_INVALID_ARG;
+  if (!work && desc->batch > 0 && !A) return SSD_ERR_INVALID_ARG;
+  // tensors read or written in 16-byte vectors, and per-token/per-head scalars
+  const void* vec[] = {x, B, C, initial_state, y, final_state, workspace};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return SSD_ERR_ALIGNMENT;
+  const void* scal[] = {dt, dt_bias, A, D};
+  for (const void* p : scal)
+    if (p && !aligned4(p)) return SSD_ERR_ALIGNMENT;
+  if (work && (!workspace || workspace_bytes < s.ws_total)) return SSD_ERR_WORKSPACE;
+
+  // outputs must not overlap any input, the workspace or each other
+  const int64_t es = (int64_t)io_size(desc->io_dtype);
+  const Range r_y = work ? range_of(y, s.n_x * es) : Range{0, 0};
+  const Range r_f = final_state ? range_of(final_state, s.n_state * 4) : Range{0, 0};
+  const Range ins[] = {
+      range_of(x, work ? s.n_x * es : 0), range_of(dt, work ? s.n_dt * 4 : 0),
+      range_of(dt_bias, desc->nheads * 4), range_of(A, desc->nheads * 4),
+      range_of(B, work ? s.n_bc * es : 0), range_of(C, work ? s.n_bc * es : 0),
+      range_of(D, desc->nheads * 4), range_of(initial_state, s.n_state * 4),
+      range_of(workspace, work ? (int64_t)s.ws_total : 0)};
+  for (const Range& r : ins)
+    if (overlap(r_y, r) || overlap(r_f, r)) return SSD_ERR_INVALID_ARG;
+  if (overlap(r_y, r_f)) return SSD_ERR_INVALID_ARG;
+
+  if (desc->batch == 0) return SSD_OK;
+  if (!work) {
+    // empty sequence: the final state is the initial state (or zeros)
+    if (final_state) {
+      if (events) {
+        for (int k = 0; k <= SSD_SCAN_PHASES; ++k)
+          if (hipEventRecord(events[k], stream) != hipSuccess) return SSD_ERR_HIP;
+      }
+      if (ssd::launch_copy_or_zero(final_state, initial_state, s.n_state, stream) != hipSuccess)
+        return SSD_ERR_HIP;
+    }
+    return SSD_OK;
+  }
+
+  ssd::ScanArgs a;
+  a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
+  a.h0 = initial_state; a.y = y; a.final_state = final_state;
+  a.ws_state = static_cast<float*>(workspace);
+  a.ws_alpha = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws_state_bytes);
+  a.Bt = desc->batch; a.T = desc->seqlen; a.H = desc->nheads; a.G = desc->ngroups;
+  a.L = desc->chunk; a.Nc = s.Nc;
+  a.softplus = desc->dt_softplus ? 1 : 0;
+  a.dt_min = desc->dt_min; a.dt_max = desc->dt_max;
+  hipError_t e = desc->io_dtype == SSD_BF16
+                     ? ssd::launch_scan_bf16(a, (int)desc->headdim, (int)desc->dstate, stream, events)
+                     : ssd::launch_scan_f32(a, (int)desc->headdim, (int)desc->dstate, stream, events);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+namespace ssd {
+bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16) {
+  // bfloat16 matrix-core steps contract 32 state elements at a time
+  const bool pn = (P == 16 || P == 32 || P == 64 || P == 128) &&
+                  ((N == 16 && !bf16) || N == 32 || N == 64 || N == 128);
+  return pn && L >= 32 && L <= 512 && L % 32 == 0 && P * L <= 32768;
+}
+}  // namespace ssd
+
+extern "C" {
+
+size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc) {
+  ScanSizes s;
+  if (check_scan_desc(desc, &s) != SSD_OK) return 0;
+  return s.ws_total;
+}
+
+ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float* dt,
+                          const float* dt_bias, const float* A, const void* B, const void* C,
+                          const float* D, const float* initial_state, void* y,
+                          float* final_state, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return scan_impl(desc, x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, workspace,
+                   workspace_bytes, stream, nullptr, 0);
+}
+
+ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const float* dt,
+                                const float* dt_bias, const float* A, const void* B,
+                                const void* C, const float* D, const float* initial_state,
+                                void* y, float* final_state, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* phase_events, int n_events) {
+  return scan_impl(desc, x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, workspace,
+                   workspace_bytes, stream, phase_events, n_events);
+}
+
+ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x_t, const float* dt_t,
+                    const float* dt_bias, const float* A, const void* B_t, const void* C_t,
+                    const float* D, void* y_t, hipStream_t stream) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+  if (d->batch < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+    return SSD_ERR_SHAPE;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_SHAPE;
+  if (!limits_ok(d->dt_min, d->dt_max)) return SSD_ERR_INVALID_ARG;
+  if (!ssd::step_shape_supported(d->headdim, d->dstate)) return SSD_ERR_UNSUPPORTED;
+  int64_t bh = 0, pn = 0, n_state = 0, n_x = 0, bg = 0, n_bc = 0;
+  if (!mul_ok(d->batch, d->nheads, &bh) || !mul_ok(d->headdim, d->dstate, &pn) ||
+      !mul_ok(bh, pn, &n_state) || !mul_ok(bh, d->headdim, &n_x) ||
+      !mul_ok(d->batch, d->ngroups, &bg) || !mul_ok(bg, d->dstate, &n_bc) || bh > INT32_MAX)
+    return SSD_ERR_UNSUPPORTED;
+  if (d->batch == 0) return SSD_OK;
+  if (!state || !x_t || !dt_t || !A || !B_t || !C_t || !y_t) return SSD_ERR_INVALID_ARG;
+  const void* vec[] = {state, x_t, B_t, C_t, y_t};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return SSD_ERR_ALIGNMENT;
+  const void* scal[] = {dt_t, dt_bias, A, D};
+  for (const void* p : scal)
+    if (p && !aligned4(p)) return SSD_ERR_ALIGNMENT;
+  const int64_t es = (int64_t)io_size(d->io_dtype);
+  const Range r_y = range_of(y_t, n_x * es);
+  const Range others[] = {range_of(state, n_state * 4), range_of(x_t, n_x * es),
+                          range_of(dt_t, bh * 4), range_of(dt_bias, d->nheads * 4),
+                          range_of(A, d->nheads * 4), range_of(B_t, n_bc * es),
+                          range_of(C_t, n_bc * es), range_of(D, d->nheads * 4)};
+  for (const Range& r : others)
+    if (overlap(r_y, r)) return SSD_ERR_INVALID_ARG;
+  const Range r_s = others[0];
+  for (int k = 1; k < 8; ++k)
+    if (overlap(r_s, others[k])) return SSD_ERR_INVALID_ARG;
+
+  ssd::StepArgs a;
+  a.state = state; a.x = x_t; a.dt = dt_t; a.dt_bias = dt_bias; a.A = A;
+  a.B = B_t; a.C = C_t; a.D = D; a.y = y_t;
+  a.Bt = d->batch; a.H = d->nheads; a.G = d->ngroups;
+  a.P = (int32_t)d->headdim; a.N = (int32_t)d->dstate;
+  a.softplus = d->dt_softplus ? 1 : 0;
+  a.dt_min = d->dt_min; a.dt_max = d->dt_max;
+  hipError_t e = d->io_dtype == SSD_BF16 ? ssd::launch_step_bf16(a, stream)
+                                         : ssd::launch_step_f32(a, stream);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+const char* ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_INVALID_ARG: return "SSD_ERR_INVALID_ARG: null, aliased or otherwise invalid argument";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: non-positive size or heads not a multiple of groups";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE: unknown io dtype";
+    case SSD_ERR_ALIGNMENT: return "SSD_ERR_ALIGNMENT: device pointer below its required alignment";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape without a compiled gfx950 variant";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown ssd_status";
+}
+
+int32_t ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+}  // extern "C"

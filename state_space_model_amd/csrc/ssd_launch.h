@@ -1,0 +1,59 @@
+// Internal interface between the C ABI (ssd_api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Arguments of the chunked scan, after validation.  Device pointers.
+struct ScanArgs {
+  const void* x;          // [Bt,T,H,P] io
+  const float* dt;        // [Bt,T,H]
+  const float* dt_bias;   // [H] or null
+  const float* A;         // [H]
+  const void* B;          // [Bt,T,G,N] io
+  const void* C;          // [Bt,T,G,N] io
+  const float* D;         // [H] or null
+  const float* h0;        // [Bt,H,P,N] or null
+  void* y;                // [Bt,T,H,P] io
+  float* final_state;     // [Bt,H,P,N] or null
+  float* ws_state;        // [Bt,H,Nc,P,N]: chunk summary states, then entering states
+  float* ws_alpha;        // [Bt,H,Nc]: exp(total decay of the chunk)
+  int64_t Bt, T, H, G, L, Nc;
+  int32_t softplus;
+  float dt_min, dt_max;
+};
+
+struct StepArgs {
+  float* state;           // [Bt,H,P,N] in/out
+  const void* x;          // [Bt,H,P] io
+  const float* dt;        // [Bt,H]
+  const float* dt_bias;   // [H] or null
+  const float* A;         // [H]
+  const void* B;          // [Bt,G,N] io
+  const void* C;          // [Bt,G,N] io
+  const float* D;         // [H] or null
+  void* y;                // [Bt,H,P] io
+  int64_t Bt, H, G;
+  int32_t P, N;
+  int32_t softplus;
+  float dt_min, dt_max;
+};
+
+// Compiled shape variants.
+bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16);
+bool step_shape_supported(int64_t P, int64_t N);
+
+// Launch the whole scan (Bt*T > 0) on `stream`.  `events` (may be null) gets
+// one record before each of the 3 phases and one after the last.
+hipError_t launch_scan_f32(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* events);
+hipError_t launch_scan_bf16(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* events);
+
+hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
+hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
+
+// dst[i] = src ? src[i] : 0 for i < n (float4 granularity; n % 4 == 0).
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,107 @@
+// One decode step of the SSD recurrence for gfx950, state updated in place.
+//
+// Source: "Compiler-First State Space Duality and Portable O(1)
+// Autoregressive Caching", O(1) cache section (the fixed-size state
+// (B,H,P,N) summarises the prefix; the next token needs one step
+// h_t = Abar h_{t-1} + Bbar x_t) and Results (decode reads and writes the same
+// state whatever the prefix length, so it is bound by memory bandwidth).
+//
+// Per (b, h):  d = clip(softplus(dt + dt_bias)),  alpha = exp(d A[h])
+//   h'[p,n] = alpha h[p,n] + d x[p] B[n];   y[p] = sum_n C[n] h'[p,n] + D[h] x[p]
+// One workgroup streams the (b, h) state slice: every lane moves 16-byte
+// vectors, a wavefront instruction covers 1 KB of contiguous state, each
+// element is read once and written once, and the row sums over n are reduced
+// across the N/4 lanes that hold one row.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 8;  // float4 loads in flight per lane
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
+  const int P = a.P, N = a.N, NQ = N / 4;
+  const int tid = threadIdx.x;
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float d = delta_of(a.dt[bh] + bias, a.softplus, a.dt_min, a.dt_max);
+  const float alpha = expf(d * a.A[h]);
+  const float Dh = a.D ? a.D[h] : 0.0f;
+  const T* xg = reinterpret_cast<const T*>(a.x) + bh * P;
+  const T* Bg = reinterpret_cast<const T*>(a.B) + (b * a.G + g) * N;
+  const T* Cg = reinterpret_cast<const T*>(a.C) + (b * a.G + g) * N;
+  T* yg = reinterpret_cast<T*>(a.y) + bh * P;
+  float4* st = reinterpret_cast<float4*>(a.state + bh * (int64_t)P * N);
+
+  // the n-quad of this lane is the same for every row it visits (NQ | 256)
+  const int n4 = tid % NQ;
+  float bv[4], cv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bv[k] = to_f32(Bg[4 * n4 + k]);
+    cv[k] = to_f32(Cg[4 * n4 + k]);
+  }
+  const int total = P * NQ;  // float4 elements of the slice, a multiple of 64
+  for (int base = 0; base < total; base += kThreads * kBatch) {
+    float4 s[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int f = base + k * kThreads + tid;
+      if (f < total) s[k] = st[f];
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int f = base + k * kThreads + tid;
+      if (f < total) {  // uniform per wavefront: total is a multiple of 64
+        const int p = f / NQ;
+        const float xp = to_f32(xg[p]);
+        const float dx = d * xp;
+        float4 v = s[k];
+        v.x = alpha * v.x + dx * bv[0];
+        v.y = alpha * v.y + dx * bv[1];
+        v.z = alpha * v.z + dx * bv[2];
+        v.w = alpha * v.w + dx * bv[3];
+        st[f] = v;
+        float part = cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w;
+        part = group_sum(part, NQ);
+        if (n4 == 0) yg[p] = to_io<T>(part + Dh * xp);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void k_copy_or_zero(float4* dst, const float4* src, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n4) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+template <typename T>
+hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
+  const int64_t blocks = a.Bt * a.H;
+  hipLaunchKernelGGL(k_step<T>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool step_shape_supported(int64_t P, int64_t N) {
+  return (P == 16 || P == 32 || P == 64 || P == 128) && (N == 16 || N == 32 || N == 64 || N == 128);
+}
+
+hipError_t launch_step_f32(const StepArgs& a, hipStream_t s) { return launch_step<float>(a, s); }
+hipError_t launch_step_bf16(const StepArgs& a, hipStream_t s) { return launch_step<bf16>(a, s); }
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const int64_t blocks = (n4 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_copy_or_zero, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                     reinterpret_cast<float4*>(dst), reinterpret_cast<const float4*>(src), n4);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,189 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and rejects invalid arguments before launching anything.
+
+Every call here fails validation (or is a documented no-op such as batch 0
+without outputs), so no HIP kernel is launched and no device memory is
+touched; the pointers are fake addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import state_space_model_amd as ssd
+from state_space_model_amd import ScanDesc, StepDesc, lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "ssd.h")
+
+OK, INVALID, SHAPE, DTYPE, ALIGN, UNSUP, WS, HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(ssd.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_abi_version_and_status_strings():
+    assert ssd.abi_version() == 1
+    for code in range(8):
+        s = lib.ssd_status_string(code).decode()
+        assert s.startswith(ssd.STATUS_NAMES[code])
+    assert lib.ssd_status_string(99).decode() == "unknown ssd_status"
+
+
+def desc(**kw):
+    d = dict(batch=1, seqlen=512, nheads=4, headdim=16, dstate=16, ngroups=1, chunk=64,
+             io_dtype=0, dt_softplus=1, dt_min=1e-4, dt_max=0.5)
+    d.update(kw)
+    return ScanDesc(**d)
+
+
+BASE = 0x7F0000000000  # fake, 256-byte aligned device addresses, never dereferenced
+
+
+def fake_args(d: ScanDesc, ws_bytes=None, **over):
+    es = 2 if d.io_dtype == 1 else 4
+    sizes = dict(x=d.batch * d.seqlen * d.nheads * d.headdim * es,
+                 dt=d.batch * d.seqlen * d.nheads * 4, dt_bias=d.nheads * 4, A=d.nheads * 4,
+                 B=d.batch * d.seqlen * d.ngroups * d.dstate * es,
+                 C=d.batch * d.seqlen * d.ngroups * d.dstate * es, D=d.nheads * 4,
+                 h0=d.batch * d.nheads * d.headdim * d.dstate * 4,
+                 y=d.batch * d.seqlen * d.nheads * d.headdim * es,
+                 fin=d.batch * d.nheads * d.headdim * d.dstate * 4, ws=1 << 30)
+    ptr, addr = {}, BASE
+    for k, v in sizes.items():
+        ptr[k] = addr
+        addr += (max(v, 1) + 4095) // 4096 * 4096
+    ptr.update(over)
+    need = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
+    wsb = need if ws_bytes is None else ws_bytes
+    P = ctypes.c_void_p
+    return (ctypes.byref(d), P(ptr["x"]), P(ptr["dt"]), P(ptr["dt_bias"]), P(ptr["A"]),
+            P(ptr["B"]), P(ptr["C"]), P(ptr["D"]), P(ptr["h0"]), P(ptr["y"]), P(ptr["fin"]),
+            P(ptr["ws"]), ctypes.c_size_t(wsb), P(0))
+
+
+def scan_status(d, **kw):
+    return lib.ssd_chunk_scan(*fake_args(d, **kw))
+
+
+def test_workspace_query():
+    d = desc()
+    n = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
+    nc = 512 // 64
+    assert n >= 4 * 1 * 4 * nc * (16 * 16 + 1)
+    assert n % 256 == 0
+    # ragged sequence: the last partial chunk still needs a state
+    d2 = desc(seqlen=513)
+    assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d2)) > n
+    assert lib.ssd_chunk_scan_workspace_bytes(None) == 0
+    assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(desc(headdim=24))) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(io_dtype=2), DTYPE),
+    (dict(batch=-1), SHAPE),
+    (dict(seqlen=-5), SHAPE),
+    (dict(nheads=0), SHAPE),
+    (dict(headdim=0), SHAPE),
+    (dict(chunk=0), SHAPE),
+    (dict(nheads=6, ngroups=4), SHAPE),
+    (dict(dt_min=0.6, dt_max=0.5), INVALID),
+    (dict(dt_min=float("nan")), INVALID),
+    (dict(headdim=24), UNSUP),
+    (dict(dstate=48), UNSUP),
+    (dict(chunk=48), UNSUP),
+    (dict(chunk=1024), UNSUP),
+    (dict(headdim=128, chunk=512), UNSUP),
+    (dict(io_dtype=1, dstate=16), UNSUP),
+])
+def test_scan_descriptor_errors(kw, code):
+    assert scan_status(desc(**kw)) == code
+
+
+def test_scan_pointer_errors():
+    d = desc()
+    assert lib.ssd_chunk_scan(None, *fake_args(d)[1:]) == INVALID
+    assert scan_status(d, x=0) == INVALID
+    assert scan_status(d, dt=0) == INVALID
+    assert scan_status(d, A=0) == INVALID
+    assert scan_status(d, y=0) == INVALID
+    assert scan_status(d, x=BASE + 8) == ALIGN
+    assert scan_status(d, fin=BASE + 4) == ALIGN
+    args = fake_args(d)
+    assert scan_status(d, dt=args[2].value + 2) == ALIGN     # scalars: 4-byte alignment
+    assert scan_status(d, A=args[4].value + 4, ws=0) == WS   # 4-byte offset is fine for A
+    assert scan_status(d, ws=0) == WS
+    assert scan_status(d, ws_bytes=1024) == WS
+    # outputs overlapping inputs, the workspace or each other
+    args = fake_args(d)
+    x_addr = args[1].value
+    assert scan_status(d, y=x_addr) == INVALID
+    assert scan_status(d, fin=args[4].value) == INVALID      # final state over A
+    assert scan_status(d, y=args[11].value + 4096) == INVALID  # y inside the workspace
+    assert scan_status(d, fin=args[9].value + 256) == INVALID  # final state inside y
+
+
+def test_scan_timed_needs_enough_events():
+    d = desc()
+    evs = (ctypes.c_void_p * 2)()
+    assert lib.ssd_chunk_scan_timed(*fake_args(d), evs, 2) == INVALID
+
+
+def test_empty_batch_is_a_noop():
+    # batch 0: nothing to compute, nothing launched
+    assert scan_status(desc(batch=0)) == OK
+    # empty sequence without a requested final state: nothing launched
+    d = desc(seqlen=0)
+    assert scan_status(d, fin=0) == OK
+
+
+def step_desc(**kw):
+    d = dict(batch=2, nheads=4, headdim=16, dstate=16, ngroups=1, io_dtype=0, dt_softplus=1,
+             dt_min=1e-4, dt_max=0.5)
+    d.update(kw)
+    return StepDesc(**d)
+
+
+def step_status(d, **over):
+    ptr = dict(state=BASE, x=BASE + (1 << 24), dt=BASE + (2 << 24), bias=BASE + (3 << 24),
+               A=BASE + (4 << 24), B=BASE + (5 << 24), C=BASE + (6 << 24), D=BASE + (7 << 24),
+               y=BASE + (8 << 24))
+    ptr.update(over)
+    P = ctypes.c_void_p
+    return lib.ssd_step(ctypes.byref(d), P(ptr["state"]), P(ptr["x"]), P(ptr["dt"]),
+                        P(ptr["bias"]), P(ptr["A"]), P(ptr["B"]), P(ptr["C"]), P(ptr["D"]),
+                        P(ptr["y"]), P(0))
+
+
+def test_step_errors():
+    assert lib.ssd_step(None, *([None] * 10)) == INVALID
+    assert step_status(step_desc(io_dtype=3)) == DTYPE
+    assert step_status(step_desc(nheads=3, ngroups=2)) == SHAPE
+    assert step_status(step_desc(headdim=8)) == UNSUP
+    assert step_status(step_desc(dt_min=1.0, dt_max=0.1)) == INVALID
+    assert step_status(step_desc(), state=0) == INVALID
+    assert step_status(step_desc(), x=BASE + (1 << 24) + 2) == ALIGN
+    assert step_status(step_desc(), dt=BASE + (2 << 24) + 2) == ALIGN
+    assert step_status(step_desc(), y=BASE) == INVALID          # y over the state
+    assert step_status(step_desc(), x=BASE + 64) == INVALID     # x inside the state
+    assert step_status(step_desc(batch=0)) == OK                # nothing to do
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 64, 4, 16)
+    B = torch.zeros(1, 64, 1, 16)
+    with pytest.raises(ValueError, match="device tensor"):
+        ssd.ssd_chunk_scan(x, torch.zeros(1, 64, 4), torch.zeros(4), B, B, chunk=64)

@@ -1,0 +1,191 @@
+"""GPU parity of ssd_chunk_scan (the chunked prefill) against the CPU oracle.
+
+Every case calls the HIP kernels through the C ABI (python binding) and
+compares element by element with the fp64 token-by-token recurrence on the
+same seeded inputs.  Error = max over (b, h) slices of
+||gpu - oracle||_inf / ||oracle||_inf; bar: 1e-4 for float32 inputs, 2e-2 for
+bfloat16 x/B/C (float32 decay, states and accumulation).
+
+Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
+Caching" (Background, Eq. 2-3; SSD properties: chunked recurrence; O(1)
+cache: the prefill's final state seeds the decode cache).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (TOL, announce, need_gpu, oracle_scan, slice_bh, state_err, to_dev,
+                      workload_inputs, y_err)
+from ssd_inputs import WORKLOADS, make_inputs, make_tiny
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(inp, w, chunk=None, **kw):
+    import state_space_model_amd as ssd
+    d = to_dev(inp)
+    y, fin = ssd.ssd_chunk_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], d.get("D"),
+                                chunk=chunk or w.chunk, dt_bias=d.get("dt_bias"),
+                                dt_limit=(w.dt_min, w.dt_max), initial_state=d.get("h0"), **kw)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "m130_f32", "m2p7_bf16"])
+def test_scan_workload_full(name):
+    """Whole-problem parity on the tiny, 130M-shaped and 2.7B-shaped layers."""
+    need_gpu()
+    w = WORKLOADS[name]
+    inp = workload_inputs(name)
+    announce(f"scan {name} {w}")
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    ey, ef = y_err(y, y_ref), state_err(fin, f_ref)
+    print(f"{name}: y err {ey:.3e}  final-state err {ef:.3e}")
+    assert ey <= TOL[w.io_dtype] and ef <= TOL[w.io_dtype]
+
+
+SAMPLE_BH = [(0, 0), (3, 17), (5, 40), (7, 63)]
+
+
+@pytest.mark.parametrize("chunk", [128, 256, 512])
+def test_scan_long_batched_sampled(chunk):
+    """1.3B-shaped batched long prefill (8 x 16384, H=64) at chunk 128/256/512:
+    the full problem runs on the GPU in the benchmark's launch configuration;
+    the oracle recomputes sampled (b, h) sequences end to end."""
+    need_gpu()
+    w = WORKLOADS["m1p3_long_bf16"]
+    inp = workload_inputs("m1p3_long_bf16")
+    announce(f"scan m1p3_long_bf16 chunk={chunk}")
+    y, fin = run_gpu(inp, w, chunk=chunk)
+    worst = 0.0
+    for b, h in SAMPLE_BH:
+        s = slice_bh(inp, b, h, w.ngroups, w.nheads)
+        y_ref, f_ref = oracle_scan(s, w)
+        ey = y_err(y[b:b + 1, :, h:h + 1], y_ref)
+        ef = state_err(fin[b:b + 1, h:h + 1], f_ref)
+        worst = max(worst, ey, ef)
+    print(f"chunk {chunk}: worst sampled err {worst:.3e}")
+    assert worst <= TOL["bf16"]
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+
+
+def test_scan_chunk_size_invariance_on_gpu():
+    """The same inputs at chunk 64/128/256 give the same result up to rounding
+    (chunked recurrence: the chunk size trades work, not the answer)."""
+    need_gpu()
+    w = make_tiny(2, 1000, 8, 64, 128, 2, 64, "bf16", seed=31)
+    inp = make_inputs(w)
+    announce("scan chunk invariance 2x1000 H8 P64 N128 G2 bf16")
+    outs = [run_gpu(inp, w, chunk=L) for L in (64, 128, 256)]
+    y_ref, f_ref = oracle_scan(inp, w)
+    for y, f in outs:
+        assert y_err(y, y_ref) <= TOL["bf16"] and state_err(f, f_ref) <= TOL["bf16"]
+    for y, f in outs[1:]:
+        assert y_err(y, outs[0][0].double().cpu()) <= TOL["bf16"]
+
+
+TINY = [
+    # (Bt, T, H, P, N, G, L, dtype)
+    (1, 96, 2, 16, 16, 1, 32, "f32"),        # three chunks
+    (2, 200, 4, 32, 32, 2, 64, "f32"),       # ragged last chunk, groups
+    (1, 77, 3, 16, 64, 1, 96, "f32"),        # one partial chunk, L not a power of two
+    (1, 1, 2, 16, 16, 1, 64, "f32"),         # a single token
+    (2, 333, 4, 64, 128, 1, 128, "f32"),     # ragged, 130M head shape
+    (1, 300, 2, 128, 128, 1, 256, "f32"),    # P = 128
+    (1, 512, 2, 64, 64, 2, 512, "f32"),      # L = 512
+    (1, 100, 4, 16, 32, 4, 32, "bf16"),      # one group per head
+    (2, 257, 4, 64, 128, 1, 256, "bf16"),    # 2.7B head shape, one token past a chunk
+    (1, 700, 2, 32, 64, 1, 512, "bf16"),     # L = 512, ragged
+    (1, 130, 2, 128, 32, 1, 64, "bf16"),     # P = 128
+    (3, 64, 6, 16, 128, 3, 32, "bf16"),      # many chunks of 32
+]
+
+
+@pytest.mark.parametrize("case", TINY, ids=lambda c: "x".join(map(str, c)))
+def test_scan_tiny_shapes(case):
+    need_gpu()
+    Bt, T, H, P, N, G, L, dt = case
+    w = make_tiny(Bt, T, H, P, N, G, L, dt, seed=1000 + TINY.index(case))
+    inp = make_inputs(w, with_initial_state=True)
+    announce(f"scan tiny {case}")
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    assert y_err(y, y_ref) <= TOL[dt], y_err(y, y_ref)
+    assert state_err(fin, f_ref) <= TOL[dt], state_err(fin, f_ref)
+
+
+def test_scan_options_off():
+    """No D, no dt_bias, softplus off, no initial state, no final state requested."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = make_tiny(2, 150, 4, 32, 64, 2, 64, "f32", seed=5)
+    inp = make_inputs(w)
+    inp["dt"] = inp["dt"].abs() * 0.2 + 0.01  # already a step size
+    announce("scan options off")
+    d = to_dev(inp)
+    y, fin = ssd.ssd_chunk_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], None, chunk=64,
+                                dt_softplus=False, return_final_state=False)
+    torch.cuda.synchronize()
+    assert fin is None
+    y_ref, _ = oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None, None,
+                           dt_softplus=False)
+    assert y_err(y, y_ref) <= TOL["f32"]
+
+
+def test_scan_is_deterministic_and_batch_invariant():
+    """Bitwise repeatable, and a batch row computed inside a batch of 8 equals
+    the same row computed alone (the pages' batch-size invariance)."""
+    need_gpu()
+    w = make_tiny(8, 600, 8, 64, 128, 1, 256, "bf16", seed=77)
+    inp = make_inputs(w, with_initial_state=True)
+    announce("scan determinism / batch invariance")
+    y1, f1 = run_gpu(inp, w)
+    y2, f2 = run_gpu(inp, w)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+    b = 5
+    one = {k: (v[b:b + 1] if k in ("x", "dt", "B", "C", "h0") else v) for k, v in inp.items()}
+    ya, fa = run_gpu(one, w.with_(batch=1))
+    assert torch.equal(ya, y1[b:b + 1]) and torch.equal(fa, f1[b:b + 1])
+
+
+def test_scan_empty_inputs():
+    need_gpu()
+    import state_space_model_amd as ssd
+    announce("scan empty inputs")
+    dev = "cuda"
+    H, P, N = 4, 16, 16
+    A = -torch.ones(H, device=dev)
+    # batch 0
+    y, fin = ssd.ssd_chunk_scan(torch.zeros(0, 10, H, P, device=dev), torch.zeros(0, 10, H, device=dev),
+                                A, torch.zeros(0, 10, 1, N, device=dev),
+                                torch.zeros(0, 10, 1, N, device=dev), chunk=64)
+    assert y.shape == (0, 10, H, P) and fin.shape == (0, H, P, N)
+    # seqlen 0: the final state is the initial state, or zeros
+    h0 = torch.randn(2, H, P, N, device=dev)
+    e = dict(x=torch.zeros(2, 0, H, P, device=dev), dt=torch.zeros(2, 0, H, device=dev),
+             B=torch.zeros(2, 0, 1, N, device=dev))
+    y, fin = ssd.ssd_chunk_scan(e["x"], e["dt"], A, e["B"], e["B"].clone(), chunk=64,
+                                initial_state=h0)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, H, P) and torch.equal(fin, h0)
+    y, fin = ssd.ssd_chunk_scan(e["x"], e["dt"], A, e["B"], e["B"].clone(), chunk=64)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(fin) == 0
+
+
+def test_scan_rejects_unsupported_shapes_before_launch():
+    need_gpu()
+    import state_space_model_amd as ssd
+    dev = "cuda"
+    x = torch.zeros(1, 64, 2, 24, device=dev)
+    B = torch.zeros(1, 64, 1, 16, device=dev)
+    with pytest.raises(ssd.SSDError, match="UNSUPPORTED"):
+        ssd.ssd_chunk_scan(x, torch.zeros(1, 64, 2, device=dev), -torch.ones(2, device=dev), B, B,
+                           chunk=64)
+    x = torch.zeros(1, 64, 2, 16, device=dev, dtype=torch.bfloat16)
+    B = torch.zeros(1, 64, 1, 16, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(ssd.SSDError, match="UNSUPPORTED"):
+        ssd.ssd_chunk_scan(x, torch.zeros(1, 64, 2, device=dev), -torch.ones(2, device=dev), B, B,
+                           chunk=64)
