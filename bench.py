@@ -48,9 +48,10 @@ def phase_flops_per_token(w):
     """Algorithmic FLOP/token of each kernel of the scan."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     return {
+        "cb": G * (L + 1) * N,                                          # C B^T, causal half
         "chunk_state": H * 2 * N * P,                                   # chunk summary states
         "state_pass": H * 2 * P * N / L,                                # inter-chunk recurrence
-        "chunk_out": H * ((L + 1) * P + 2 * N * P) + G * (L + 1) * N,   # decay, C B^T, products
+        "chunk_out": H * ((L + 1) * P + 2 * N * P),                     # decay, products
     }
 
 
@@ -120,7 +121,7 @@ def bench_prefill(ssd, torch, w, steps, warmup):
     for i in range(steps):
         run(i, evs[i])
     torch.cuda.synchronize()
-    names = ["chunk_state", "state_pass", "chunk_out"]
+    names = ["cb", "chunk_state", "state_pass", "chunk_out"]
     phase_ms = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
                 for k, n in enumerate(names)}
     return {"ms": ms, "wall_ms": wall * 1e3 / steps, "phase_ms": phase_ms, "nsets": nsets,

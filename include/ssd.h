@@ -102,8 +102,9 @@ typedef struct {
 
 /*
  * Workspace bytes ssd_chunk_scan needs for `desc` (0 if desc is invalid).
- * It holds one float32 P x N state per (batch, head, chunk) plus one float32
- * decay per (batch, head, chunk): about 4*Bt*H*ceil(T/L)*(P*N+1) bytes.
+ * It holds one float32 P x N state and one float32 decay per (batch, head,
+ * chunk), and the float32 L x L matrix C B^T of every (batch, chunk, group):
+ * about 4*Bt*ceil(T/L)*(H*(P*N+1) + G*L*L) bytes.
  */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc);
 
@@ -139,10 +140,12 @@ ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float*
  * it must hold `n_events` created HIP events; event k is recorded on `stream`
  * before phase k and event n_phases after the last one (n_phases =
  * SSD_SCAN_PHASES).  Used by the benchmark to time each kernel of the scan on
- * the stream it runs on.  n_events < SSD_SCAN_PHASES + 1 is SSD_ERR_INVALID_ARG.
- * Phases: 0 chunk states, 1 state passing, 2 chunk outputs.
+ * the stream it runs on.  n_events < SSD_SCAN_PHASES + 1, or a NULL event among
+ * the first SSD_SCAN_PHASES + 1, is SSD_ERR_INVALID_ARG.
+ * Phases: 0 C B^T per chunk, 1 chunk states, 2 state passing, 3 chunk outputs
+ * (a phase may be empty on some paths: its two events then coincide).
  */
-#define SSD_SCAN_PHASES 3
+#define SSD_SCAN_PHASES 4
 ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const float* dt,
                                 const float* dt_bias, const float* A, const void* B,
                                 const void* C, const float* D, const float* initial_state,

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(_HERE, "libssd.so")
 SSD_OK = 0
 SSD_F32 = 0
 SSD_BF16 = 1
-SSD_SCAN_PHASES = 3
+SSD_SCAN_PHASES = 4
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
                 4: "SSD_ERR_ALIGNMENT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE",
                 7: "SSD_ERR_HIP"}
@@ -172,6 +172,9 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     if phase_events is None:
         st = lib.ssd_chunk_scan(*args)
     else:
+        for e in phase_events:  # torch creates the HIP event at its first record
+            if not e.cuda_event:
+                e.record()
         evs = (ctypes.c_void_p * len(phase_events))(*[ctypes.c_void_p(e.cuda_event)
                                                       for e in phase_events])
         st = lib.ssd_chunk_scan_timed(*args, evs, len(phase_events))

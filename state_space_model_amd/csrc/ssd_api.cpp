@@ -49,7 +49,7 @@ inline bool limits_ok(float lo, float hi) { return !isnan(lo) && !isnan(hi) && l
 struct ScanSizes {
   int64_t Nc = 0;
   int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0;  // element counts
-  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_total = 0;
+  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_cb_bytes = 0, ws_total = 0;
 };
 
 ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
@@ -76,9 +76,15 @@ ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
     return SSD_ERR_UNSUPPORTED;
   // one workgroup per (batch, chunk, head): the grid must fit a 32-bit x-dimension
   if (units > INT32_MAX || s->n_x > (INT64_MAX / 8)) return SSD_ERR_UNSUPPORTED;
+  int64_t bcg = 0, ll = 0, cb_elems = 0;
+  if (!mul_ok(d->batch, Nc, &bcg) || !mul_ok(bcg, d->ngroups, &bcg) ||
+      !mul_ok(d->chunk, d->chunk, &ll) || !mul_ok(bcg, ll, &cb_elems) ||
+      !mul_ok(cb_elems, 4, &tmp))
+    return SSD_ERR_UNSUPPORTED;
   s->ws_state_bytes = round_up((size_t)ws_elems * 4, kAlign);
   s->ws_alpha_bytes = round_up((size_t)units * 4, kAlign);
-  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes;
+  s->ws_cb_bytes = round_up((size_t)cb_elems * 4, kAlign);
+  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes + s->ws_cb_bytes;
   return SSD_OK;
 }
 
@@ -90,7 +96,11 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   ScanSizes s;
   ssd_status st = check_scan_desc(desc, &s);
   if (st != SSD_OK) return st;
-  if (events && n_events < SSD_SCAN_PHASES + 1) return SSD_ERR_INVALID_ARG;
+  if (events) {
+    if (n_events < SSD_SCAN_PHASES + 1) return SSD_ERR_INVALID_ARG;
+    for (int k = 0; k <= SSD_SCAN_PHASES; ++k)
+      if (!events[k]) return SSD_ERR_INVALID_ARG;
+  }
   const bool work = desc->batch > 0 && desc->seqlen > 0;
   if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_INVALID_ARG;
   if (!work && desc->batch > 0 && !A) return SSD_ERR_INVALID_ARG;
@@ -136,6 +146,8 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   a.h0 = initial_state; a.y = y; a.final_state = final_state;
   a.ws_state = static_cast<float*>(workspace);
   a.ws_alpha = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws_state_bytes);
+  a.ws_cb = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws_state_bytes +
+                                     s.ws_alpha_bytes);
   a.Bt = desc->batch; a.T = desc->seqlen; a.H = desc->nheads; a.G = desc->ngroups;
   a.L = desc->chunk; a.Nc = s.Nc;
   a.softplus = desc->dt_softplus ? 1 : 0;

@@ -20,6 +20,7 @@ struct ScanArgs {
   float* final_state;     // [Bt,H,P,N] or null
   float* ws_state;        // [Bt,H,Nc,P,N]: chunk summary states, then entering states
   float* ws_alpha;        // [Bt,H,Nc]: exp(total decay of the chunk)
+  float* ws_cb;           // [Bt,Nc,G,L,L]: C B^T of each chunk (causal 16x16 tiles)
   int64_t Bt, T, H, G, L, Nc;
   int32_t softplus;
   float dt_min, dt_max;
@@ -46,9 +47,12 @@ bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16);
 bool step_shape_supported(int64_t P, int64_t N);
 
 // Launch the whole scan (Bt*T > 0) on `stream`.  `events` (may be null) gets
-// one record before each of the 3 phases and one after the last.
+// one record before each of the 4 phases and one after the last.
 hipError_t launch_scan_f32(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* events);
 hipError_t launch_scan_bf16(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* events);
+
+// Inter-chunk recurrence over the workspace states (both io types).
+hipError_t launch_state_pass(const ScanArgs& a, int P, int N, hipStream_t stream);
 
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);

@@ -1,8 +1,539 @@
-// float32 instantiation of the chunked SSD scan kernels (x, B, C, y in float32).
-#include "ssd_prefill_impl.h"
+// Chunked SSD scan (prefill) for gfx950, float32 x/B/C/y.
+//
+// Source: "Compiler-First State Space Duality and Portable O(1)
+// Autoregressive Caching", Background (Eq. 3, inter-chunk recurrence), SSD
+// properties ("diagonal state matrix", "chunked recurrence") and
+// Implementation ("static masking": prefix sum, subtraction, mask and
+// exponentiation fused around the contractions; "precision management": the
+// highest matmul precision -- here full float32 matrix-core products, there is
+// no reduced-precision float32 mode on gfx950).
+//
+// Per (batch b, chunk c of L tokens, head h; g = B/C group of h), with
+// Delta_l the clipped softplus step, cum_l = sum_{k<=l} Delta_k A[h]:
+//   phase 0  S   = C_c B_c^T                       (once per (b, c, g), causal tiles)
+//   phase 1  S_c = sum_l exp(cum_last - cum_l) Delta_l x_l (x) B_l,  alpha_c = exp(cum_last)
+//   phase 2  h_{c-1} for every chunk               (ssd_state_pass.hip)
+//   phase 3  y_i = exp(cum_i) C_i h_{c-1}^T
+//                + sum_{j<=i} S[i][j] exp(cum_i - cum_j) Delta_j x_j + D x_i
+// The decay factor exp(cum_i - cum_j) is formed in registers as each score
+// tile is consumed; the causal mask is a select taken before the exponential.
+//
+// Matrix-core layout (v_mfma_f32_16x16x4_f32): lane l holds one A element
+// A[l%16][k], one B element B[k][l%16] and four outputs D[4(l/16)+r][l%16].
+// The contraction index is free to permute, so for contractions over a
+// contiguous dimension (n in C B^T and C h^T, j in S x) lane l uses
+// k = 16*blk + 4*(l/16) + kk, kk = 0..3: each lane then reads one float4 of
+// plain row-major data per four instructions.
+#include "ssd_prefill_common.h"
 
 namespace ssd {
-hipError_t launch_scan_f32(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* ev) {
-  return prefill::launch_scan<float>(a, P, N, stream, ev);
+namespace prefill {
+namespace {
+
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// ---------------------------------------------------------------------------
+// Phase 0: S = C B^T for the causal 16x16 tiles of every (b, c, g).
+// One wavefront computes one tile (I, J), J <= I.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void cb_tile_f32(const ScanArgs& a, int ntiles, int64_t block) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
+  const int64_t item = block * 4 + wave;
+  const int64_t bcg = item / ntiles;
+  if (bcg >= a.Bt * a.Nc * a.G) return;
+  const int t = (int)(item % ntiles);
+  // triangular index t -> (I, J), 0 <= J <= I
+  int I = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
+  while ((I + 1) * (I + 2) / 2 <= t) ++I;
+  while (I * (I + 1) / 2 > t) --I;
+  const int J = t - I * (I + 1) / 2;
+  const int64_t g = bcg % a.G, bc = bcg / a.G, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t t0 = c * a.L;
+  const int Lc = chunk_len(a, c);
+  if (16 * I >= Lc) return;
+  const float* Cg = reinterpret_cast<const float*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
+  const float* Bg = reinterpret_cast<const float*>(a.B) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
+  const int64_t rs = a.G * N;
+  const int ri = 16 * I + r16, rj = 16 * J + r16;
+  float4 cf[N / 16], bf[N / 16];
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb) {
+    cf[nb] = ri < Lc ? ld4(Cg + ri * rs + nb * 16) : zero4();
+    bf[nb] = rj < Lc ? ld4(Bg + rj * rs + nb * 16) : zero4();
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nb = 0; nb < N / 16; ++nb) {
+    acc = mma(cf[nb].x, bf[nb].x, acc);
+    acc = mma(cf[nb].y, bf[nb].y, acc);
+    acc = mma(cf[nb].z, bf[nb].z, acc);
+    acc = mma(cf[nb].w, bf[nb].w, acc);
+  }
+  float* S = a.ws_cb + bcg * a.L * a.L;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) S[(int64_t)(16 * I + 4 * q + r) * a.L + 16 * J + r16] = acc[r];
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1: chunk summary states S_c[p][n] = sum_l (x_l[p] w_l) B_l[n],
+// w_l = Delta_l exp(cum_last - cum_l).  A workgroup covers NW of the N state
+// columns.  Tokens go through LDS in double-buffered blocks of KB: the global
+// loads of block k+1 are in flight while block k feeds the matrix cores.
+// ---------------------------------------------------------------------------
+template <int P, int N, int NW>
+struct ChunkStateShape {
+  static constexpr int KB = 32;
+  static constexpr int XS = P + 4, BS = NW + 4;  // = 4 (mod 8): conflict-free fragment reads
+};
+
+template <int P, int N, int NW>
+__device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int64_t block, int64_t nblocks,
+                                                float* s_d, float* s_cum, float* s_w, float* s_wsum,
+                                                float* s_x0, float* s_x1, float* s_b0, float* s_b1) {
+  using Sh = ChunkStateShape<P, N, NW>;
+  constexpr int NSPLIT = N / NW;
+  constexpr int KB = Sh::KB, XS = Sh::XS, BS = Sh::BS;
+  constexpr int TP = P / 16, TN = NW / 16, TT = TP * TN;
+  // output tiles of one wavefront: NPT p-tiles x NNT n-tiles
+  constexpr int TPW = TT >= 4 ? TT / 4 : 1;
+  constexpr int NNT = TPW < TN ? TPW : TN;
+  constexpr int NPT = TPW / NNT;
+  constexpr int XQ = P / 4, BQ = NW / 4;                  // float4 per staged row
+  constexpr int XL = (KB * XQ + kThreads - 1) / kThreads;  // float4 loads per thread
+  constexpr int BL = (KB * BQ + kThreads - 1) / kThreads;
+
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t u = xcd_remap(block, nblocks);
+  const int ns = (int)(u % NSPLIT);
+  const int64_t u2 = u / NSPLIT;
+  const int64_t h = u2 % a.H, bc = u2 / a.H, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t g = h / (a.H / a.G);
+  const int64_t t0 = c * a.L;
+  const int Lc = chunk_len(a, c);
+  const float* xg = reinterpret_cast<const float*>(a.x) + ((b * a.T + t0) * a.H + h) * P;
+  const float* Bg = reinterpret_cast<const float*>(a.B) + ((b * a.T + t0) * a.G + g) * N + ns * NW;
+  const int64_t xstride = a.H * P, bstride = a.G * N;
+
+  auto load_block = [&](int kb0, float4 (&xr)[XL], float4 (&br)[BL]) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int e = tid + i * kThreads, l = e / XQ, m = e % XQ;
+      xr[i] = (e < KB * XQ && kb0 + l < Lc) ? ld4(&xg[(kb0 + l) * xstride + 4 * m]) : zero4();
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int e = tid + i * kThreads, l = e / BQ, m = e % BQ;
+      br[i] = (e < KB * BQ && kb0 + l < Lc) ? ld4(&Bg[(kb0 + l) * bstride + 4 * m]) : zero4();
+    }
+  };
+  auto store_block = [&](int kb0, const float4 (&xr)[XL], const float4 (&br)[BL], float* sx,
+                         float* sb) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int e = tid + i * kThreads, l = e / XQ, m = e % XQ;
+      if (e < KB * XQ) {
+        const float w = s_w[kb0 + l];
+        float4 v = xr[i];
+        v.x *= w; v.y *= w; v.z *= w; v.w *= w;
+        st4(&sx[l * XS + 4 * m], v);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BL; ++i) {
+      const int e = tid + i * kThreads, l = e / BQ, m = e % BQ;
+      if (e < KB * BQ) st4(&sb[l * BS + 4 * m], br[i]);
+    }
+  };
+  // two token blocks are always in flight ahead of the one being consumed
+  float4 xA[XL], bA[BL], xB[XL], bB[BL];
+  load_block(0, xA, bA);
+  if (KB < Lc) load_block(KB, xB, bB);
+
+  chunk_delta_cumsum(a, b, c, h, s_d, s_cum, s_wsum);
+  const float cum_last = s_cum[Lc - 1];
+  for (int l = tid; l < (int)a.L; l += kThreads)
+    s_w[l] = (l < Lc) ? s_d[l] * fast_exp(cum_last - s_cum[l]) : 0.0f;
+  if (tid == 0 && ns == 0) a.ws_alpha[(b * a.H + h) * a.Nc + c] = fast_exp(cum_last);
+  __syncthreads();
+
+  const bool active = TT >= 4 || wave < TT;   // uniform per wavefront
+  const int tile0 = wave * TPW;
+  const int pt0 = tile0 / TN, nt0 = tile0 % TN;
+  f32x4 acc[NPT][NNT];
+#pragma unroll
+  for (int ip = 0; ip < NPT; ++ip)
+#pragma unroll
+    for (int in = 0; in < NNT; ++in) acc[ip][in] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const float* sx, const float* sb) {
+    if (!active) return;
+    // token of k-slot (ks, q, kk) = ks + 4q + kk; all fragments of the block are
+    // read before its MFMAs, so the LDS latency is paid once per block
+    const float* xa = &sx[4 * q * XS + pt0 * 16 + r16];
+    const float* xb = &sb[4 * q * BS + nt0 * 16 + r16];
+    float av[KB / 4][NPT], bv[KB / 4][NNT];
+#pragma unroll
+    for (int k = 0; k < KB / 4; ++k) {
+      const int row = (k / 4) * 16 + (k % 4);
+#pragma unroll
+      for (int ip = 0; ip < NPT; ++ip) av[k][ip] = xa[row * XS + ip * 16];
+#pragma unroll
+      for (int in = 0; in < NNT; ++in) bv[k][in] = xb[row * BS + in * 16];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < KB / 4; ++k)
+#pragma unroll
+      for (int ip = 0; ip < NPT; ++ip)
+#pragma unroll
+        for (int in = 0; in < NNT; ++in) acc[ip][in] = mma(av[k][ip], bv[k][in], acc[ip][in]);
+  };
+  for (int kb0 = 0; kb0 < Lc; kb0 += 2 * KB) {
+    store_block(kb0, xA, bA, s_x0, s_b0);
+    __syncthreads();
+    if (kb0 + 2 * KB < Lc) load_block(kb0 + 2 * KB, xA, bA);
+    compute(s_x0, s_b0);
+    if (kb0 + KB >= Lc) break;
+    store_block(kb0 + KB, xB, bB, s_x1, s_b1);
+    __syncthreads();
+    if (kb0 + 3 * KB < Lc) load_block(kb0 + 3 * KB, xB, bB);
+    compute(s_x1, s_b1);
+  }
+  if (active) {
+    float* out = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) + ns * NW;
+#pragma unroll
+    for (int ip = 0; ip < NPT; ++ip)
+#pragma unroll
+      for (int in = 0; in < NNT; ++in)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          out[((pt0 + ip) * 16 + 4 * q + r) * N + (nt0 + in) * 16 + r16] = acc[ip][in][r];
+  }
+}
+
+// Phases 0 and 1 share one launch: the first ncb workgroups compute C B^T
+// tiles (short-lived), the rest compute chunk states.  ncb is a multiple of
+// 8, so the chunk-state workgroups keep their XCD-aware numbering.
+template <int P, int N, int NW>
+__global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_f32(ScanArgs a, int ntiles,
+                                                                     int64_t ncb) {
+  using Sh = ChunkStateShape<P, N, NW>;
+  __shared__ float s_d[kMaxL], s_cum[kMaxL], s_w[kMaxL], s_wsum[4];
+  __shared__ __attribute__((aligned(16))) float s_x[2][Sh::KB * Sh::XS];
+  __shared__ __attribute__((aligned(16))) float s_b[2][Sh::KB * Sh::BS];
+  if ((int64_t)blockIdx.x < ncb) {
+    cb_tile_f32<N>(a, ntiles, blockIdx.x);
+    return;
+  }
+  chunk_state_f32<P, N, NW>(a, blockIdx.x - ncb, gridDim.x - ncb, s_d, s_cum, s_w, s_wsum,
+                            s_x[0], s_x[1], s_b[0], s_b[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Phase 3: chunk outputs.  A workgroup covers PW of the P head columns of one
+// (b, c, h).  Wavefront w owns the 16-row tiles row_tile_of(w, k), k < RT,
+// and keeps all their accumulators live, so every h and x fragment it loads
+// serves all of its row tiles.
+//
+// Decay factors.  For a row tile in 64-token block R > 0 and a key j in an
+// earlier block, exp(cum_i - cum_j) = exp(cum_i - cum_r) * exp(cum_r - cum_j)
+// with r = 64 R the first token of block R; both factors are <= 1.  The key
+// factors exp(cum_r - cum_j) Delta_j are tabulated in LDS once per workgroup
+// (one row per block boundary), the row factor is one exponential per lane
+// and row tile.  Inside the row tile's own block the decay is exponentiated
+// element by element, with the causal mask selected first.
+// ---------------------------------------------------------------------------
+template <int P, int N, int PW, int LMAX>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void k_chunk_out_f32(ScanArgs a) {
+  constexpr int PSPLIT = P / PW, TP = PW / 16;
+  constexpr int XS = PW + 4;   // = 4 (mod 8): conflict-free B-fragment reads
+  constexpr int NBLK = LMAX / 64;
+  constexpr int RT = NBLK;     // row tiles per wavefront
+  __shared__ __attribute__((aligned(16))) float s_d[LMAX];
+  __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
+  __shared__ float s_wsum[4];
+  __shared__ __attribute__((aligned(16))) float s_w[(NBLK - 1) * LMAX];  // key factors
+  __shared__ __attribute__((aligned(16))) float s_x[LMAX * XS];
+
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t u = xcd_remap(blockIdx.x, gridDim.x);
+  const int ps = (int)(u % PSPLIT);
+  const int64_t u2 = u / PSPLIT;
+  const int64_t h = u2 % a.H, bc = u2 / a.H, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t g = h / (a.H / a.G);
+  const int64_t t0 = c * a.L;
+  const int Lc = chunk_len(a, c);
+  const int nrt = (Lc + 15) / 16;
+  const int p0 = ps * PW;
+  const float* xg = reinterpret_cast<const float*>(a.x);
+
+  // stage x (this workgroup's PW columns of every chunk row); all loads of a
+  // batch are issued before any LDS store
+  {
+    constexpr int XQ = PW / 4, XLB = 8;
+    const int nx = nrt * 16 * XQ;
+    for (int e0 = 0; e0 < nx; e0 += XLB * kThreads) {
+      float4 v[XLB];
+#pragma unroll
+      for (int i = 0; i < XLB; ++i) {
+        const int e = e0 + i * kThreads + tid, j = e / XQ, m = e % XQ;
+        v[i] = (e < nx && j < Lc) ? ld4(&xg[((b * a.T + t0 + j) * a.H + h) * P + p0 + 4 * m])
+                                  : zero4();
+      }
+#pragma unroll
+      for (int i = 0; i < XLB; ++i) {
+        const int e = e0 + i * kThreads + tid, j = e / XQ, m = e % XQ;
+        if (e < nx) st4(&s_x[j * XS + 4 * m], v[i]);
+      }
+    }
+  }
+  chunk_delta_cumsum(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
+  for (int e = tid; e < (NBLK - 1) * LMAX; e += kThreads) {
+    const int R = e / LMAX + 1, j = e % LMAX;
+    const int r = min(64 * R, Lc - 1);
+    s_w[e] = (j < r) ? fast_exp(s_cum[r] - s_cum[j]) * s_d[j] : 0.0f;
+  }
+  __syncthreads();
+
+  // per row tile k of this wavefront: validity (uniform), query row, decay data
+  int Ik[RT];
+  bool vk[RT];
+  float cumk[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    Ik[k] = row_tile_of(wave, k);
+    vk[k] = Ik[k] < nrt;
+    const int ri = 16 * Ik[k] + r16;
+    cumk[k] = s_cum[min(ri, Lc - 1)];
+  }
+  f32x4 acc[RT][TP];
+#pragma unroll
+  for (int k = 0; k < RT; ++k)
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- inter-chunk term: acc[k] += sum_n (exp(cum_i) C[i][n]) h_{c-1}[p][n] ----
+  {
+    const float* Cg = reinterpret_cast<const float*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
+    const int64_t crs = a.G * N;
+    const float* hp = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) +
+                      (int64_t)(p0 + r16) * N + 4 * q;
+    float sc[RT];
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const int ri = 16 * Ik[k] + r16;
+      sc[k] = (vk[k] && ri < Lc) ? fast_exp(cumk[k]) : 0.0f;
+    }
+    auto load_nb = [&](int nb, float4 (&hv)[TP], float4 (&cv)[RT]) {
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) hv[pt] = ld4(hp + pt * 16 * N + nb * 16);
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        const int ri = 16 * Ik[k] + r16;
+        cv[k] = (vk[k] && ri < Lc) ? ld4(Cg + ri * crs + nb * 16) : zero4();
+      }
+    };
+    auto mma_nb = [&](const float4 (&hv)[TP], const float4 (&cv)[RT]) {
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        if (!vk[k]) continue;
+        const float4 c4 = make_float4(cv[k].x * sc[k], cv[k].y * sc[k], cv[k].z * sc[k],
+                                      cv[k].w * sc[k]);
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt) {
+          acc[k][pt] = mma(c4.x, hv[pt].x, acc[k][pt]);
+          acc[k][pt] = mma(c4.y, hv[pt].y, acc[k][pt]);
+          acc[k][pt] = mma(c4.z, hv[pt].z, acc[k][pt]);
+          acc[k][pt] = mma(c4.w, hv[pt].w, acc[k][pt]);
+        }
+      }
+    };
+    float4 hA[TP], cA[RT], hB[TP], cB[RT];
+    load_nb(0, hA, cA);
+#pragma unroll 1
+    for (int nb = 0; nb < N / 16; nb += 2) {
+      const bool two = nb + 1 < N / 16;     // N / 16 is 1 for N = 16
+      if (two) load_nb(nb + 1, hB, cB);
+      mma_nb(hA, cA);
+      if (!two) break;
+      if (nb + 2 < N / 16) load_nb(nb + 2, hA, cA);
+      mma_nb(hB, cB);
+    }
+  }
+
+  // ---- intra-chunk term: row tile by row tile, one block of 64 keys at a time ----
+  const float* S = a.ws_cb + ((b * a.Nc + c) * a.G + g) * a.L * a.L;
+  const float* xq = &s_x[4 * q * XS + r16];   // + key * XS + pt * 16
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    if (!vk[k]) continue;                      // uniform
+    const int I = Ik[k], R = I >> 2;
+    const int ri = 16 * I + r16;
+    const float cum_i = cumk[k];
+    const float* sr = S + (int64_t)ri * a.L + 4 * q;
+    auto load_s = [&](int jb, float4 (&st)[4]) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) st[t] = ld4(sr + 64 * jb + 16 * min(t, I - 4 * jb));
+    };
+    const float u_i = R > 0 ? fast_exp(cum_i - s_cum[64 * R]) : 0.0f;
+    auto block = [&](int jb, const float4 (&st)[4]) {
+      float xv[4][4][TP];   // [key tile][kk][pt]
+      if (jb < R) {
+        // earlier key block: factored decay u_i * s_w[R-1][j]
+        const float* wrow = &s_w[(R - 1) * LMAX + 64 * jb + 4 * q];
+        float4 w4[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          w4[t] = ld4(wrow + 16 * t);
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int pt = 0; pt < TP; ++pt) xv[t][kk][pt] = xq[(64 * jb + 16 * t + kk) * XS + pt * 16];
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float m0 = st[t].x * u_i * w4[t].x, m1 = st[t].y * u_i * w4[t].y;
+          const float m2 = st[t].z * u_i * w4[t].z, m3 = st[t].w * u_i * w4[t].w;
+#pragma unroll
+          for (int pt = 0; pt < TP; ++pt) {
+            acc[k][pt] = mma(m0, xv[t][0][pt], acc[k][pt]);
+            acc[k][pt] = mma(m1, xv[t][1][pt], acc[k][pt]);
+            acc[k][pt] = mma(m2, xv[t][2][pt], acc[k][pt]);
+            acc[k][pt] = mma(m3, xv[t][3][pt], acc[k][pt]);
+          }
+        }
+      } else {
+        // the row tile's own block, up to the diagonal: masked exponentials
+        const int nt = I - 4 * R + 1;           // key tiles up to the diagonal (uniform)
+        float4 cj[4], dj[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < nt) {
+            const int j0 = 64 * jb + 16 * t + 4 * q;
+            cj[t] = ld4(&s_cum[j0]);
+            dj[t] = ld4(&s_d[j0]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+              for (int pt = 0; pt < TP; ++pt) xv[t][kk][pt] = xq[(64 * jb + 16 * t + kk) * XS + pt * 16];
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (t < nt) {
+            const int j0 = 64 * jb + 16 * t + 4 * q;
+            const float m0 = (j0 + 0 <= ri) ? st[t].x * fast_exp(cum_i - cj[t].x) * dj[t].x : 0.0f;
+            const float m1 = (j0 + 1 <= ri) ? st[t].y * fast_exp(cum_i - cj[t].y) * dj[t].y : 0.0f;
+            const float m2 = (j0 + 2 <= ri) ? st[t].z * fast_exp(cum_i - cj[t].z) * dj[t].z : 0.0f;
+            const float m3 = (j0 + 3 <= ri) ? st[t].w * fast_exp(cum_i - cj[t].w) * dj[t].w : 0.0f;
+#pragma unroll
+            for (int pt = 0; pt < TP; ++pt) {
+              acc[k][pt] = mma(m0, xv[t][0][pt], acc[k][pt]);
+              acc[k][pt] = mma(m1, xv[t][1][pt], acc[k][pt]);
+              acc[k][pt] = mma(m2, xv[t][2][pt], acc[k][pt]);
+              acc[k][pt] = mma(m3, xv[t][3][pt], acc[k][pt]);
+            }
+          }
+        }
+      }
+    };
+    // score tiles double-buffered in two fixed register sets
+    float4 sa[4], sb[4];
+    load_s(0, sa);
+    for (int jb = 0; jb <= R; jb += 2) {
+      if (jb + 1 <= R) load_s(jb + 1, sb);
+      block(jb, sa);
+      if (jb + 1 > R) break;
+      if (jb + 2 <= R) load_s(jb + 2, sa);
+      block(jb + 1, sb);
+    }
+  }
+
+  // ---- skip term and store ----
+  const float Dh = a.D ? a.D[h] : 0.0f;
+  float* yg = reinterpret_cast<float*>(a.y);
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    if (!vk[k]) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * Ik[k] + 4 * q + r;
+      if (i < Lc) {
+        const int64_t row = ((b * a.T + t0 + i) * a.H + h) * P + p0;
+#pragma unroll
+        for (int pt = 0; pt < TP; ++pt)
+          yg[row + pt * 16 + r16] = acc[k][pt][r] + Dh * s_x[i * XS + pt * 16 + r16];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+template <int P, int N>
+hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
+  // phases 0 and 1 (C B^T, chunk states) in one launch
+  if ((e = rec(0)) != hipSuccess) return e;
+  if ((e = rec(1)) != hipSuccess) return e;
+  const int nrt = (int)((a.L + 15) / 16), ntiles = nrt * (nrt + 1) / 2;
+  const int64_t items = a.Bt * a.Nc * a.G * ntiles;
+  const int64_t ncb = ((items + 3) / 4 + 7) / 8 * 8;
+  constexpr int NW = N < 64 ? N : 64;
+  const int64_t units1 = a.Bt * a.Nc * a.H * (N / NW);
+  hipLaunchKernelGGL((k_cb_and_chunk_state_f32<P, N, NW>), dim3((unsigned)(ncb + units1)),
+                     dim3(kThreads), 0, stream, a, ntiles, ncb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // phase 2: inter-chunk recurrence
+  if ((e = rec(2)) != hipSuccess) return e;
+  if ((e = launch_state_pass(a, P, N, stream)) != hipSuccess) return e;
+  // phase 3: outputs
+  if ((e = rec(3)) != hipSuccess) return e;
+  constexpr int PW = P < 32 ? P : 32;
+  const int64_t units3 = a.Bt * a.Nc * a.H * (P / PW);
+  if (a.L <= 256)
+    hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 256>), dim3((unsigned)units3), dim3(kThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 512>), dim3((unsigned)units3), dim3(kThreads),
+                       0, stream, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return rec(4);
+}
+
+template <int P>
+hipError_t launch_p(const ScanArgs& a, int N, hipStream_t s, hipEvent_t* ev) {
+  switch (N) {
+    case 16: return launch_pn<P, 16>(a, s, ev);
+    case 32: return launch_pn<P, 32>(a, s, ev);
+    case 64: return launch_pn<P, 64>(a, s, ev);
+    case 128: return launch_pn<P, 128>(a, s, ev);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+}  // namespace prefill
+
+hipError_t launch_scan_f32(const ScanArgs& a, int P, int N, hipStream_t s, hipEvent_t* ev) {
+  switch (P) {
+    case 16: return prefill::launch_p<16>(a, N, s, ev);
+    case 32: return prefill::launch_p<32>(a, N, s, ev);
+    case 64: return prefill::launch_p<64>(a, N, s, ev);
+    case 128: return prefill::launch_p<128>(a, N, s, ev);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace ssd

@@ -1,4 +1,4 @@
-// Chunked SSD scan (prefill) for gfx950: three kernels on one stream.
+// Chunked SSD scan (prefill) for gfx950, bfloat16 x/B/C/y: first version.
 //
 // Source: "Compiler-First State Space Duality and Portable O(1)
 // Autoregressive Caching", Background (Eq. 3 and the inter-chunk recurrence
@@ -23,45 +23,11 @@
 // Included once per io type by ssd_prefill_f32.hip / ssd_prefill_bf16.hip.
 #pragma once
 
-#include "ssd_device.h"
-#include "ssd_launch.h"
+#include "ssd_prefill_common.h"
 
 namespace ssd {
 namespace prefill {
 namespace {  // each io-type translation unit keeps its own copy
-
-constexpr int kThreads = 256;  // 4 wavefronts
-constexpr int kMaxL = 512;
-
-// Step Delta and the inclusive prefix sum of a = Delta*A over the chunk's L
-// tokens; tokens at or past T get Delta = 0 (so the sum stays flat there).
-// Every thread of the block must call this; it ends with a barrier.
-__device__ __forceinline__ void chunk_delta_cumsum(const ScanArgs& a, int64_t b, int64_t c,
-                                                   int64_t h, float* s_d, float* s_cum,
-                                                   float* s_wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = (int)a.L;
-  const int64_t t0 = c * a.L;
-  const float Ah = a.A[h];
-  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  const int l0 = 2 * tid, l1 = 2 * tid + 1;
-  float d0 = 0.0f, d1 = 0.0f;
-  if (l0 < L && t0 + l0 < a.T)
-    d0 = delta_of(a.dt[(b * a.T + t0 + l0) * a.H + h] + bias, a.softplus, a.dt_min, a.dt_max);
-  if (l1 < L && t0 + l1 < a.T)
-    d1 = delta_of(a.dt[(b * a.T + t0 + l1) * a.H + h] + bias, a.softplus, a.dt_min, a.dt_max);
-  const float a0 = d0 * Ah, a1 = d1 * Ah;
-  const float local = a0 + a1;
-  const float incl = wave_inclusive_scan(local);
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  float off = 0.0f;
-  for (int w = 0; w < wave; ++w) off += s_wsum[w];
-  const float excl = off + (incl - local);
-  if (l0 < L) { s_d[l0] = d0; s_cum[l0] = excl + a0; }
-  if (l1 < L) { s_d[l1] = d1; s_cum[l1] = excl + a0 + a1; }
-  __syncthreads();
-}
 
 struct Unit {
   int64_t b, c, h, g;
@@ -156,47 +122,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk_state(ScanArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Phase 1: sequential inter-chunk recurrence, element-wise over P x N.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const float* ws_alpha,
-                                                         const float* h0, float* final_state,
-                                                         int64_t nslices, int64_t Nc, int PN) {
-  const int64_t bh = blockIdx.x / nslices;
-  const int e4 = (int)(blockIdx.x % nslices) * kThreads + threadIdx.x;
-  const int PN4 = PN / 4;
-  if (e4 >= PN4) return;
-  float4* st = reinterpret_cast<float4*>(ws_state + bh * Nc * PN) + e4;
-  const float* al = ws_alpha + bh * Nc;
-  float4 hc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (h0) hc = reinterpret_cast<const float4*>(h0 + bh * PN)[e4];
-  int64_t c = 0;
-  for (; c + 4 <= Nc; c += 4) {
-    float4 s[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) s[k] = st[(c + k) * PN4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      st[(c + k) * PN4] = hc;
-      const float al_c = al[c + k];
-      hc.x = al_c * hc.x + s[k].x;
-      hc.y = al_c * hc.y + s[k].y;
-      hc.z = al_c * hc.z + s[k].z;
-      hc.w = al_c * hc.w + s[k].w;
-    }
-  }
-  for (; c < Nc; ++c) {
-    const float4 s = st[c * PN4];
-    st[c * PN4] = hc;
-    const float al_c = al[c];
-    hc.x = al_c * hc.x + s.x;
-    hc.y = al_c * hc.y + s.y;
-    hc.z = al_c * hc.z + s.z;
-    hc.w = al_c * hc.w + s.w;
-  }
-  if (final_state) reinterpret_cast<float4*>(final_state + bh * PN)[e4] = hc;
-}
-
-// ---------------------------------------------------------------------------
 // Phase 2: chunk outputs.
 //   y_i = exp(cum_i) C_i h_{c-1}^T + sum_{j<=i} (C_i . B_j) exp(cum_i - cum_j) d_j x_j + D x_i
 // Row tiles of 16 tokens are dealt to the 4 wavefronts in a snake order
@@ -204,10 +129,6 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const 
 // tile is computed transposed (S^T = B C^T) so that its accumulator layout is
 // directly the A operand of the following (S o decay) X product.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int row_tile_of(int wave, int k) {
-  return 4 * k + ((k & 1) ? 3 - wave : wave);
-}
-
 template <typename T, int P, int N, int RT>
 __global__ __launch_bounds__(kThreads) void k_chunk_out(ScanArgs a) {
   using M = Mfma<T>;
@@ -375,19 +296,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out(ScanArgs a) {
 // ---------------------------------------------------------------------------
 template <typename T, int P, int N>
 hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
+  hipError_t e;
+  auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
   const int64_t units = a.Bt * a.Nc * a.H;
-  if (ev) { hipError_t e = hipEventRecord(ev[0], stream); if (e != hipSuccess) return e; }
+  // phase 0 (C B^T) is computed inside the output kernel on this path
+  if ((e = rec(0)) != hipSuccess) return e;
+  if ((e = rec(1)) != hipSuccess) return e;
   hipLaunchKernelGGL((k_chunk_state<T, P, N>), dim3((unsigned)units), dim3(kThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) { e = hipEventRecord(ev[1], stream); if (e != hipSuccess) return e; }
-  const int PN = P * N;
-  const int64_t nsl = (PN / 4 + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(k_state_pass, dim3((unsigned)(a.Bt * a.H * nsl)), dim3(kThreads), 0, stream,
-                     a.ws_state, (const float*)a.ws_alpha, a.h0, a.final_state, nsl, a.Nc, PN);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) { e = hipEventRecord(ev[2], stream); if (e != hipSuccess) return e; }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = rec(2)) != hipSuccess) return e;
+  if ((e = launch_state_pass(a, P, N, stream)) != hipSuccess) return e;
+  if ((e = rec(3)) != hipSuccess) return e;
   const int rt_needed = (int)((a.L + 63) / 64);
   if (rt_needed <= 4) {
     hipLaunchKernelGGL((k_chunk_out<T, P, N, 4>), dim3((unsigned)units), dim3(kThreads), 0, stream, a);
@@ -398,10 +317,8 @@ hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
       return hipErrorInvalidValue;
     }
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (ev) { e = hipEventRecord(ev[3], stream); if (e != hipSuccess) return e; }
-  return hipSuccess;
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return rec(4);
 }
 
 template <typename T, int P>

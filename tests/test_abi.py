@@ -139,6 +139,8 @@ def test_scan_timed_needs_enough_events():
     d = desc()
     evs = (ctypes.c_void_p * 2)()
     assert lib.ssd_chunk_scan_timed(*fake_args(d), evs, 2) == INVALID
+    evs = (ctypes.c_void_p * 5)()  # enough slots, but NULL events
+    assert lib.ssd_chunk_scan_timed(*fake_args(d), evs, 5) == INVALID
 
 
 def test_empty_batch_is_a_noop():
