@@ -276,6 +276,31 @@ void k_chunk_out_f32(ScanArgs a) {
   const int p0 = ps * PW;
   const float* xg = reinterpret_cast<const float*>(a.x);
 
+  // row tiles of this wavefront (uniform) and the operands of the first state
+  // block of the inter-chunk term, in flight during the staging and prologue
+  int Ik[RT];
+  bool vk[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    Ik[k] = row_tile_of(wave, k);
+    vk[k] = Ik[k] < nrt;
+  }
+  const float* Cg = reinterpret_cast<const float*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
+  const int64_t crs = a.G * N;
+  const float* hp = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) +
+                    (int64_t)(p0 + r16) * N + 4 * q;
+  auto load_nb = [&](int nb, float4 (&hv)[TP], float4 (&cv)[RT]) {
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt) hv[pt] = ld4(hp + pt * 16 * N + nb * 16);
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const int ri = 16 * Ik[k] + r16;
+      cv[k] = (vk[k] && ri < Lc) ? ld4(Cg + ri * crs + nb * 16) : zero4();
+    }
+  };
+  float4 hA[TP], cA[RT], hB[TP], cB[RT];
+  load_nb(0, hA, cA);
+
   // stage x (this workgroup's PW columns of every chunk row); all loads of a
   // batch are issued before any LDS store
   {
@@ -304,17 +329,10 @@ void k_chunk_out_f32(ScanArgs a) {
   }
   __syncthreads();
 
-  // per row tile k of this wavefront: validity (uniform), query row, decay data
-  int Ik[RT];
-  bool vk[RT];
+  // decay data of this wavefront's query rows
   float cumk[RT];
 #pragma unroll
-  for (int k = 0; k < RT; ++k) {
-    Ik[k] = row_tile_of(wave, k);
-    vk[k] = Ik[k] < nrt;
-    const int ri = 16 * Ik[k] + r16;
-    cumk[k] = s_cum[min(ri, Lc - 1)];
-  }
+  for (int k = 0; k < RT; ++k) cumk[k] = s_cum[min(16 * Ik[k] + r16, Lc - 1)];
   f32x4 acc[RT][TP];
 #pragma unroll
   for (int k = 0; k < RT; ++k)
@@ -323,25 +341,12 @@ void k_chunk_out_f32(ScanArgs a) {
 
   // ---- inter-chunk term: acc[k] += sum_n (exp(cum_i) C[i][n]) h_{c-1}[p][n] ----
   {
-    const float* Cg = reinterpret_cast<const float*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
-    const int64_t crs = a.G * N;
-    const float* hp = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) +
-                      (int64_t)(p0 + r16) * N + 4 * q;
     float sc[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
       const int ri = 16 * Ik[k] + r16;
       sc[k] = (vk[k] && ri < Lc) ? fast_exp(cumk[k]) : 0.0f;
     }
-    auto load_nb = [&](int nb, float4 (&hv)[TP], float4 (&cv)[RT]) {
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) hv[pt] = ld4(hp + pt * 16 * N + nb * 16);
-#pragma unroll
-      for (int k = 0; k < RT; ++k) {
-        const int ri = 16 * Ik[k] + r16;
-        cv[k] = (vk[k] && ri < Lc) ? ld4(Cg + ri * crs + nb * 16) : zero4();
-      }
-    };
     auto mma_nb = [&](const float4 (&hv)[TP], const float4 (&cv)[RT]) {
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
@@ -357,8 +362,6 @@ void k_chunk_out_f32(ScanArgs a) {
         }
       }
     };
-    float4 hA[TP], cA[RT], hB[TP], cB[RT];
-    load_nb(0, hA, cA);
 #pragma unroll 1
     for (int nb = 0; nb < N / 16; nb += 2) {
       const bool two = nb + 1 < N / 16;     // N / 16 is 1 for N = 16
