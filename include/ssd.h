@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
   SSD_OK = 0,
@@ -102,11 +102,31 @@ typedef struct {
 
 /*
  * Workspace bytes ssd_chunk_scan needs for `desc` (0 if desc is invalid).
- * It holds one float32 P x N state and one float32 decay per (batch, head,
- * chunk), and the float32 L x L matrix C B^T of every (batch, chunk, group):
- * about 4*Bt*ceil(T/L)*(H*(P*N+1) + G*L*L) bytes.
+ * Both schedules (see ssd_chunk_scan_schedule) hold the float32 L x L matrix
+ * C B^T of every (batch, chunk, group): 4*Bt*ceil(T/L)*G*L*L bytes.  The
+ * phased schedule adds one float32 P x N state and one float32 decay per
+ * (batch, head, chunk): 4*Bt*ceil(T/L)*H*(P*N+1) bytes; the chain schedule
+ * adds a bfloat16 transposed copy of B per (batch, chunk, group):
+ * 2*Bt*ceil(T/L)*G*N*L bytes.  Each region is rounded up to 256 bytes.
  */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc);
+
+/*
+ * Which schedule ssd_chunk_scan runs for `desc`; a negative ssd_status if the
+ * descriptor is invalid.  Both compute bit-identical results (the same
+ * matrix-core instructions on the same operands in the same order for every
+ * element), so the choice, which depends on the batch size, never changes an
+ * answer; the pages' batch-size invariance holds across it.
+ *   SSD_SCHEDULE_PHASED  one workgroup per (batch, chunk, head) and phase:
+ *                        C B^T, chunk states, state pass, outputs
+ *   SSD_SCHEDULE_CHAIN   bfloat16 io, P in {32, 64}, N in {64, 128}, L <= 256
+ *                        and batch*heads >= 256: a C B^T / B^T pre-pass, then
+ *                        one workgroup per (batch, head) walks the chunks in
+ *                        order with its state on chip
+ */
+#define SSD_SCHEDULE_PHASED 0
+#define SSD_SCHEDULE_CHAIN 1
+int32_t ssd_chunk_scan_schedule(const ssd_scan_desc* desc);
 
 /*
  * Chunked SSD scan over a whole sequence (prefill).
@@ -143,7 +163,9 @@ ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float*
  * the stream it runs on.  n_events < SSD_SCAN_PHASES + 1, or a NULL event among
  * the first SSD_SCAN_PHASES + 1, is SSD_ERR_INVALID_ARG.
  * Phases: 0 C B^T per chunk, 1 chunk states, 2 state passing, 3 chunk outputs
- * (a phase may be empty on some paths: its two events then coincide).
+ * (a phase may be empty on some paths: its two events then coincide).  On
+ * the chain schedule phase 0 is the C B^T / B^T pre-pass, phases 1 and 2 are
+ * empty and phase 3 is the chain kernel (states, recurrence and outputs).
  */
 #define SSD_SCAN_PHASES 4
 ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const float* dt,

@@ -27,11 +27,13 @@ SSD_OK = 0
 SSD_F32 = 0
 SSD_BF16 = 1
 SSD_SCAN_PHASES = 4
+SSD_SCHEDULE_PHASED = 0
+SSD_SCHEDULE_CHAIN = 1
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
                 4: "SSD_ERR_ALIGNMENT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE",
                 7: "SSD_ERR_HIP"}
 EXPORTED = ("ssd_chunk_scan", "ssd_chunk_scan_timed", "ssd_chunk_scan_workspace_bytes",
-            "ssd_step", "ssd_status_string", "ssd_abi_version")
+            "ssd_chunk_scan_schedule", "ssd_step", "ssd_status_string", "ssd_abi_version")
 
 
 class ScanDesc(ctypes.Structure):
@@ -73,6 +75,8 @@ def _load() -> ctypes.CDLL:
                                        + [ctypes.POINTER(vp), ctypes.c_int])
     L.ssd_chunk_scan_workspace_bytes.restype = sz
     L.ssd_chunk_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
+    L.ssd_chunk_scan_schedule.restype = i32
+    L.ssd_chunk_scan_schedule.argtypes = [ctypes.POINTER(ScanDesc)]
     L.ssd_step.restype = i32
     L.ssd_step.argtypes = [ctypes.POINTER(StepDesc)] + [vp] * 9 + [vp]
     L.ssd_status_string.restype = ctypes.c_char_p
@@ -123,6 +127,16 @@ def scan_desc(x: torch.Tensor, B: torch.Tensor, chunk: int, dt_softplus: bool,
 def ssd_chunk_scan_workspace_bytes(x: torch.Tensor, B: torch.Tensor, chunk: int = 256) -> int:
     d = scan_desc(x, B, chunk, True, (1e-4, 0.5))
     return int(lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d)))
+
+
+def ssd_chunk_scan_schedule(x: torch.Tensor, B: torch.Tensor, chunk: int = 256) -> int:
+    """SSD_SCHEDULE_PHASED or SSD_SCHEDULE_CHAIN: the kernel schedule a scan of
+    these shapes runs (both give bit-identical results)."""
+    d = scan_desc(x, B, chunk, True, (1e-4, 0.5))
+    r = int(lib.ssd_chunk_scan_schedule(ctypes.byref(d)))
+    if r < 0:
+        raise SSDError(-r, "ssd_chunk_scan_schedule")
+    return r
 
 
 def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,

@@ -48,8 +48,9 @@ inline bool limits_ok(float lo, float hi) { return !isnan(lo) && !isnan(hi) && l
 
 struct ScanSizes {
   int64_t Nc = 0;
+  bool chain = false;
   int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0;  // element counts
-  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_cb_bytes = 0, ws_total = 0;
+  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_cb_bytes = 0, ws_bt_bytes = 0, ws_total = 0;
 };
 
 ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
@@ -81,10 +82,18 @@ ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
       !mul_ok(d->chunk, d->chunk, &ll) || !mul_ok(bcg, ll, &cb_elems) ||
       !mul_ok(cb_elems, 4, &tmp))
     return SSD_ERR_UNSUPPORTED;
-  s->ws_state_bytes = round_up((size_t)ws_elems * 4, kAlign);
-  s->ws_alpha_bytes = round_up((size_t)units * 4, kAlign);
+  s->chain = ssd::scan_uses_chain(d->batch, d->nheads, d->headdim, d->dstate, d->chunk,
+                                  d->io_dtype == SSD_BF16);
+  // the chain schedule keeps states on chip; the phased one needs S_c and alpha_c
+  s->ws_state_bytes = s->chain ? 0 : round_up((size_t)ws_elems * 4, kAlign);
+  s->ws_alpha_bytes = s->chain ? 0 : round_up((size_t)units * 4, kAlign);
+  int64_t bt_elems = 0;
+  if (!mul_ok(bcg, d->dstate, &bt_elems) || !mul_ok(bt_elems, d->chunk, &bt_elems) ||
+      !mul_ok(bt_elems, 2, &tmp))
+    return SSD_ERR_UNSUPPORTED;
   s->ws_cb_bytes = round_up((size_t)cb_elems * 4, kAlign);
-  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes + s->ws_cb_bytes;
+  s->ws_bt_bytes = s->chain ? round_up((size_t)bt_elems * 2, kAlign) : 0;
+  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes + s->ws_cb_bytes + s->ws_bt_bytes;
   return SSD_OK;
 }
 
@@ -148,10 +157,12 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   a.ws_alpha = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws_state_bytes);
   a.ws_cb = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws_state_bytes +
                                      s.ws_alpha_bytes);
+  a.ws_bt = static_cast<char*>(workspace) + s.ws_state_bytes + s.ws_alpha_bytes + s.ws_cb_bytes;
   a.Bt = desc->batch; a.T = desc->seqlen; a.H = desc->nheads; a.G = desc->ngroups;
   a.L = desc->chunk; a.Nc = s.Nc;
   a.softplus = desc->dt_softplus ? 1 : 0;
   a.dt_min = desc->dt_min; a.dt_max = desc->dt_max;
+  a.chain = s.chain ? 1 : 0;
   hipError_t e = desc->io_dtype == SSD_BF16
                      ? ssd::launch_scan_bf16(a, (int)desc->headdim, (int)desc->dstate, stream, events)
                      : ssd::launch_scan_f32(a, (int)desc->headdim, (int)desc->dstate, stream, events);
@@ -167,6 +178,10 @@ bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16) {
                   ((N == 16 && !bf16) || N == 32 || N == 64 || N == 128);
   return pn && L >= 32 && L <= 512 && L % 32 == 0 && P * L <= 32768;
 }
+
+bool scan_uses_chain(int64_t batch, int64_t nheads, int64_t P, int64_t N, int64_t L, bool bf16) {
+  return bf16 && chain_variant(P, N) && L <= 256 && batch * nheads >= kChainMinChains;
+}
 }  // namespace ssd
 
 extern "C" {
@@ -175,6 +190,13 @@ size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc) {
   ScanSizes s;
   if (check_scan_desc(desc, &s) != SSD_OK) return 0;
   return s.ws_total;
+}
+
+int32_t ssd_chunk_scan_schedule(const ssd_scan_desc* desc) {
+  ScanSizes s;
+  const ssd_status st = check_scan_desc(desc, &s);
+  if (st != SSD_OK) return -(int32_t)st;
+  return s.chain ? SSD_SCHEDULE_CHAIN : SSD_SCHEDULE_PHASED;
 }
 
 ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float* dt,

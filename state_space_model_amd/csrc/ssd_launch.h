@@ -21,9 +21,11 @@ struct ScanArgs {
   float* ws_state;        // [Bt,H,Nc,P,N]: chunk summary states, then entering states
   float* ws_alpha;        // [Bt,H,Nc]: exp(total decay of the chunk)
   float* ws_cb;           // [Bt,Nc,G,L,L]: C B^T of each chunk (causal 16x16 tiles)
+  void* ws_bt;            // [Bt,Nc,G,N,L] bf16: B of each chunk, transposed (token-contiguous)
   int64_t Bt, T, H, G, L, Nc;
   int32_t softplus;
   float dt_min, dt_max;
+  int32_t chain;          // 1: chain schedule (bfloat16 only), 0: phased
 };
 
 struct StepArgs {
@@ -44,6 +46,17 @@ struct StepArgs {
 
 // Compiled shape variants.
 bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16);
+
+// Head/state sizes with a compiled chain kernel (bfloat16 io, L <= 256).
+constexpr bool chain_variant(int64_t P, int64_t N) {
+  return (P == 32 || P == 64) && (N == 64 || N == 128);
+}
+// The chain schedule runs one workgroup per (batch, head) for the whole
+// sequence; it is chosen once batch x heads alone fill the GPU's 256 compute
+// units (two workgroups per unit at most).  Both schedules give bit-identical
+// results, so the choice never changes an answer.
+constexpr int64_t kChainMinChains = 256;
+bool scan_uses_chain(int64_t batch, int64_t nheads, int64_t P, int64_t N, int64_t L, bool bf16);
 bool step_shape_supported(int64_t P, int64_t N);
 
 // Launch the whole scan (Bt*T > 0) on `stream`.  `events` (may be null) gets

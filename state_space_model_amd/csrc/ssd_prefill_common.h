@@ -16,35 +16,73 @@ constexpr int kThreads = 256;  // 4 wavefronts per workgroup
 constexpr int kMaxL = 512;
 
 // Step Delta_l and the inclusive prefix sum cum_l of a_l = Delta_l A[h] over
-// the chunk's L tokens, into LDS.  Tokens at or past T get Delta = 0 (so the
-// sum stays flat there).  Every thread of the block must call this; it ends
-// with a barrier.  Each thread owns tokens 2*tid and 2*tid+1; the wavefront
-// scan and the cross-wave offsets run in a fixed order, so every kernel that
-// calls this gets bit-identical values.
-__device__ __forceinline__ void chunk_delta_cumsum(const ScanArgs& a, int64_t b, int64_t c,
-                                                   int64_t h, float* s_d, float* s_cum,
-                                                   float* s_wsum) {
+// the chunk's L tokens.  Tokens at or past T get Delta = 0 (so the sum stays
+// flat there).  Each thread owns tokens 2*tid and 2*tid+1.  The work is split
+// in two stages around a barrier so that a kernel can overlap the first stage
+// with other work; every kernel runs the same operations in the same order,
+// so all of them get bit-identical Delta and cum values.  Products and sums
+// are written with explicit rounding so the compiler cannot fuse them
+// differently from one kernel to another.
+struct DeltaScan {
+  float d0, d1, a0, a1, local, incl;
+};
+
+// Raw dt of this thread's two tokens (0 past the chunk or past T).
+__device__ __forceinline__ float2 chunk_dt_load(const ScanArgs& a, int64_t b, int64_t c,
+                                                int64_t h) {
+  const int l0 = 2 * (int)threadIdx.x, l1 = l0 + 1;
+  const int64_t t0 = c * a.L;
+  const int last = (int)min<int64_t>(a.L, a.T - t0) - 1;   // last token of the chunk
+  // unconditional loads of clamped rows, then a select: no branch per load
+  const float v0 = a.dt[(b * a.T + t0 + min(l0, last)) * a.H + h];
+  const float v1 = a.dt[(b * a.T + t0 + min(l1, last)) * a.H + h];
+  return make_float2(l0 <= last ? v0 : 0.0f, l1 <= last ? v1 : 0.0f);
+}
+
+// Stage 1: Delta, a and the wavefront-inclusive scan; publishes each
+// wavefront's total in s_wsum[wave].  No barrier inside.
+__device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_t c, int64_t h,
+                                                       float2 dtv, float* s_wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = (int)a.L;
+  const int l0 = 2 * tid, l1 = l0 + 1;
   const int64_t t0 = c * a.L;
   const float Ah = a.A[h];
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  const int l0 = 2 * tid, l1 = 2 * tid + 1;
-  float d0 = 0.0f, d1 = 0.0f;
-  if (l0 < L && t0 + l0 < a.T)
-    d0 = delta_of(a.dt[(b * a.T + t0 + l0) * a.H + h] + bias, a.softplus, a.dt_min, a.dt_max);
-  if (l1 < L && t0 + l1 < a.T)
-    d1 = delta_of(a.dt[(b * a.T + t0 + l1) * a.H + h] + bias, a.softplus, a.dt_min, a.dt_max);
-  const float a0 = d0 * Ah, a1 = d1 * Ah;
-  const float local = a0 + a1;
-  const float incl = wave_inclusive_scan(local);
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
+  DeltaScan s;
+  s.d0 = (l0 < a.L && t0 + l0 < a.T)
+             ? delta_of(__fadd_rn(dtv.x, bias), a.softplus, a.dt_min, a.dt_max) : 0.0f;
+  s.d1 = (l1 < a.L && t0 + l1 < a.T)
+             ? delta_of(__fadd_rn(dtv.y, bias), a.softplus, a.dt_min, a.dt_max) : 0.0f;
+  s.a0 = __fmul_rn(s.d0, Ah);
+  s.a1 = __fmul_rn(s.d1, Ah);
+  s.local = __fadd_rn(s.a0, s.a1);
+  s.incl = wave_inclusive_scan(s.local);
+  if (lane == 63) s_wsum[wave] = s.incl;
+  return s;
+}
+
+// Stage 2 (after a barrier that follows stage 1): cross-wavefront offsets;
+// writes s_d and s_cum for this thread's tokens.  No barrier inside.
+__device__ __forceinline__ void chunk_scan_stage2(const ScanArgs& a, const DeltaScan& s,
+                                                  const float* s_wsum, float* s_d, float* s_cum) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int l0 = 2 * tid, l1 = l0 + 1;
   float off = 0.0f;
-  for (int w = 0; w < wave; ++w) off += s_wsum[w];
-  const float excl = off + (incl - local);
-  if (l0 < L) { s_d[l0] = d0; s_cum[l0] = excl + a0; }
-  if (l1 < L) { s_d[l1] = d1; s_cum[l1] = excl + a0 + a1; }
+  for (int w = 0; w < wave; ++w) off = __fadd_rn(off, s_wsum[w]);
+  const float excl = __fadd_rn(off, __fsub_rn(s.incl, s.local));
+  const float c0 = __fadd_rn(excl, s.a0);
+  if (l0 < a.L) { s_d[l0] = s.d0; s_cum[l0] = c0; }
+  if (l1 < a.L) { s_d[l1] = s.d1; s_cum[l1] = __fadd_rn(c0, s.a1); }
+}
+
+// Both stages with their barriers: s_d and s_cum are ready for every thread
+// on return.  Every thread of the block must call this.
+__device__ __forceinline__ void chunk_delta_cumsum(const ScanArgs& a, int64_t b, int64_t c,
+                                                   int64_t h, float* s_d, float* s_cum,
+                                                   float* s_wsum) {
+  const DeltaScan s = chunk_scan_stage1(a, c, h, chunk_dt_load(a, b, c, h), s_wsum);
+  __syncthreads();
+  chunk_scan_stage2(a, s, s_wsum, s_d, s_cum);
   __syncthreads();
 }
 

@@ -7,6 +7,9 @@
 //
 //   h_c = alpha_c h_{c-1} + S_c,   h_{-1} = initial state (or 0)
 //
+// computed as one fused multiply-add per element (the same operation the
+// bfloat16 chain kernel applies to its on-chip state).
+//
 // Element-wise over the P x N state of every (batch, head), sequential over
 // chunks.  The workspace holds S_c on entry and the state entering chunk c,
 // h_{c-1}, on exit; the last state goes to final_state.  One lane owns one
@@ -48,10 +51,10 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const 
       if (k < n) {
         st[(c0 + k) * PN4] = hc;
         const float a = al_c[k];
-        hc.x = a * hc.x + s[k].x;
-        hc.y = a * hc.y + s[k].y;
-        hc.z = a * hc.z + s[k].z;
-        hc.w = a * hc.w + s[k].w;
+        hc.x = __fmaf_rn(a, hc.x, s[k].x);
+        hc.y = __fmaf_rn(a, hc.y, s[k].y);
+        hc.z = __fmaf_rn(a, hc.z, s[k].z);
+        hc.w = __fmaf_rn(a, hc.w, s[k].w);
       }
     }
   }

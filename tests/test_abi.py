@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert ssd.abi_version() == 1
+    assert ssd.abi_version() == 2
     for code in range(8):
         s = lib.ssd_status_string(code).decode()
         assert s.startswith(ssd.STATUS_NAMES[code])
@@ -89,6 +89,41 @@ def test_workspace_query():
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d2)) > n
     assert lib.ssd_chunk_scan_workspace_bytes(None) == 0
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(desc(headdim=24))) == 0
+
+
+def _r256(v):
+    return (v + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("kw,chain", [
+    (dict(io_dtype=1, batch=8, nheads=64, headdim=64, dstate=128, chunk=256), True),
+    (dict(io_dtype=1, batch=4, nheads=64, headdim=64, dstate=128, chunk=128), True),
+    (dict(io_dtype=1, batch=16, nheads=16, headdim=32, dstate=64, chunk=64), True),
+    (dict(io_dtype=1, batch=1, nheads=255, headdim=64, dstate=128, chunk=256), False),  # too few chains
+    (dict(io_dtype=0, batch=8, nheads=64, headdim=64, dstate=128, chunk=256), False),   # float32 io
+    (dict(io_dtype=1, batch=8, nheads=64, headdim=64, dstate=128, chunk=512), False),   # L > 256
+    (dict(io_dtype=1, batch=8, nheads=64, headdim=128, dstate=128, chunk=256), False),  # P = 128
+    (dict(io_dtype=1, batch=8, nheads=64, headdim=64, dstate=32, chunk=256), False),    # N = 32
+])
+def test_schedule_and_workspace(kw, chain):
+    """The schedule choice and the exact workspace size of each schedule."""
+    d = desc(seqlen=1000, **kw)
+    sched = lib.ssd_chunk_scan_schedule(ctypes.byref(d))
+    assert sched == (ssd.SSD_SCHEDULE_CHAIN if chain else ssd.SSD_SCHEDULE_PHASED)
+    Bt, H, P, N, L, G = d.batch, d.nheads, d.headdim, d.dstate, d.chunk, d.ngroups
+    nc = (d.seqlen + L - 1) // L
+    cb = _r256(4 * Bt * nc * G * L * L)
+    if chain:
+        want = cb + _r256(2 * Bt * nc * G * N * L)
+    else:
+        want = _r256(4 * Bt * H * nc * P * N) + _r256(4 * Bt * H * nc) + cb
+    assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d)) == want
+
+
+def test_schedule_query_rejects_invalid_descriptors():
+    assert lib.ssd_chunk_scan_schedule(None) == -INVALID
+    assert lib.ssd_chunk_scan_schedule(ctypes.byref(desc(headdim=24))) == -UNSUP
+    assert lib.ssd_chunk_scan_schedule(ctypes.byref(desc(io_dtype=5))) == -DTYPE
 
 
 @pytest.mark.parametrize("kw,code", [

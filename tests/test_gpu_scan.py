@@ -116,6 +116,55 @@ def test_scan_tiny_shapes(case):
     assert state_err(fin, f_ref) <= TOL[dt], state_err(fin, f_ref)
 
 
+CHAIN = [
+    # (Bt, T, H, P, N, G, L): batch x heads >= 256 with bf16 io selects the chain schedule
+    (4, 700, 64, 64, 128, 1, 256),     # 2.7B head shape, ragged last chunk
+    (2, 600, 128, 64, 64, 2, 128),     # N = 64, two groups
+    (16, 333, 16, 32, 128, 4, 128),    # P = 32, four groups, ragged
+    (8, 64, 32, 32, 64, 1, 64),        # a single full chunk
+    (16, 1, 16, 64, 128, 1, 256),      # a single token
+    (1, 1100, 256, 64, 128, 8, 256),   # one batch row, many heads
+]
+
+
+@pytest.mark.parametrize("case", CHAIN, ids=lambda c: "x".join(map(str, c)))
+def test_scan_chain_schedule(case):
+    """Shapes that run the chain schedule (one workgroup per (batch, head)
+    walking the chunks with the state on chip) against the oracle."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    Bt, T, H, P, N, G, L = case
+    w = make_tiny(Bt, T, H, P, N, G, L, "bf16", seed=2000 + CHAIN.index(case))
+    inp = make_inputs(w, with_initial_state=True)
+    announce(f"scan chain {case}")
+    d = to_dev(inp)
+    assert ssd.ssd_chunk_scan_schedule(d["x"], d["B"], L) == ssd.SSD_SCHEDULE_CHAIN
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    assert y_err(y, y_ref) <= TOL["bf16"], y_err(y, y_ref)
+    assert state_err(fin, f_ref) <= TOL["bf16"], state_err(fin, f_ref)
+
+
+def test_chain_and_phased_schedules_agree_bitwise():
+    """A batch of 32 x 8 heads runs the chain schedule; each row alone (8
+    heads) runs the phased one.  The two must agree bit for bit, so the
+    batch-size invariance holds across the schedule switch."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = make_tiny(32, 600, 8, 64, 128, 1, 256, "bf16", seed=78)
+    inp = make_inputs(w, with_initial_state=True)
+    announce("scan chain vs phased bitwise 32x600 H8 P64 N128 L256")
+    d = to_dev(inp)
+    assert ssd.ssd_chunk_scan_schedule(d["x"], d["B"], 256) == ssd.SSD_SCHEDULE_CHAIN
+    y1, f1 = run_gpu(inp, w)
+    for b in (0, 13, 31):
+        one = {k: (v[b:b + 1] if k in ("x", "dt", "B", "C", "h0") else v) for k, v in inp.items()}
+        d1 = to_dev(one)
+        assert ssd.ssd_chunk_scan_schedule(d1["x"], d1["B"], 256) == ssd.SSD_SCHEDULE_PHASED
+        ya, fa = run_gpu(one, w.with_(batch=1))
+        assert torch.equal(ya, y1[b:b + 1]) and torch.equal(fa, f1[b:b + 1]), b
+
+
 def test_scan_options_off():
     """No D, no dt_bias, softplus off, no initial state, no final state requested."""
     need_gpu()
