@@ -108,16 +108,11 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 v, float4 w0, float4 w1) {
 
 // ---------------------------------------------------------------------------
 // S = C B^T (float32) for the causal 16x16 tiles of every (b, c, g).
-// One wavefront computes one tile (I, J), J <= I.
+// One wavefront computes tile t of (b, c, g) = bcg: (I, J), J <= I.
 // ---------------------------------------------------------------------------
 template <int N>
-__device__ __forceinline__ void cb_tile_bf16(const ScanArgs& a, int ntiles, int64_t block) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void cb_tile_bf16(const ScanArgs& a, int64_t bcg, int t) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
-  const int64_t item = block * 4 + wave;
-  const int64_t bcg = item / ntiles;
-  if (bcg >= a.Bt * a.Nc * a.G) return;
-  const int t = (int)(item % ntiles);
   int I = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while ((I + 1) * (I + 2) / 2 <= t) ++I;
   while (I * (I + 1) / 2 > t) --I;
@@ -145,7 +140,8 @@ __device__ __forceinline__ void cb_tile_bf16(const ScanArgs& a, int ntiles, int6
 }
 
 // Number of causal 16x16 tiles of one chunk and the C B^T blocks of a grid
-// (4 tiles per block, rounded up to whole rounds of the 8 XCDs).
+// that gives them workgroups of their own (4 tiles per block, rounded up to
+// whole rounds of the 8 XCDs).
 inline int cb_tiles(const ScanArgs& a) {
   const int nrt = (int)((a.L + 15) / 16);
   return nrt * (nrt + 1) / 2;
@@ -153,6 +149,15 @@ inline int cb_tiles(const ScanArgs& a) {
 inline int64_t cb_blocks(const ScanArgs& a) {
   const int64_t items = a.Bt * a.Nc * a.G * cb_tiles(a);
   return ((items + 3) / 4 + 7) / 8 * 8;
+}
+// Tile work of C B^T block `block` (4 tiles, one per wavefront).
+template <int N>
+__device__ __forceinline__ void cb_block_bf16(const ScanArgs& a, int ntiles, int64_t block) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t item = block * 4 + wave;
+  const int64_t bcg = item / ntiles;
+  if (bcg >= a.Bt * a.Nc * a.G) return;
+  cb_tile_bf16<N>(a, bcg, (int)(item % ntiles));
 }
 
 // ---------------------------------------------------------------------------
@@ -486,7 +491,8 @@ struct ChunkStateShapeB {
 };
 
 template <int P, int N>
-__device__ __forceinline__ void chunk_state_bf16(const ScanArgs& a, int64_t block, int64_t nblocks,
+__device__ __forceinline__ void chunk_state_bf16(const ScanArgs& a, int ntiles, int64_t block,
+                                                 int64_t nblocks,
                                                  float* s_d, float* s_cum, float* s_w,
                                                  float* s_wsum, bf16* s_x0, bf16* s_x1,
                                                  bf16* s_b0, bf16* s_b1) {
@@ -610,20 +616,24 @@ __device__ __forceinline__ void chunk_state_bf16(const ScanArgs& a, int64_t bloc
             make_float4(v[0], v[1], v[2], v[3]));
       }
   }
+  // this workgroup's share of the causal C B^T tiles of (b, c, g)
+  {
+    const int hpg = (int)(a.H / a.G);
+    const int wi = (int)(h % hpg);
+    const int64_t bcg = (b * a.Nc + c) * a.G + g;
+    for (int t = wi * 4 + wave; t < ntiles; t += hpg * 4) cb_tile_bf16<N>(a, bcg, t);
+  }
 }
 
+// Every chunk-state workgroup also computes its share of the C B^T tiles of
+// its (b, c, g) once its state is stored.
 template <int P, int N>
-__global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_bf16(ScanArgs a, int ntiles,
-                                                                      int64_t ncb) {
+__global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_bf16(ScanArgs a, int ntiles) {
   using Sh = ChunkStateShapeB<P, N>;
   __shared__ float s_d[kMaxL], s_cum[kMaxL], s_w[kMaxL], s_wsum[4];
   __shared__ __attribute__((aligned(16))) bf16 s_x[2][P * Sh::TS];
   __shared__ __attribute__((aligned(16))) bf16 s_b[2][N * Sh::TS];
-  if ((int64_t)blockIdx.x < ncb) {
-    cb_tile_bf16<N>(a, ntiles, blockIdx.x);
-    return;
-  }
-  chunk_state_bf16<P, N>(a, blockIdx.x - ncb, gridDim.x - ncb, s_d, s_cum, s_w, s_wsum, s_x[0],
+  chunk_state_bf16<P, N>(a, ntiles, blockIdx.x, gridDim.x, s_d, s_cum, s_w, s_wsum, s_x[0],
                          s_x[1], s_b[0], s_b[1]);
 }
 
@@ -696,7 +706,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out_bf16(ScanArgs a) {
 template <int N>
 __global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int ntiles, int64_t ncb) {
   if ((int64_t)blockIdx.x < ncb) {
-    cb_tile_bf16<N>(a, ntiles, blockIdx.x);
+    cb_block_bf16<N>(a, ntiles, blockIdx.x);
     return;
   }
   const int LB = (int)(a.L / 8);
@@ -895,10 +905,9 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
   auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
   if ((e = rec(0)) != hipSuccess) return e;
   if ((e = rec(1)) != hipSuccess) return e;
-  const int64_t ncb = cb_blocks(a);
   const int64_t units = a.Bt * a.Nc * a.H;
-  hipLaunchKernelGGL((k_cb_and_chunk_state_bf16<P, N>), dim3((unsigned)(ncb + units)),
-                     dim3(kThreads), 0, stream, a, cb_tiles(a), ncb);
+  hipLaunchKernelGGL((k_cb_and_chunk_state_bf16<P, N>), dim3((unsigned)units), dim3(kThreads), 0,
+                     stream, a, cb_tiles(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = rec(2)) != hipSuccess) return e;
   if ((e = launch_state_pass(a, P, N, stream)) != hipSuccess) return e;

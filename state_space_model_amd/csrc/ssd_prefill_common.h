@@ -99,6 +99,13 @@ __device__ __forceinline__ int chunk_len(const ScanArgs& a, int64_t c) {
 
 // 16 bytes = one fragment chunk of a lane.
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// Branch-free masked load: `p` must be a valid address whether or not `ok`
+// (callers clamp the row); the value is replaced by zeros when !ok.  A plain
+// `ok ? load : 0` becomes one exec-masked branch, and a wait, per load.
+__device__ __forceinline__ float4 ld4_masked(const float* p, bool ok) {
+  const float4 v = ld4(p);
+  return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+}
 __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
 __device__ __forceinline__ float get(const float4& v, int k) {
   return k == 0 ? v.x : (k == 1 ? v.y : (k == 2 ? v.z : v.w));

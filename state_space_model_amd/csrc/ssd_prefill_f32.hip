@@ -38,16 +38,13 @@ __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.
 
 // ---------------------------------------------------------------------------
 // Phase 0: S = C B^T for the causal 16x16 tiles of every (b, c, g).
-// One wavefront computes one tile (I, J), J <= I.
+// One wavefront computes tile t of (b, c, g) = bcg: (I, J), J <= I.  The
+// tiles are shared out among the chunk-state workgroups of the same
+// (b, c, g), which compute them after their own state.
 // ---------------------------------------------------------------------------
 template <int N>
-__device__ __forceinline__ void cb_tile_f32(const ScanArgs& a, int ntiles, int64_t block) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+__device__ __forceinline__ void cb_tile_f32(const ScanArgs& a, int64_t bcg, int t) {
   const int lane = threadIdx.x & 63, q = lane >> 4, r16 = lane & 15;
-  const int64_t item = block * 4 + wave;
-  const int64_t bcg = item / ntiles;
-  if (bcg >= a.Bt * a.Nc * a.G) return;
-  const int t = (int)(item % ntiles);
   // triangular index t -> (I, J), 0 <= J <= I
   int I = (int)((sqrtf(8.0f * (float)t + 1.0f) - 1.0f) * 0.5f);
   while ((I + 1) * (I + 2) / 2 <= t) ++I;
@@ -64,8 +61,8 @@ __device__ __forceinline__ void cb_tile_f32(const ScanArgs& a, int ntiles, int64
   float4 cf[N / 16], bf[N / 16];
 #pragma unroll
   for (int nb = 0; nb < N / 16; ++nb) {
-    cf[nb] = ri < Lc ? ld4(Cg + ri * rs + nb * 16) : zero4();
-    bf[nb] = rj < Lc ? ld4(Bg + rj * rs + nb * 16) : zero4();
+    cf[nb] = ld4_masked(Cg + min(ri, Lc - 1) * rs + nb * 16, ri < Lc);
+    bf[nb] = ld4_masked(Bg + min(rj, Lc - 1) * rs + nb * 16, rj < Lc);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -82,8 +79,9 @@ __device__ __forceinline__ void cb_tile_f32(const ScanArgs& a, int ntiles, int64
 
 // ---------------------------------------------------------------------------
 // Phase 1: chunk summary states S_c[p][n] = sum_l (x_l[p] w_l) B_l[n],
-// w_l = Delta_l exp(cum_last - cum_l).  A workgroup covers NW of the N state
-// columns.  Tokens go through LDS in double-buffered blocks of KB: the global
+// w_l = Delta_l exp(cum_last - cum_l), computed as tiles of S_c^T (rows n) so
+// that each lane stores four consecutive n of one p.  A workgroup covers NW
+// of the N state columns.  Tokens go through LDS in double-buffered blocks of KB: the global
 // loads of block k+1 are in flight while block k feeds the matrix cores.
 // ---------------------------------------------------------------------------
 template <int P, int N, int NW>
@@ -93,7 +91,8 @@ struct ChunkStateShape {
 };
 
 template <int P, int N, int NW>
-__device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int64_t block, int64_t nblocks,
+__device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int ntiles, int64_t block,
+                                                int64_t nblocks,
                                                 float* s_d, float* s_cum, float* s_w, float* s_wsum,
                                                 float* s_x0, float* s_x1, float* s_b0, float* s_b1) {
   using Sh = ChunkStateShape<P, N, NW>;
@@ -125,12 +124,12 @@ __device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int64_t block
 #pragma unroll
     for (int i = 0; i < XL; ++i) {
       const int e = tid + i * kThreads, l = e / XQ, m = e % XQ;
-      xr[i] = (e < KB * XQ && kb0 + l < Lc) ? ld4(&xg[(kb0 + l) * xstride + 4 * m]) : zero4();
+      xr[i] = ld4_masked(&xg[min(kb0 + l, Lc - 1) * xstride + 4 * m], e < KB * XQ && kb0 + l < Lc);
     }
 #pragma unroll
     for (int i = 0; i < BL; ++i) {
       const int e = tid + i * kThreads, l = e / BQ, m = e % BQ;
-      br[i] = (e < KB * BQ && kb0 + l < Lc) ? ld4(&Bg[(kb0 + l) * bstride + 4 * m]) : zero4();
+      br[i] = ld4_masked(&Bg[min(kb0 + l, Lc - 1) * bstride + 4 * m], e < KB * BQ && kb0 + l < Lc);
     }
   };
   auto store_block = [&](int kb0, const float4 (&xr)[XL], const float4 (&br)[BL], float* sx,
@@ -152,11 +151,17 @@ __device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int64_t block
     }
   };
   // two token blocks are always in flight ahead of the one being consumed
+  const float2 dtv = chunk_dt_load(a, b, c, h);
   float4 xA[XL], bA[BL], xB[XL], bB[BL];
   load_block(0, xA, bA);
   if (KB < Lc) load_block(KB, xB, bB);
 
-  chunk_delta_cumsum(a, b, c, h, s_d, s_cum, s_wsum);
+  {
+    const DeltaScan ds = chunk_scan_stage1(a, c, h, dtv, s_wsum);
+    __syncthreads();
+    chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
+    __syncthreads();
+  }
   const float cum_last = s_cum[Lc - 1];
   for (int l = tid; l < (int)a.L; l += kThreads)
     s_w[l] = (l < Lc) ? s_d[l] * fast_exp(cum_last - s_cum[l]) : 0.0f;
@@ -193,7 +198,7 @@ __device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int64_t block
 #pragma unroll
       for (int ip = 0; ip < NPT; ++ip)
 #pragma unroll
-        for (int in = 0; in < NNT; ++in) acc[ip][in] = mma(av[k][ip], bv[k][in], acc[ip][in]);
+        for (int in = 0; in < NNT; ++in) acc[ip][in] = mma(bv[k][in], av[k][ip], acc[ip][in]);
   };
   for (int kb0 = 0; kb0 < Lc; kb0 += 2 * KB) {
     store_block(kb0, xA, bA, s_x0, s_b0);
@@ -207,56 +212,69 @@ __device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int64_t block
     compute(s_x1, s_b1);
   }
   if (active) {
+    // tiles are S_c^T [n][p]: lane holds S_c[p = 16 pt + r16][n = 16 nt + 4q .. +3]
     float* out = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) + ns * NW;
 #pragma unroll
     for (int ip = 0; ip < NPT; ++ip)
 #pragma unroll
-      for (int in = 0; in < NNT; ++in)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          out[((pt0 + ip) * 16 + 4 * q + r) * N + (nt0 + in) * 16 + r16] = acc[ip][in][r];
+      for (int in = 0; in < NNT; ++in) {
+        const f32x4 v = acc[ip][in];
+        st4(out + ((pt0 + ip) * 16 + r16) * N + (nt0 + in) * 16 + 4 * q,
+            make_float4(v[0], v[1], v[2], v[3]));
+      }
+  }
+  // this workgroup's share of the causal C B^T tiles of (b, c, g)
+  {
+    const int hpg = (int)(a.H / a.G);
+    const int nwg = hpg * NSPLIT;                       // chunk-state workgroups of (b, c, g)
+    const int wi = (int)(h % hpg) * NSPLIT + ns;
+    const int64_t bcg = (b * a.Nc + c) * a.G + g;
+    for (int t = wi * 4 + wave; t < ntiles; t += nwg * 4) cb_tile_f32<N>(a, bcg, t);
   }
 }
 
-// Phases 0 and 1 share one launch: the first ncb workgroups compute C B^T
-// tiles (short-lived), the rest compute chunk states.  ncb is a multiple of
-// 8, so the chunk-state workgroups keep their XCD-aware numbering.
+// Phases 0 and 1 share one launch: every chunk-state workgroup also computes
+// its share of the C B^T tiles of its (b, c, g) once its state is stored (a
+// few tiles each; separate short workgroups ahead of the chunk-state ones
+// would hold their slots and delay them).
 template <int P, int N, int NW>
-__global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_f32(ScanArgs a, int ntiles,
-                                                                     int64_t ncb) {
+__global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_f32(ScanArgs a, int ntiles) {
   using Sh = ChunkStateShape<P, N, NW>;
   __shared__ float s_d[kMaxL], s_cum[kMaxL], s_w[kMaxL], s_wsum[4];
   __shared__ __attribute__((aligned(16))) float s_x[2][Sh::KB * Sh::XS];
   __shared__ __attribute__((aligned(16))) float s_b[2][Sh::KB * Sh::BS];
-  if ((int64_t)blockIdx.x < ncb) {
-    cb_tile_f32<N>(a, ntiles, blockIdx.x);
-    return;
-  }
-  chunk_state_f32<P, N, NW>(a, blockIdx.x - ncb, gridDim.x - ncb, s_d, s_cum, s_w, s_wsum,
-                            s_x[0], s_x[1], s_b[0], s_b[1]);
+  chunk_state_f32<P, N, NW>(a, ntiles, blockIdx.x, gridDim.x, s_d, s_cum, s_w, s_wsum, s_x[0],
+                            s_x[1], s_b[0], s_b[1]);
 }
 
 // ---------------------------------------------------------------------------
 // Phase 3: chunk outputs.  A workgroup covers PW of the P head columns of one
-// (b, c, h).  Wavefront w owns the 16-row tiles row_tile_of(w, k), k < RT,
-// and keeps all their accumulators live, so every h and x fragment it loads
-// serves all of its row tiles.
+// (b, c, h).  Wavefront w owns the 16-token column tiles row_tile_of(w, k),
+// k < RT, of y^T (tiles [p][i]) and keeps all their accumulators live, so
+// every h and x fragment it loads serves all of its tiles.  Computing y^T
+// rather than y puts four consecutive head columns of one token in each lane:
+// the skip term and the store are float4 accesses.
 //
-// Decay factors.  For a row tile in 64-token block R > 0 and a key j in an
+// Order: the x loads are issued first and land while the inter-chunk term
+// (which needs only h_{c-1} and C) runs on the matrix cores; its decay
+// exp(cum_i) is applied to the accumulators afterwards, once the prefix sum
+// is known.  Then x is staged, and the intra-chunk term runs.
+//
+// Decay factors.  For a token in 64-token block R > 0 and a key j in an
 // earlier block, exp(cum_i - cum_j) = exp(cum_i - cum_r) * exp(cum_r - cum_j)
 // with r = 64 R the first token of block R; both factors are <= 1.  The key
 // factors exp(cum_r - cum_j) Delta_j are tabulated in LDS once per workgroup
 // (one row per block boundary), the row factor is one exponential per lane
-// and row tile.  Inside the row tile's own block the decay is exponentiated
+// and column tile.  Inside the token's own block the decay is exponentiated
 // element by element, with the causal mask selected first.
 // ---------------------------------------------------------------------------
 template <int P, int N, int PW, int LMAX>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void k_chunk_out_f32(ScanArgs a) {
   constexpr int PSPLIT = P / PW, TP = PW / 16;
-  constexpr int XS = PW + 4;   // = 4 (mod 8): conflict-free B-fragment reads
+  constexpr int XS = PW + 4;   // = 4 (mod 8): conflict-free x^T-fragment reads
   constexpr int NBLK = LMAX / 64;
-  constexpr int RT = NBLK;     // row tiles per wavefront
+  constexpr int RT = NBLK;     // column tiles per wavefront
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
   __shared__ float s_wsum[4];
@@ -276,8 +294,7 @@ void k_chunk_out_f32(ScanArgs a) {
   const int p0 = ps * PW;
   const float* xg = reinterpret_cast<const float*>(a.x);
 
-  // row tiles of this wavefront (uniform) and the operands of the first state
-  // block of the inter-chunk term, in flight during the staging and prologue
+  // column tiles of this wavefront (uniform)
   int Ik[RT];
   bool vk[RT];
 #pragma unroll
@@ -285,83 +302,58 @@ void k_chunk_out_f32(ScanArgs a) {
     Ik[k] = row_tile_of(wave, k);
     vk[k] = Ik[k] < nrt;
   }
-  const float* Cg = reinterpret_cast<const float*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
-  const int64_t crs = a.G * N;
-  const float* hp = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) +
-                    (int64_t)(p0 + r16) * N + 4 * q;
-  auto load_nb = [&](int nb, float4 (&hv)[TP], float4 (&cv)[RT]) {
-#pragma unroll
-    for (int pt = 0; pt < TP; ++pt) hv[pt] = ld4(hp + pt * 16 * N + nb * 16);
-#pragma unroll
-    for (int k = 0; k < RT; ++k) {
-      const int ri = 16 * Ik[k] + r16;
-      cv[k] = (vk[k] && ri < Lc) ? ld4(Cg + ri * crs + nb * 16) : zero4();
-    }
-  };
-  float4 hA[TP], cA[RT], hB[TP], cB[RT];
-  load_nb(0, hA, cA);
 
-  // stage x (this workgroup's PW columns of every chunk row); all loads of a
-  // batch are issued before any LDS store
-  {
-    constexpr int XQ = PW / 4, XLB = 8;
-    const int nx = nrt * 16 * XQ;
-    for (int e0 = 0; e0 < nx; e0 += XLB * kThreads) {
-      float4 v[XLB];
+  // dt of the chunk and x of this workgroup's PW columns for every chunk row:
+  // loads issued now, consumed by the staging
+  constexpr int XQ = PW / 4;
+  constexpr int XLB = (LMAX * XQ + kThreads - 1) / kThreads;
+  const int nx = nrt * 16 * XQ;
+  float4 xv_stage[XLB];
 #pragma unroll
-      for (int i = 0; i < XLB; ++i) {
-        const int e = e0 + i * kThreads + tid, j = e / XQ, m = e % XQ;
-        v[i] = (e < nx && j < Lc) ? ld4(&xg[((b * a.T + t0 + j) * a.H + h) * P + p0 + 4 * m])
-                                  : zero4();
-      }
-#pragma unroll
-      for (int i = 0; i < XLB; ++i) {
-        const int e = e0 + i * kThreads + tid, j = e / XQ, m = e % XQ;
-        if (e < nx) st4(&s_x[j * XS + 4 * m], v[i]);
-      }
-    }
+  for (int i = 0; i < XLB; ++i) {
+    const int e = i * kThreads + tid, j = e / XQ, m = e % XQ;
+    xv_stage[i] = ld4_masked(&xg[((b * a.T + t0 + min(j, Lc - 1)) * a.H + h) * P + p0 + 4 * m],
+                             e < nx && j < Lc);
   }
-  chunk_delta_cumsum(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
-  for (int e = tid; e < (NBLK - 1) * LMAX; e += kThreads) {
-    const int R = e / LMAX + 1, j = e % LMAX;
-    const int r = min(64 * R, Lc - 1);
-    s_w[e] = (j < r) ? fast_exp(s_cum[r] - s_cum[j]) * s_d[j] : 0.0f;
-  }
-  __syncthreads();
 
-  // decay data of this wavefront's query rows
-  float cumk[RT];
-#pragma unroll
-  for (int k = 0; k < RT; ++k) cumk[k] = s_cum[min(16 * Ik[k] + r16, Lc - 1)];
+  const float2 dtv = chunk_dt_load(a, b, c, h);
+
   f32x4 acc[RT][TP];
 #pragma unroll
   for (int k = 0; k < RT; ++k)
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- inter-chunk term: acc[k] += sum_n (exp(cum_i) C[i][n]) h_{c-1}[p][n] ----
-  {
-    float sc[RT];
+  // ---- inter-chunk term: acc[k][pt] = sum_n h_{c-1}[p][n] C[i][n] ----
+  auto inter = [&]() {
+    const float* Cg = reinterpret_cast<const float*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 4 * q;
+    const int64_t crs = a.G * N;
+    const float* hp = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N) +
+                      (int64_t)(p0 + r16) * N + 4 * q;
+    auto load_nb = [&](int nb, float4 (&hv)[TP], float4 (&cv)[RT]) {
 #pragma unroll
-    for (int k = 0; k < RT; ++k) {
-      const int ri = 16 * Ik[k] + r16;
-      sc[k] = (vk[k] && ri < Lc) ? fast_exp(cumk[k]) : 0.0f;
-    }
+      for (int pt = 0; pt < TP; ++pt) hv[pt] = ld4(hp + pt * 16 * N + nb * 16);
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        const int ri = 16 * Ik[k] + r16;
+        cv[k] = ld4_masked(Cg + min(ri, Lc - 1) * crs + nb * 16, vk[k] && ri < Lc);
+      }
+    };
     auto mma_nb = [&](const float4 (&hv)[TP], const float4 (&cv)[RT]) {
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
         if (!vk[k]) continue;
-        const float4 c4 = make_float4(cv[k].x * sc[k], cv[k].y * sc[k], cv[k].z * sc[k],
-                                      cv[k].w * sc[k]);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
-          acc[k][pt] = mma(c4.x, hv[pt].x, acc[k][pt]);
-          acc[k][pt] = mma(c4.y, hv[pt].y, acc[k][pt]);
-          acc[k][pt] = mma(c4.z, hv[pt].z, acc[k][pt]);
-          acc[k][pt] = mma(c4.w, hv[pt].w, acc[k][pt]);
+          acc[k][pt] = mma(hv[pt].x, cv[k].x, acc[k][pt]);
+          acc[k][pt] = mma(hv[pt].y, cv[k].y, acc[k][pt]);
+          acc[k][pt] = mma(hv[pt].z, cv[k].z, acc[k][pt]);
+          acc[k][pt] = mma(hv[pt].w, cv[k].w, acc[k][pt]);
         }
       }
     };
+    float4 hA[TP], cA[RT], hB[TP], cB[RT];
+    load_nb(0, hA, cA);
 #pragma unroll 1
     for (int nb = 0; nb < N / 16; nb += 2) {
       const bool two = nb + 1 < N / 16;     // N / 16 is 1 for N = 16
@@ -371,9 +363,55 @@ void k_chunk_out_f32(ScanArgs a) {
       if (nb + 2 < N / 16) load_nb(nb + 2, hA, cA);
       mma_nb(hB, cB);
     }
+  };
+
+  // ---- prefix sum, x staging, decay tables (ends with a barrier) ----
+  auto stage = [&]() {
+    const DeltaScan ds = chunk_scan_stage1(a, c, h, dtv, s_wsum);
+    __syncthreads();
+    chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
+#pragma unroll
+    for (int i = 0; i < XLB; ++i) {
+      const int e = i * kThreads + tid, j = e / XQ, m = e % XQ;
+      if (e < nx) st4(&s_x[j * XS + 4 * m], xv_stage[i]);
+    }
+    __syncthreads();
+    for (int e = tid; e < (NBLK - 1) * LMAX; e += kThreads) {
+      const int R = e / LMAX + 1, j = e % LMAX;
+      const int r = min(64 * R, Lc - 1);
+      s_w[e] = (j < r) ? fast_exp(s_cum[r] - s_cum[j]) * s_d[j] : 0.0f;
+    }
+    __syncthreads();
+  };
+
+  // The workgroups sharing a compute unit start together; alternating the
+  // order of the two independent phases lets one workgroup's staging (LDS
+  // and vector work, waits) overlap another's inter-chunk term (matrix
+  // cores).  Workgroups are dealt to the 256 compute units in rounds of 256
+  // (blockIdx % 8 picks the XCD, the rest the unit), so the round's parity
+  // is what differs between the workgroups of one unit.
+  if ((blockIdx.x >> 8) & 1) {
+    stage();
+    inter();
+  } else {
+    inter();
+    stage();
   }
 
-  // ---- intra-chunk term: row tile by row tile, one block of 64 keys at a time ----
+  // decay from the chunk start: column i = 16 I + r16 of every accumulator
+  float cumk[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    const int ri = 16 * Ik[k] + r16;
+    cumk[k] = s_cum[min(ri, Lc - 1)];
+    const float sc = (vk[k] && ri < Lc) ? fast_exp(cumk[k]) : 0.0f;
+#pragma unroll
+    for (int pt = 0; pt < TP; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[k][pt][r] *= sc;
+  }
+
+  // ---- intra-chunk term: column tile by column tile, one block of 64 keys at a time ----
   const float* S = a.ws_cb + ((b * a.Nc + c) * a.G + g) * a.L * a.L;
   const float* xq = &s_x[4 * q * XS + r16];   // + key * XS + pt * 16
 #pragma unroll
@@ -408,14 +446,14 @@ void k_chunk_out_f32(ScanArgs a) {
           const float m2 = st[t].z * u_i * w4[t].z, m3 = st[t].w * u_i * w4[t].w;
 #pragma unroll
           for (int pt = 0; pt < TP; ++pt) {
-            acc[k][pt] = mma(m0, xv[t][0][pt], acc[k][pt]);
-            acc[k][pt] = mma(m1, xv[t][1][pt], acc[k][pt]);
-            acc[k][pt] = mma(m2, xv[t][2][pt], acc[k][pt]);
-            acc[k][pt] = mma(m3, xv[t][3][pt], acc[k][pt]);
+            acc[k][pt] = mma(xv[t][0][pt], m0, acc[k][pt]);
+            acc[k][pt] = mma(xv[t][1][pt], m1, acc[k][pt]);
+            acc[k][pt] = mma(xv[t][2][pt], m2, acc[k][pt]);
+            acc[k][pt] = mma(xv[t][3][pt], m3, acc[k][pt]);
           }
         }
       } else {
-        // the row tile's own block, up to the diagonal: masked exponentials
+        // the column tile's own block, up to the diagonal: masked exponentials
         const int nt = I - 4 * R + 1;           // key tiles up to the diagonal (uniform)
         float4 cj[4], dj[4];
 #pragma unroll
@@ -440,10 +478,10 @@ void k_chunk_out_f32(ScanArgs a) {
             const float m3 = (j0 + 3 <= ri) ? st[t].w * fast_exp(cum_i - cj[t].w) * dj[t].w : 0.0f;
 #pragma unroll
             for (int pt = 0; pt < TP; ++pt) {
-              acc[k][pt] = mma(m0, xv[t][0][pt], acc[k][pt]);
-              acc[k][pt] = mma(m1, xv[t][1][pt], acc[k][pt]);
-              acc[k][pt] = mma(m2, xv[t][2][pt], acc[k][pt]);
-              acc[k][pt] = mma(m3, xv[t][3][pt], acc[k][pt]);
+              acc[k][pt] = mma(xv[t][0][pt], m0, acc[k][pt]);
+              acc[k][pt] = mma(xv[t][1][pt], m1, acc[k][pt]);
+              acc[k][pt] = mma(xv[t][2][pt], m2, acc[k][pt]);
+              acc[k][pt] = mma(xv[t][3][pt], m3, acc[k][pt]);
             }
           }
         }
@@ -461,20 +499,23 @@ void k_chunk_out_f32(ScanArgs a) {
     }
   }
 
-  // ---- skip term and store ----
+  // ---- skip term and store: lane holds y[i][p..p+3], p = p0 + 16 pt + 4q ----
   const float Dh = a.D ? a.D[h] : 0.0f;
   float* yg = reinterpret_cast<float*>(a.y);
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
     if (!vk[k]) continue;
+    const int i = 16 * Ik[k] + r16;
+    if (i < Lc) {
+      float* row = yg + ((b * a.T + t0 + i) * a.H + h) * P + p0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * Ik[k] + 4 * q + r;
-      if (i < Lc) {
-        const int64_t row = ((b * a.T + t0 + i) * a.H + h) * P + p0;
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-          yg[row + pt * 16 + r16] = acc[k][pt][r] + Dh * s_x[i * XS + pt * 16 + r16];
+      for (int pt = 0; pt < TP; ++pt) {
+        const float4 xv4 = ld4(&s_x[i * XS + 16 * pt + 4 * q]);
+        const f32x4 v = acc[k][pt];
+        // y is not read again by the scan: stream it past the caches
+        __builtin_nontemporal_store(
+            f32x4{v[0] + Dh * xv4.x, v[1] + Dh * xv4.y, v[2] + Dh * xv4.z, v[3] + Dh * xv4.w},
+            reinterpret_cast<f32x4*>(row + 16 * pt + 4 * q));
       }
     }
   }
@@ -491,12 +532,10 @@ hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
   if ((e = rec(0)) != hipSuccess) return e;
   if ((e = rec(1)) != hipSuccess) return e;
   const int nrt = (int)((a.L + 15) / 16), ntiles = nrt * (nrt + 1) / 2;
-  const int64_t items = a.Bt * a.Nc * a.G * ntiles;
-  const int64_t ncb = ((items + 3) / 4 + 7) / 8 * 8;
   constexpr int NW = N < 64 ? N : 64;
   const int64_t units1 = a.Bt * a.Nc * a.H * (N / NW);
-  hipLaunchKernelGGL((k_cb_and_chunk_state_f32<P, N, NW>), dim3((unsigned)(ncb + units1)),
-                     dim3(kThreads), 0, stream, a, ntiles, ncb);
+  hipLaunchKernelGGL((k_cb_and_chunk_state_f32<P, N, NW>), dim3((unsigned)units1),
+                     dim3(kThreads), 0, stream, a, ntiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // phase 2: inter-chunk recurrence
   if ((e = rec(2)) != hipSuccess) return e;
