@@ -18,6 +18,14 @@ causal half of each L x L block, C B^T once per group):
   decode bytes/token = 8HPN (state read + write) + HP(s_x + s_y) + 4H + 2GN s_BC
 Peaks are MI355X's published dense figures (fp32 MFMA 157.3 TFLOP/s, bf16
 2.5 PFLOP/s, HBM3E 8 TB/s).
+
+roofline.traffic is the HBM bytes one launch of the reported kernel moved,
+from rocprofv3 FETCH_SIZE and WRITE_SIZE counter runs (one counter per run)
+scaled by what the same counters read for a plain copy of known size
+(python bench.py --copy-calibration: the library's own float4 copy kernel on
+a 1 GiB state).  The values are kept in TRAFFIC below with a digest of the
+kernel's sources; once a source changes the digest no longer matches and
+traffic is reported as null until the counters are taken again.
 """
 from __future__ import annotations
 
@@ -37,6 +45,20 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "m130_f32"
+CSRC = os.path.join(ROOT, "state_space_model_amd", "csrc")
+# sources a kernel's code comes from (the digest that keys TRAFFIC)
+KERNEL_SOURCES = {
+    "chunk_out/f32": ["ssd_prefill_f32.hip", "ssd_prefill_common.h", "ssd_device.h"],
+    "chunk_out/bf16": ["ssd_prefill_bf16.hip", "ssd_prefill_common.h", "ssd_device.h"],
+    "decode": ["ssd_step.hip", "ssd_device.h"],
+}
+# HBM bytes per launch from the counter runs: (kernel key, workload) -> (bytes, digest)
+TRAFFIC = {
+    # counter runs and calibration: profiles/chunk_out_f32_m130_f32_decode_m2p7_b64_hbm_bytes.txt
+    ("chunk_out/f32", "m130_f32"): (41.17e6 + 30.55e6, "461d061fb242ece3"),
+    ("decode", "m2p7_decode_b64"): (169.12e6 + 168.48e6, "a9cd5d42c984beb1"),
+}
+COPY_CALIBRATION_BYTES = 1 << 30
 
 
 def prefill_flops_per_token(w):
@@ -63,6 +85,42 @@ def prefill_bytes_per_token(w, T):
 
 def decode_bytes_per_token(H, P, N, G, s):
     return 8 * H * P * N + H * P * 2 * s + 4 * H + 2 * G * N * s
+
+
+def source_digest(key):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[key]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(key, workload):
+    """Counter-derived HBM bytes per launch, or None if not measured for the current sources."""
+    entry = TRAFFIC.get((key, workload))
+    if entry is None or entry[1] != source_digest(key):
+        return None
+    return entry[0]
+
+
+def copy_calibration(ssd, torch, reps=5):
+    """A plain copy of known size for the counter calibration: an empty-sequence
+    scan copies the initial state (1 GiB) to the final state with the library's
+    float4 copy kernel (k_copy_or_zero)."""
+    Bt, H, P, N = 512, 64, 64, 128          # 2^28 float32 = 1 GiB
+    h0 = torch.randn(Bt, H, P, N, device="cuda")
+    fin = torch.empty_like(h0)
+    x = torch.empty(Bt, 0, H, P, device="cuda")
+    dt = torch.empty(Bt, 0, H, device="cuda")
+    B = torch.empty(Bt, 0, 1, N, device="cuda")
+    A = -torch.ones(H, device="cuda")
+    for _ in range(reps):
+        ssd.ssd_chunk_scan(x, dt, A, B, B, None, chunk=64, initial_state=h0, final_state=fin)
+    torch.cuda.synchronize()
+    assert torch.equal(fin, h0)
+    return {"copy_bytes_read": h0.numel() * 4, "copy_bytes_written": fin.numel() * 4,
+            "dispatches": reps, "kernel": "k_copy_or_zero"}
 
 
 def cpu_model():
@@ -179,7 +237,8 @@ def bench_decode(ssd, torch, batch, steps_n, warmup):
             "tokens_per_s": batch / (ms_step * 1e-3), "state_buffers": nstates,
             "state_bytes_each": state_bytes,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+                         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                         "traffic": traffic_for("decode", f"m2p7_decode_b{batch}")},
             "bytes_per_token": bpt}
 
 
@@ -227,6 +286,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the known-size copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -240,6 +301,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration(ssd, torch)))
+        return
     w = WORKLOADS[args.workload]
     if args.chunk:
         w = w.with_(chunk=args.chunk)
@@ -263,7 +327,9 @@ def main():
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk": w.chunk, "io_dtype": w.io_dtype, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": traffic_for(f"{dom}/{w.io_dtype}", w.name)
+                     if f"{dom}/{w.io_dtype}" in KERNEL_SOURCES else None,
                      "flops_per_launch": dom_flops, "avg_launch_ms": dom_ms},
         "prefill": {"algorithmic_tflops": fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12,
                     "mfma_peak_frac": fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12 / peak,
