@@ -105,9 +105,11 @@ typedef struct {
  * Both schedules (see ssd_chunk_scan_schedule) hold the float32 L x L matrix
  * C B^T of every (batch, chunk, group): 4*Bt*ceil(T/L)*G*L*L bytes.  The
  * phased schedule adds one float32 P x N state and one float32 decay per
- * (batch, head, chunk): 4*Bt*ceil(T/L)*H*(P*N+1) bytes; the chain schedule
- * adds a bfloat16 transposed copy of B per (batch, chunk, group):
- * 2*Bt*ceil(T/L)*G*N*L bytes.  Each region is rounded up to 256 bytes.
+ * (batch, head, chunk): 4*Bt*ceil(T/L)*H*(P*N+1) bytes, and with bfloat16 io
+ * a bfloat16 copy of the entering states: 2*Bt*ceil(T/L)*H*P*N bytes; the
+ * chain schedule adds a bfloat16 transposed copy of B per (batch, chunk,
+ * group): 2*Bt*ceil(T/L)*G*N*L bytes.  Each region is rounded up to 256
+ * bytes.
  */
 size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc);
 

@@ -50,7 +50,8 @@ struct ScanSizes {
   int64_t Nc = 0;
   bool chain = false;
   int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0;  // element counts
-  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_cb_bytes = 0, ws_bt_bytes = 0, ws_total = 0;
+  size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_cb_bytes = 0, ws_bt_bytes = 0, ws_hb_bytes = 0,
+         ws_total = 0;
 };
 
 ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
@@ -93,7 +94,10 @@ ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
     return SSD_ERR_UNSUPPORTED;
   s->ws_cb_bytes = round_up((size_t)cb_elems * 4, kAlign);
   s->ws_bt_bytes = s->chain ? round_up((size_t)bt_elems * 2, kAlign) : 0;
-  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes + s->ws_cb_bytes + s->ws_bt_bytes;
+  // the bfloat16 phased schedule hands the entering states to its output kernel in bf16
+  s->ws_hb_bytes = (!s->chain && d->io_dtype == SSD_BF16) ? round_up((size_t)ws_elems * 2, kAlign) : 0;
+  s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes + s->ws_cb_bytes + s->ws_bt_bytes +
+                s->ws_hb_bytes;
   return SSD_OK;
 }
 
@@ -158,6 +162,7 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   a.ws_cb = reinterpret_cast<float*>(static_cast<char*>(workspace) + s.ws_state_bytes +
                                      s.ws_alpha_bytes);
   a.ws_bt = static_cast<char*>(workspace) + s.ws_state_bytes + s.ws_alpha_bytes + s.ws_cb_bytes;
+  a.ws_hb = static_cast<char*>(a.ws_bt) + s.ws_bt_bytes;
   a.Bt = desc->batch; a.T = desc->seqlen; a.H = desc->nheads; a.G = desc->ngroups;
   a.L = desc->chunk; a.Nc = s.Nc;
   a.softplus = desc->dt_softplus ? 1 : 0;

@@ -22,6 +22,7 @@ struct ScanArgs {
   float* ws_alpha;        // [Bt,H,Nc]: exp(total decay of the chunk)
   float* ws_cb;           // [Bt,Nc,G,L,L]: C B^T of each chunk (causal 16x16 tiles)
   void* ws_bt;            // [Bt,Nc,G,N,L] bf16: B of each chunk, transposed (token-contiguous)
+  void* ws_hb;            // [Bt,H,Nc,P,N] bf16: entering states, rounded (bf16 phased schedule)
   int64_t Bt, T, H, G, L, Nc;
   int32_t softplus;
   float dt_min, dt_max;
@@ -64,8 +65,10 @@ bool step_shape_supported(int64_t P, int64_t N);
 hipError_t launch_scan_f32(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* events);
 hipError_t launch_scan_bf16(const ScanArgs& a, int P, int N, hipStream_t stream, hipEvent_t* events);
 
-// Inter-chunk recurrence over the workspace states (both io types).
-hipError_t launch_state_pass(const ScanArgs& a, int P, int N, hipStream_t stream);
+// Inter-chunk recurrence over the workspace states (both io types).  The
+// entering states go to ws_state in float32, or, when bf16_out, to ws_hb
+// rounded to bfloat16 (the only form the bfloat16 output kernel uses).
+hipError_t launch_state_pass(const ScanArgs& a, int P, int N, hipStream_t stream, bool bf16_out);
 
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);

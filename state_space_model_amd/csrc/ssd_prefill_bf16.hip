@@ -639,8 +639,8 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_bf16(ScanArgs a
 
 // ---------------------------------------------------------------------------
 // Phased schedule, phase 3: chunk outputs, one workgroup per (b, c, h).  The
-// entering state h_{c-1} (float32, from the state pass) is copied to LDS, x
-// is staged transposed, then the shared chunk_outputs runs.
+// entering state h_{c-1} (rounded to bf16 by the state pass) is copied to
+// LDS, x is staged transposed, then the shared ChunkOut runs.
 // ---------------------------------------------------------------------------
 constexpr int kOutPass = 2;     // column tiles per output pass, phased schedule
 constexpr int kChainPass = 1;   // and chain schedule (which holds more besides)
@@ -667,14 +667,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out_bf16(ScanArgs a) {
   xs.load(a, b, c, h);
   constexpr int HV = P * N / 8;                 // 8-element groups of the state
   constexpr int NHV = (HV + kThreads - 1) / kThreads;
-  const float* hp = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
-  float4 hv[NHV][2];
+  const bf16* hp = reinterpret_cast<const bf16*>(a.ws_hb) +
+                   ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
+  bf16x8 hv[NHV];
 #pragma unroll
-  for (int i = 0; i < NHV; ++i) {
-    const int e = min(tid + i * kThreads, HV - 1) * 8;
-    hv[i][0] = ld4(hp + e);
-    hv[i][1] = ld4(hp + e + 4);
-  }
+  for (int i = 0; i < NHV; ++i) hv[i] = ld8(hp + min(tid + i * kThreads, HV - 1) * 8);
   ChunkOut<P, N, LMAX, kOutPass> out(a, b, c, h, g, Lc);
   out.prefetch(0);
   chunk_delta_cumsum(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
@@ -683,13 +680,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out_bf16(ScanArgs a) {
 #pragma unroll
   for (int i = 0; i < NHV; ++i) {
     const int e = tid + i * kThreads;
-    if (e < HV) {
-      bf16x8 v;
-      v[0] = (bf16)hv[i][0].x; v[1] = (bf16)hv[i][0].y; v[2] = (bf16)hv[i][0].z;
-      v[3] = (bf16)hv[i][0].w; v[4] = (bf16)hv[i][1].x; v[5] = (bf16)hv[i][1].y;
-      v[6] = (bf16)hv[i][1].z; v[7] = (bf16)hv[i][1].w;
-      st8(s_h + ((e * 8) / N) * HS + (e * 8) % N, v);
-    }
+    if (e < HV) st8(s_h + ((e * 8) / N) * HS + (e * 8) % N, hv[i]);
   }
   __syncthreads();
   out.run(s_d, s_cum, s_w, s_xt, s_h);
@@ -910,7 +901,7 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
                      stream, a, cb_tiles(a));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = rec(2)) != hipSuccess) return e;
-  if ((e = launch_state_pass(a, P, N, stream)) != hipSuccess) return e;
+  if ((e = launch_state_pass(a, P, N, stream, true)) != hipSuccess) return e;
   if ((e = rec(3)) != hipSuccess) return e;
   if (a.L <= 256) {
     hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 256>), dim3((unsigned)units), dim3(kThreads), 0,

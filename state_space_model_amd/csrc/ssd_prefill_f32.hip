@@ -539,7 +539,7 @@ hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // phase 2: inter-chunk recurrence
   if ((e = rec(2)) != hipSuccess) return e;
-  if ((e = launch_state_pass(a, P, N, stream)) != hipSuccess) return e;
+  if ((e = launch_state_pass(a, P, N, stream, false)) != hipSuccess) return e;
   // phase 3: outputs
   if ((e = rec(3)) != hipSuccess) return e;
   constexpr int PW = P < 32 ? P : 32;

@@ -117,6 +117,8 @@ def test_schedule_and_workspace(kw, chain):
         want = cb + _r256(2 * Bt * nc * G * N * L)
     else:
         want = _r256(4 * Bt * H * nc * P * N) + _r256(4 * Bt * H * nc) + cb
+        if d.io_dtype == 1:
+            want += _r256(2 * Bt * H * nc * P * N)
     assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d)) == want
 
 
