@@ -242,6 +242,53 @@ def bench_decode(ssd, torch, batch, steps_n, warmup):
             "bytes_per_token": bpt}
 
 
+def bench_cached_vs_recompute(ssd, torch, context=4096, reps=20):
+    """Cached decode against recomputing the prefix: the time to produce the
+    output of token `context` from the cached state with one ssd_step, and by
+    re-running ssd_chunk_scan over all context+1 tokens (2.7B shape, batch 1,
+    bf16 x/B/C).  The layer-level analogue of the pages' cached-versus-
+    recompute comparison at a 4096-token context."""
+    from ssd_inputs import WORKLOADS, make_inputs
+    w = WORKLOADS["m2p7_decode"].with_(batch=1, seqlen=context + 1)
+    inp = make_inputs(w)
+    d = {k: v.cuda() for k, v in inp.items()}
+    Bt, T, H, P = d["x"].shape
+    N = d["B"].shape[3]
+    y = torch.empty_like(d["x"])
+    fin = torch.empty(Bt, H, P, N, device="cuda")
+    ws = torch.empty(ssd.ssd_chunk_scan_workspace_bytes(d["x"], d["B"], w.chunk),
+                     dtype=torch.uint8, device="cuda")
+    state = torch.empty(Bt, H, P, N, device="cuda")
+    x_t, dt_t = d["x"][:, T - 1].contiguous(), d["dt"][:, T - 1].contiguous()
+    B_t, C_t = d["B"][:, T - 1].contiguous(), d["C"][:, T - 1].contiguous()
+    y_t = torch.empty_like(x_t)
+
+    def recompute():
+        ssd.ssd_chunk_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=w.chunk,
+                           dt_bias=d["dt_bias"], y=y, final_state=fin, workspace=ws)
+
+    def step():
+        ssd.ssd_step(state, x_t, dt_t, d["A"], B_t, C_t, d["D"], dt_bias=d["dt_bias"], y_t=y_t)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    t_re = timed(recompute)
+    state.copy_(fin)
+    t_st = timed(step)
+    return {"context": context, "shape": "H=80 P=64 N=128 bf16 x/B/C, batch 1",
+            "recompute_us": t_re, "cached_step_us": t_st, "speedup": t_re / t_st}
+
+
 def cpu_baseline(w, target_s=10.0):
     """The fp64 oracle on the host cores, on a bounded sample of the workload."""
     import oracle
@@ -344,6 +391,8 @@ def main():
               flush=True)
         out["decode"] = bench_decode(ssd, torch, args.decode_batch, args.decode_steps,
                                      args.warmup)
+        print("[bench] cached decode vs recompute at 4096", file=sys.stderr, flush=True)
+        out["cached_vs_recompute"] = bench_cached_vs_recompute(ssd, torch)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)
