@@ -7,12 +7,16 @@ links anything here, and nothing here imports the GPU library.
 Contents
   scan(...)         token-by-token fp64 recurrence (C, OpenMP over (b, h))
   step(...)         the same recurrence run for one token from a given state
+  conv1d(...)       depthwise causal convolution over time with its k-1 input
+                    window carried in and out (C, fp64)
+  conv1d_step(...)  the same convolution for one token from a cached window
   dual_form.py      dense quadratic "dual form" materialisation (numpy, fp64)
   chunked.py        chunked SSD algorithm written step by step (numpy, fp64)
   brute.py          the recurrence at 50 significant digits (mpmath)
 
 The source is "Compiler-First State Space Duality and Portable O(1)
-Autoregressive Caching" (Background, Eq. 1-3; SSD properties; O(1) cache).
+Autoregressive Caching" (Background, Eq. 1-3; SSD properties; O(1) cache;
+Setup for the convolution width).
 The recurrence is what the chunked method computes faster; the other three are
 independent formulations used to pin it.
 """
@@ -39,6 +43,8 @@ def _load():
         i64, vp = ctypes.c_int64, ctypes.c_void_p
         lib.ssd_oracle_scan.argtypes = [i64] * 6 + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
                                                            ctypes.c_double, vp, vp, ctypes.c_int]
+        lib.ssd_oracle_conv1d.restype = ctypes.c_int
+        lib.ssd_oracle_conv1d.argtypes = [i64] * 4 + [vp] * 4 + [ctypes.c_int, vp, vp, ctypes.c_int]
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -111,3 +117,38 @@ def step(state, x_t, dt_t, A, B_t, C_t, D=None, dt_bias=None, *, dt_softplus: bo
     y, fin = scan(x_t[:, None], dt_t[:, None], A, B_t[:, None], C_t[:, None], D, dt_bias,
                   state, dt_softplus=dt_softplus, dt_min=dt_min, dt_max=dt_max)
     return y[:, 0], fin
+
+
+def conv1d(x, w, bias=None, state=None, *, silu: bool = False, nthreads: int = 0
+           ) -> Tuple[np.ndarray, np.ndarray]:
+    """Depthwise causal convolution over time (O(1) cache section: a sliding
+    window of the k-1 previous inputs per channel; Setup: k = 4).
+
+    Shapes: x [Bt,T,D], w [D,k] (w[c][0] multiplies the oldest input of the
+    window, w[c][k-1] the current one), bias [D] or None, state [Bt,D,k-1]
+    (the k-1 inputs before x[:,0], oldest first) or None for zeros.
+    Float inputs are taken as float32 values; state in float64.
+    Returns (y [Bt,T,D], state_out [Bt,D,k-1] = the last k-1 inputs), float64.
+    """
+    x, w, bias, state = _f32(x), _f32(w), _f32(bias), _f64(state)
+    Bt, T, D = x.shape
+    K = w.shape[1]
+    assert w.shape == (D, K) and K >= 1
+    assert bias is None or bias.shape == (D,)
+    assert state is None or state.shape == (Bt, D, K - 1)
+    y = np.empty((Bt, T, D), dtype=np.float64)
+    st = np.empty((Bt, D, K - 1), dtype=np.float64)
+    rc = _load().ssd_oracle_conv1d(Bt, T, D, K, _ptr(x), _ptr(w), _ptr(bias), _ptr(state),
+                                   int(bool(silu)), _ptr(y), _ptr(st), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_conv1d failed with code {rc}")
+    return y, st
+
+
+def conv1d_step(state, x_t, w, bias=None, *, silu: bool = False
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """One token of conv1d from a cached window: state [Bt,D,k-1], x_t [Bt,D].
+    Returns (y_t [Bt,D], new_state [Bt,D,k-1]), both float64."""
+    x_t = _f32(x_t)
+    y, st = conv1d(x_t[:, None], w, bias, state, silu=silu)
+    return y[:, 0], st

@@ -116,3 +116,63 @@ int ssd_oracle_scan(int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N, int6
   }
   return failed ? 2 : 0;
 }
+
+/*
+ * Depthwise causal convolution over time, the step that precedes the SSD scan
+ * in a Mamba-2 block ("Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching", O(1) cache: decoding updates a depthwise convolution
+ * over a sliding window of the k-1 previous inputs, held in a cache of shape
+ * (B, D_conv, k-1); Setup: kernel size k = 4).  Per batch row b and channel c,
+ * with the window w[c][0..k-1] applied oldest input first:
+ *
+ *   xp[j] = state_in[b][c][j]          for j < k-1     (zeros if no state)
+ *   xp[j] = x[b][j-(k-1)][c]           for k-1 <= j < k-1+T
+ *   z[t]  = bias[c] + sum_{i<k} w[c][i] * xp[t+i]
+ *   y[b][t][c] = silu ? z / (1 + exp(-z)) : z
+ *   state_out[b][c][i] = xp[T+i]       for i < k-1     (the last k-1 inputs)
+ *
+ * Layouts: x, y [Bt,T,D]; w [D,k]; bias [D]; states [Bt,D,k-1].  Inputs are
+ * float32 values (bfloat16 upcast exactly), states and outputs double, every
+ * operation in double.  (b, c) pairs run in parallel; each is serial in t.
+ * Returns 0 on success, 1 on a bad argument, 2 when scratch allocation fails.
+ */
+int ssd_oracle_conv1d(int64_t Bt, int64_t T, int64_t D, int64_t K, const float* x,
+                      const float* w, const float* bias, const double* state_in, int silu,
+                      double* y, double* state_out, int nthreads) {
+  if (Bt < 0 || T < 0 || D <= 0 || K <= 0 || !w) return 1;
+  if (T > 0 && (!x || !y)) return 1;
+  const int64_t npairs = Bt * D;
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double* xp = (double*)malloc(sizeof(double) * (size_t)(K - 1 + T + 1));
+    if (!xp) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    }
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+    for (int64_t pair = 0; pair < npairs; ++pair) {
+      if (!xp) continue;
+      const int64_t b = pair / D, c = pair % D;
+      for (int64_t j = 0; j < K - 1; ++j)
+        xp[j] = state_in ? state_in[(b * D + c) * (K - 1) + j] : 0.0;
+      for (int64_t t = 0; t < T; ++t) xp[K - 1 + t] = (double)x[(b * T + t) * D + c];
+      for (int64_t t = 0; t < T; ++t) {
+        double z = bias ? (double)bias[c] : 0.0;
+        for (int64_t i = 0; i < K; ++i) z += (double)w[c * K + i] * xp[t + i];
+        y[(b * T + t) * D + c] = silu ? z / (1.0 + exp(-z)) : z;
+      }
+      if (state_out)
+        for (int64_t i = 0; i < K - 1; ++i) state_out[(b * D + c) * (K - 1) + i] = xp[T + i];
+    }
+    free(xp);
+  }
+  return failed ? 2 : 0;
+}

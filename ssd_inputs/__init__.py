@@ -19,6 +19,18 @@ Draws are made in float32 on the CPU with a torch.Generator, in the fixed order
 dt_bias, A, D, x, dt, B, C.  x, B and C are then rounded to bfloat16
 (round-to-nearest-even) when the workload says so; every consumer receives the
 same rounded values.
+
+The depthwise causal convolution that precedes the scan in a Mamba-2 block
+(O(1) cache section; Setup: kernel size k = 4, expand factor 2, so
+D_conv = 2 d_model + 2 G N channels) takes, in draw order:
+
+  weight   ~ U(-1/sqrt(k), 1/sqrt(k))         [D, k]
+  bias     ~ U(-1/sqrt(k), 1/sqrt(k))         [D]
+  x        ~ N(0, 1)                          [Bt, T, D]
+  state    ~ N(0, 1)  (when asked)            [Bt, D, k-1]
+
+(the bound is the usual initialisation scale of a depthwise kernel of fan-in
+k); x and the state are rounded to bfloat16 for bfloat16 workloads.
 """
 
 from __future__ import annotations
@@ -108,6 +120,55 @@ def make_inputs(w: Workload, seed: Optional[int] = None,
     }
     if with_initial_state:
         out["h0"] = torch.randn(Bt, H, P, N, generator=g, dtype=f32)
+    return out
+
+
+@dataclass(frozen=True)
+class ConvWorkload:
+    """Shape and dtype of one synthetic depthwise causal convolution problem."""
+
+    name: str
+    batch: int
+    seqlen: int
+    channels: int
+    width: int = 4
+    io_dtype: str = "f32"  # dtype of x, y and the cached window
+    silu: bool = True
+    seed: int = 2000
+    note: str = ""
+
+    def with_(self, **kw) -> "ConvWorkload":
+        return replace(self, **kw)
+
+
+# D_conv = 2 d_model + 2 G N: 2 * 768 + 256 for the 130M shape (H = 24 heads of
+# 64), 2 * 2560 + 256 for the 2.7B shape (H = 80 heads of 64).
+CONV_WORKLOADS: Dict[str, ConvWorkload] = {
+    "conv_m130_f32": ConvWorkload("conv_m130_f32", 1, 4096, 1792, 4, "f32", True, 2001,
+                                  note="130M-shaped conv1d prefill, fp32"),
+    "conv_m2p7_bf16": ConvWorkload("conv_m2p7_bf16", 1, 4096, 5376, 4, "bf16", True, 2002,
+                                   note="2.7B-shaped conv1d prefill, bf16"),
+    "conv_m2p7_decode": ConvWorkload("conv_m2p7_decode", 64, 1, 5376, 4, "bf16", True, 2004,
+                                     note="2.7B-shaped conv1d decode step, bf16 window"),
+}
+
+
+def make_conv_inputs(w: ConvWorkload, seed: Optional[int] = None,
+                     with_state: bool = False) -> Dict[str, torch.Tensor]:
+    """Draw one convolution problem's inputs on the CPU: x and (when asked)
+    state in the io dtype, weight and bias in float32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed if seed is None else seed)
+    Bt, T, Dc, K = w.batch, w.seqlen, w.channels, w.width
+    f32 = torch.float32
+    bound = 1.0 / math.sqrt(K)
+    weight = (torch.rand(Dc, K, generator=g, dtype=f32) * 2.0 - 1.0) * bound
+    bias = (torch.rand(Dc, generator=g, dtype=f32) * 2.0 - 1.0) * bound
+    x = torch.randn(Bt, T, Dc, generator=g, dtype=f32)
+    io = _torch_dtype(w.io_dtype)
+    out = {"x": x.to(io), "weight": weight, "bias": bias}
+    if with_state:
+        out["state"] = torch.randn(Bt, Dc, K - 1, generator=g, dtype=f32).to(io)
     return out
 
 
