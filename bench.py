@@ -289,6 +289,93 @@ def bench_cached_vs_recompute(ssd, torch, context=4096, reps=20):
             "recompute_us": t_re, "cached_step_us": t_st, "speedup": t_re / t_st}
 
 
+def conv_bytes(Bt, T, D, K, es):
+    """Algorithmic bytes of one conv1d call: x read and y written once, the
+    window read and written once, weights and bias read once."""
+    return 2 * Bt * T * D * es + 2 * Bt * D * (K - 1) * es + D * (K + 1) * 4
+
+
+def bench_conv(ssd, torch, warmup, reps=20, steps_n=256):
+    """The depthwise causal conv1d before the scan: a 4096-token prefill of
+    the 2.7B shape (D_conv 5376, bf16) and the one-token step at batch 64,
+    the latter captured in a HIP graph.  Inputs rotate over enough buffers
+    to exceed twice the 256 MB last-level cache."""
+    from ssd_inputs import CONV_WORKLOADS, make_conv_inputs
+    out = {}
+    w = CONV_WORKLOADS["conv_m2p7_bf16"]
+    inp = make_conv_inputs(w, with_state=True)
+    d = {k: v.cuda() for k, v in inp.items()}
+    Bt, T, Dc = d["x"].shape
+    K = d["weight"].shape[1]
+    es = d["x"].element_size()
+    nbytes = conv_bytes(Bt, T, Dc, K, es)
+    nsets = max(1, math.ceil(2 * MALL_BYTES / nbytes))
+    xs = [d["x"]] + [torch.randn_like(d["x"], dtype=torch.float32).to(d["x"].dtype)
+                     for _ in range(nsets - 1)]
+    ys = [torch.empty_like(d["x"]) for _ in range(nsets)]
+    sts = [torch.empty_like(d["state"]) for _ in range(nsets)]
+    for i in range(max(1, warmup)):
+        ssd.ssd_conv1d(xs[i % nsets], d["weight"], d["bias"], state=d["state"], y=ys[i % nsets],
+                       state_out=sts[i % nsets])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        ssd.ssd_conv1d(xs[i % nsets], d["weight"], d["bias"], state=d["state"], y=ys[i % nsets],
+                       state_out=sts[i % nsets])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out["prefill"] = {"workload": w.name, "batch": Bt, "seqlen": T, "channels": Dc, "width": K,
+                      "io_dtype": w.io_dtype, "silu": w.silu, "ms": ms,
+                      "tokens_per_s": Bt * T / (ms * 1e-3), "bytes_per_launch": nbytes,
+                      "rotated_sets": nsets,
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                   "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+    wd = CONV_WORKLOADS["conv_m2p7_decode"]
+    inp = make_conv_inputs(wd.with_(seqlen=steps_n), with_state=True)
+    dd = {k: v.cuda() for k, v in inp.items()}
+    Bt = wd.batch
+    xs = dd["x"].transpose(0, 1).contiguous()        # [steps, Bt, D]
+    ys = torch.empty_like(xs)
+    win_bytes = Bt * Dc * (K - 1) * es
+    nwin = max(1, math.ceil(2 * MALL_BYTES / (win_bytes + 2 * Bt * Dc * es)))
+    nwin = min(nwin, steps_n)
+    wins = [dd["state"].clone() for _ in range(nwin)]
+
+    def body():
+        for t in range(steps_n):
+            ssd.ssd_conv1d_step(wins[t % nwin], xs[t], dd["weight"], dd["bias"], y_t=ys[t])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / (3 * steps_n)
+    sbytes = conv_bytes(Bt, 1, Dc, K, es)
+    gbs = sbytes / (ms_step * 1e-3) / 1e9
+    out["step"] = {"workload": wd.name, "batch": Bt, "channels": Dc, "width": K,
+                   "io_dtype": wd.io_dtype, "steps": steps_n, "graph_replays": 3,
+                   "us_per_step": ms_step * 1e3, "tokens_per_s": Bt / (ms_step * 1e-3),
+                   "bytes_per_step": sbytes, "windows": nwin,
+                   "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
+                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+    return out
+
+
 def cpu_baseline(w, target_s=10.0):
     """The fp64 oracle on the host cores, on a bounded sample of the workload."""
     import oracle
@@ -393,6 +480,8 @@ def main():
                                      args.warmup)
         print("[bench] cached decode vs recompute at 4096", file=sys.stderr, flush=True)
         out["cached_vs_recompute"] = bench_cached_vs_recompute(ssd, torch)
+        print("[bench] conv1d prefill and step", file=sys.stderr, flush=True)
+        out["conv1d"] = bench_conv(ssd, torch, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

@@ -1,7 +1,7 @@
 /*
  * ssd.h -- C ABI of the MI355X (gfx950) Mamba-2 SSD library (libssd.so).
  *
- * Two operations, following "Compiler-First State Space Duality and Portable
+ * Operations, following "Compiler-First State Space Duality and Portable
  * O(1) Autoregressive Caching" (arXiv 2603.09555):
  *
  *   ssd_chunk_scan  the chunked state-space-duality scan over a whole
@@ -10,6 +10,10 @@
  *                   state matrix", "chunked recurrence", "static control flow".
  *   ssd_step        one token of the recurrence from a fixed-size state held
  *                   on the device (decode): the O(1) cache section.
+ *   ssd_conv1d, ssd_conv1d_step
+ *                   the depthwise causal convolution that precedes the scan
+ *                   in a Mamba-2 block, over a sequence and for one token
+ *                   from its cached window (O(1) cache section; Setup: k = 4).
  *
  * Both compute, for every batch row b and head h (g = h / (H/G) is the B/C
  * group of head h), the selective diagonal SSM
@@ -31,9 +35,10 @@
  *    descriptor, which is a host pointer read during the call only.
  *  - Tensors are dense, contiguous, row-major, in the layouts listed per call.
  *    x, B, C, y and every state (and the workspace) must be 16-byte aligned;
- *    dt, dt_bias, A and D 4-byte aligned.
+ *    dt, dt_bias, A, D and the convolution weights and bias 4-byte aligned.
  *  - x, B, C and y share one dtype (desc->io_dtype: SSD_F32 or SSD_BF16);
- *    dt, dt_bias, A, D and every state are float32.  All arithmetic inside is
+ *    dt, dt_bias, A, D and every SSM state are float32 (the convolution
+ *    window holds past inputs and keeps io_dtype).  All arithmetic inside is
  *    float32 (decay, exponentials, states, accumulation); bfloat16 appears
  *    only as matrix-core operands and at the output store (round to nearest
  *    even).
@@ -63,7 +68,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
   SSD_OK = 0,
@@ -197,6 +202,64 @@ ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const 
 ssd_status ssd_step(const ssd_step_desc* desc, float* state, const void* x_t, const float* dt_t,
                     const float* dt_bias, const float* A, const void* B_t, const void* C_t,
                     const float* D, void* y_t, hipStream_t stream);
+
+/* Problem description of a depthwise causal convolution (prefill or step). */
+typedef struct {
+  int64_t batch;     /* Bt >= 0 */
+  int64_t seqlen;    /* T >= 0 (ssd_conv1d); not used by ssd_conv1d_step */
+  int64_t channels;  /* D >= 1 */
+  int64_t width;     /* k: taps per channel, the current input and k-1 cached ones */
+  int32_t io_dtype;  /* ssd_dtype of x, y and the cached window */
+  int32_t silu;      /* 1: y = z * logistic(z) of the convolution z; 0: y = z */
+} ssd_conv_desc;
+
+/*
+ * Depthwise causal convolution over a sequence, carrying the window of the
+ * k-1 previous inputs in and out.
+ *
+ * Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
+ * Caching", O(1) cache section (each channel is convolved over a sliding
+ * window of its k-1 previous inputs, cached with shape (B, D_conv, k-1);
+ * prefill initialises that cache) and Setup (kernel size k = 4).  Per batch
+ * row b and channel c, with xp = (state_in[b][c][0..k-2], x[b][0..T-1][c]):
+ *
+ *   z[t] = bias[c] + sum_{i<k} w[c][i] * xp[t+i]     (w[c][k-1]: current input)
+ *   y[b][t][c] = silu ? z[t] * logistic(z[t]) : z[t]
+ *   state_out[b][c][j] = xp[T+j], j < k-1             (the last k-1 inputs)
+ *
+ *   x     [Bt,T,D] io_dtype       w    [D,k] f32      bias [D] f32 or NULL
+ *   state_in  [Bt,D,k-1] io_dtype, oldest input first, or NULL (zeros)
+ *   y     [Bt,T,D] io_dtype (written)
+ *   state_out [Bt,D,k-1] io_dtype (written) or NULL; it may be state_in
+ *             itself (updated in place) but may not overlap it otherwise.
+ *
+ * The sum is float32 fused multiply-adds in the order i = 0..k-1 starting
+ * from the bias, the same in ssd_conv1d_step, so a sequence split anywhere
+ * (each part seeded with the previous part's state_out) or run token by
+ * token gives bitwise the same outputs.  The window is kept in io_dtype: it
+ * holds past inputs, which that type represents exactly.  Supported: k in
+ * {2, 3, 4}; any D (D a multiple of 8 for bfloat16 or of 4 for float32 takes
+ * the 16-byte vector path).  y may not overlap any input or state.
+ */
+ssd_status ssd_conv1d(const ssd_conv_desc* desc, const void* x, const float* w,
+                      const float* bias, const void* state_in, void* y, void* state_out,
+                      hipStream_t stream);
+
+/*
+ * One token of the depthwise causal convolution from its cached window, the
+ * window updated in place (O(1) cache section: the decode body updates the
+ * convolution window, then runs one recurrence step).
+ *
+ *   state [Bt,D,k-1] io_dtype, read and overwritten: the oldest input drops
+ *         out and x_t enters as the newest
+ *   x_t   [Bt,D] io_dtype         w [D,k] f32      bias [D] f32 or NULL
+ *   y_t   [Bt,D] io_dtype (written; must not overlap the state or inputs)
+ *
+ * y_t[b][c] = act(bias[c] + sum_{i<k-1} w[c][i] * state[b][c][i] + w[c][k-1] * x_t[b][c]),
+ * bitwise equal to ssd_conv1d over the one token.  desc->seqlen is not read.
+ */
+ssd_status ssd_conv1d_step(const ssd_conv_desc* desc, void* state, const void* x_t,
+                           const float* w, const float* bias, void* y_t, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* ssd_status_string(ssd_status status);

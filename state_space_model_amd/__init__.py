@@ -33,7 +33,8 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "S
                 4: "SSD_ERR_ALIGNMENT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE",
                 7: "SSD_ERR_HIP"}
 EXPORTED = ("ssd_chunk_scan", "ssd_chunk_scan_timed", "ssd_chunk_scan_workspace_bytes",
-            "ssd_chunk_scan_schedule", "ssd_step", "ssd_status_string", "ssd_abi_version")
+            "ssd_chunk_scan_schedule", "ssd_step", "ssd_conv1d", "ssd_conv1d_step",
+            "ssd_status_string", "ssd_abi_version")
 
 
 class ScanDesc(ctypes.Structure):
@@ -51,6 +52,12 @@ class StepDesc(ctypes.Structure):
                 ("ngroups", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
                 ("dt_softplus", ctypes.c_int32), ("dt_min", ctypes.c_float),
                 ("dt_max", ctypes.c_float)]
+
+
+class ConvDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("channels", ctypes.c_int64), ("width", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("silu", ctypes.c_int32)]
 
 
 class SSDError(RuntimeError):
@@ -79,6 +86,10 @@ def _load() -> ctypes.CDLL:
     L.ssd_chunk_scan_schedule.argtypes = [ctypes.POINTER(ScanDesc)]
     L.ssd_step.restype = i32
     L.ssd_step.argtypes = [ctypes.POINTER(StepDesc)] + [vp] * 9 + [vp]
+    L.ssd_conv1d.restype = i32
+    L.ssd_conv1d.argtypes = [ctypes.POINTER(ConvDesc)] + [vp] * 6 + [vp]
+    L.ssd_conv1d_step.restype = i32
+    L.ssd_conv1d_step.argtypes = [ctypes.POINTER(ConvDesc)] + [vp] * 5 + [vp]
     L.ssd_status_string.restype = ctypes.c_char_p
     L.ssd_status_string.argtypes = [i32]
     L.ssd_abi_version.restype = i32
@@ -227,6 +238,62 @@ def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torc
                       _ptr(A), _ptr(B_t), _ptr(C_t), _ptr(D), _ptr(y_t), _stream(state.device))
     if st != SSD_OK:
         raise SSDError(st, "ssd_step")
+    return y_t
+
+
+def ssd_conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+               state: Optional[torch.Tensor] = None, silu: bool = True,
+               y: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+               return_state: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Depthwise causal convolution over a sequence on the current stream.
+
+    x [Bt,T,D] float32 or bfloat16; weight [D,k] float32 (weight[:, k-1]
+    multiplies the current input); bias [D] float32 or None; state
+    [Bt,D,k-1] in x's dtype (the k-1 inputs before x[:, 0], oldest first) or
+    None for zeros.  Returns (y [Bt,T,D] in x's dtype, the outgoing window
+    [Bt,D,k-1] or None when return_state is False).  state_out may be
+    `state` itself (updated in place)."""
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[2]:
+        raise ValueError("x [Bt,T,D], weight [D,k]")
+    Bt, T, Dc = x.shape
+    K = weight.shape[1]
+    for t, n, dt_ in ((x, "x", None), (weight, "weight", torch.float32),
+                      (bias, "bias", torch.float32), (state, "state", x.dtype)):
+        _check(t, n, dt_)
+    if y is None:
+        y = torch.empty_like(x)
+    if state_out is None and return_state:
+        state_out = torch.empty(Bt, Dc, K - 1, dtype=x.dtype, device=x.device)
+    _check(y, "y", x.dtype)
+    _check(state_out, "state_out", x.dtype)
+    desc = ConvDesc(Bt, T, Dc, K, _io_code(x.dtype), int(bool(silu)))
+    st = lib.ssd_conv1d(ctypes.byref(desc), _ptr(x), _ptr(weight), _ptr(bias), _ptr(state),
+                        _ptr(y), _ptr(state_out), _stream(x.device))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_conv1d")
+    return y, state_out
+
+
+def ssd_conv1d_step(state: torch.Tensor, x_t: torch.Tensor, weight: torch.Tensor,
+                    bias: Optional[torch.Tensor] = None, *, silu: bool = True,
+                    y_t: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token of the convolution on the current stream; the window `state`
+    [Bt,D,k-1] (x_t's dtype) is updated in place.  x_t [Bt,D].  Returns y_t."""
+    if state.dim() != 3 or x_t.dim() != 2 or weight.dim() != 2:
+        raise ValueError("state [Bt,D,k-1], x_t [Bt,D], weight [D,k]")
+    Bt, Dc = x_t.shape
+    K = weight.shape[1]
+    for t, n, dt_ in ((state, "state", x_t.dtype), (x_t, "x_t", None),
+                      (weight, "weight", torch.float32), (bias, "bias", torch.float32)):
+        _check(t, n, dt_)
+    if y_t is None:
+        y_t = torch.empty_like(x_t)
+    _check(y_t, "y_t", x_t.dtype)
+    desc = ConvDesc(Bt, 1, Dc, K, _io_code(x_t.dtype), int(bool(silu)))
+    st = lib.ssd_conv1d_step(ctypes.byref(desc), _ptr(state), _ptr(x_t), _ptr(weight),
+                             _ptr(bias), _ptr(y_t), _stream(x_t.device))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_conv1d_step")
     return y_t
 
 

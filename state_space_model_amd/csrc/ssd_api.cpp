@@ -189,6 +189,39 @@ bool scan_uses_chain(int64_t batch, int64_t nheads, int64_t P, int64_t N, int64_
 }
 }  // namespace ssd
 
+namespace {
+
+struct ConvSizes {
+  int64_t n_x = 0, n_state = 0, n_w = 0, es = 4;
+};
+
+ssd_status check_conv_desc(const ssd_conv_desc* d, bool step, ConvSizes* s) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_DTYPE;
+  const int64_t T = step ? 1 : d->seqlen;
+  if (d->batch < 0 || T < 0 || d->channels <= 0 || d->width <= 0) return SSD_ERR_SHAPE;
+  if (!ssd::conv_width_supported(d->width)) return SSD_ERR_UNSUPPORTED;
+  int64_t bt = 0, bd = 0;
+  if (!mul_ok(d->batch, T, &bt) || !mul_ok(bt, d->channels, &s->n_x) ||
+      !mul_ok(d->batch, d->channels, &bd) || !mul_ok(bd, d->width - 1, &s->n_state) ||
+      !mul_ok(d->channels, d->width, &s->n_w))
+    return SSD_ERR_UNSUPPORTED;
+  // one thread per (batch row, channel, token) at most: the grid must fit
+  if (s->n_x > (int64_t)INT32_MAX * 64 || bd > (int64_t)INT32_MAX * 64) return SSD_ERR_UNSUPPORTED;
+  s->es = (int64_t)io_size(d->io_dtype);
+  return SSD_OK;
+}
+
+ssd::ConvArgs conv_args(const ssd_conv_desc* d, int64_t T) {
+  ssd::ConvArgs a;
+  a.Bt = d->batch; a.T = T; a.D = d->channels;
+  a.K = (int32_t)d->width;
+  a.silu = d->silu ? 1 : 0;
+  return a;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc) {
@@ -267,6 +300,59 @@ ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x_t, const
   a.dt_min = d->dt_min; a.dt_max = d->dt_max;
   hipError_t e = d->io_dtype == SSD_BF16 ? ssd::launch_step_bf16(a, stream)
                                          : ssd::launch_step_f32(a, stream);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_conv1d(const ssd_conv_desc* d, const void* x, const float* w, const float* bias,
+                      const void* state_in, void* y, void* state_out, hipStream_t stream) {
+  ConvSizes s;
+  const ssd_status st = check_conv_desc(d, false, &s);
+  if (st != SSD_OK) return st;
+  if (d->batch == 0 || (d->seqlen == 0 && !state_out)) return SSD_OK;
+  if (!w || (d->seqlen > 0 && (!x || !y))) return SSD_ERR_INVALID_ARG;
+  const void* vec[] = {x, y, state_in, state_out};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return SSD_ERR_ALIGNMENT;
+  if (!aligned4(w) || (bias && !aligned4(bias))) return SSD_ERR_ALIGNMENT;
+  const Range r_x = range_of(x, s.n_x * s.es), r_y = range_of(y, s.n_x * s.es);
+  const Range r_w = range_of(w, s.n_w * 4), r_b = range_of(bias, d->channels * 4);
+  const Range r_si = range_of(state_in, s.n_state * s.es);
+  const Range r_so = range_of(state_out, s.n_state * s.es);
+  const Range for_y[] = {r_x, r_w, r_b, r_si, r_so};
+  for (const Range& r : for_y)
+    if (overlap(r_y, r)) return SSD_ERR_INVALID_ARG;
+  const Range for_so[] = {r_x, r_w, r_b};
+  for (const Range& r : for_so)
+    if (overlap(r_so, r)) return SSD_ERR_INVALID_ARG;
+  if (state_out != state_in && overlap(r_so, r_si)) return SSD_ERR_INVALID_ARG;
+
+  ssd::ConvArgs a = conv_args(d, d->seqlen);
+  a.x = x; a.w = w; a.bias = bias; a.state_in = state_in; a.y = y; a.state_out = state_out;
+  const hipError_t e = ssd::launch_conv(a, d->io_dtype == SSD_BF16, false, stream);
+  return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_conv1d_step(const ssd_conv_desc* d, void* state, const void* x_t, const float* w,
+                           const float* bias, void* y_t, hipStream_t stream) {
+  ConvSizes s;
+  const ssd_status st = check_conv_desc(d, true, &s);
+  if (st != SSD_OK) return st;
+  if (d->batch == 0) return SSD_OK;
+  if (!state || !x_t || !w || !y_t) return SSD_ERR_INVALID_ARG;
+  const void* vec[] = {state, x_t, y_t};
+  for (const void* p : vec)
+    if (!aligned16(p)) return SSD_ERR_ALIGNMENT;
+  if (!aligned4(w) || (bias && !aligned4(bias))) return SSD_ERR_ALIGNMENT;
+  const Range r_s = range_of(state, s.n_state * s.es), r_y = range_of(y_t, s.n_x * s.es);
+  const Range inputs[] = {range_of(x_t, s.n_x * s.es), range_of(w, s.n_w * 4),
+                          range_of(bias, d->channels * 4)};
+  for (const Range& r : inputs)
+    if (overlap(r_y, r) || overlap(r_s, r)) return SSD_ERR_INVALID_ARG;
+  if (overlap(r_y, r_s)) return SSD_ERR_INVALID_ARG;
+
+  ssd::ConvArgs a = conv_args(d, 1);
+  a.x = x_t; a.w = w; a.bias = bias; a.state_in = state; a.y = y_t; a.state_out = state;
+  const hipError_t e = ssd::launch_conv(a, d->io_dtype == SSD_BF16, true, stream);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 

@@ -45,6 +45,18 @@ struct StepArgs {
   float dt_min, dt_max;
 };
 
+struct ConvArgs {
+  const void* x;          // [Bt,T,D] io (the step: x_t [Bt,D])
+  const float* w;         // [D,K]
+  const float* bias;      // [D] or null
+  const void* state_in;   // [Bt,D,K-1] io or null (the step: the in/out window)
+  void* y;                // [Bt,T,D] io (the step: y_t [Bt,D])
+  void* state_out;        // [Bt,D,K-1] io or null (the step: the in/out window)
+  int64_t Bt, T, D;
+  int32_t K;
+  int32_t silu;
+};
+
 // Compiled shape variants.
 bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16);
 
@@ -72,6 +84,11 @@ hipError_t launch_state_pass(const ScanArgs& a, int P, int N, hipStream_t stream
 
 hipError_t launch_step_f32(const StepArgs& a, hipStream_t stream);
 hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
+
+// Depthwise causal convolution: the sequence kernel (step == false) or the
+// one-token kernel (step == true, window in state_out, updated in place).
+bool conv_width_supported(int64_t K);
+hipError_t launch_conv(const ConvArgs& a, bool io_bf16, bool step, hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < n (float4 granularity; n % 4 == 0).
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);

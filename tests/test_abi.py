@@ -12,7 +12,7 @@ import re
 import pytest
 
 import state_space_model_amd as ssd
-from state_space_model_amd import ScanDesc, StepDesc, lib
+from state_space_model_amd import ConvDesc, ScanDesc, StepDesc, lib
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
                       "ssd.h")
@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert ssd.abi_version() == 2
+    assert ssd.abi_version() == 3
     for code in range(8):
         s = lib.ssd_status_string(code).decode()
         assert s.startswith(ssd.STATUS_NAMES[code])
@@ -218,6 +218,65 @@ def test_step_errors():
     assert step_status(step_desc(), y=BASE) == INVALID          # y over the state
     assert step_status(step_desc(), x=BASE + 64) == INVALID     # x inside the state
     assert step_status(step_desc(batch=0)) == OK                # nothing to do
+
+
+def conv_desc(**kw):
+    d = dict(batch=2, seqlen=64, channels=40, width=4, io_dtype=0, silu=1)
+    d.update(kw)
+    return ConvDesc(**d)
+
+
+def conv_status(d, **over):
+    ptr = dict(x=BASE, w=BASE + (1 << 24), bias=BASE + (2 << 24), si=BASE + (3 << 24),
+               y=BASE + (4 << 24), so=BASE + (5 << 24))
+    ptr.update(over)
+    P = ctypes.c_void_p
+    return lib.ssd_conv1d(ctypes.byref(d), P(ptr["x"]), P(ptr["w"]), P(ptr["bias"]),
+                          P(ptr["si"]), P(ptr["y"]), P(ptr["so"]), P(0))
+
+
+def conv_step_status(d, **over):
+    ptr = dict(state=BASE, x=BASE + (1 << 24), w=BASE + (2 << 24), bias=BASE + (3 << 24),
+               y=BASE + (4 << 24))
+    ptr.update(over)
+    P = ctypes.c_void_p
+    return lib.ssd_conv1d_step(ctypes.byref(d), P(ptr["state"]), P(ptr["x"]), P(ptr["w"]),
+                               P(ptr["bias"]), P(ptr["y"]), P(0))
+
+
+def test_conv_errors():
+    assert lib.ssd_conv1d(None, *([None] * 7)) == INVALID
+    assert conv_status(conv_desc(io_dtype=2)) == DTYPE
+    assert conv_status(conv_desc(channels=0)) == SHAPE
+    assert conv_status(conv_desc(seqlen=-1)) == SHAPE
+    assert conv_status(conv_desc(width=0)) == SHAPE
+    assert conv_status(conv_desc(width=1)) == UNSUP
+    assert conv_status(conv_desc(width=5)) == UNSUP
+    assert conv_status(conv_desc(), w=0) == INVALID
+    assert conv_status(conv_desc(), x=0) == INVALID
+    assert conv_status(conv_desc(), y=0) == INVALID
+    assert conv_status(conv_desc(), x=BASE + 4) == ALIGN
+    assert conv_status(conv_desc(), so=BASE + (5 << 24) + 8) == ALIGN
+    assert conv_status(conv_desc(), w=BASE + (1 << 24) + 2) == ALIGN
+    assert conv_status(conv_desc(), y=BASE + 1024) == INVALID       # y inside x
+    assert conv_status(conv_desc(), so=BASE + (1 << 24)) == INVALID  # window over the weights
+    assert conv_status(conv_desc(), so=BASE + (3 << 24) + 16) == INVALID  # partly over state_in
+    assert conv_status(conv_desc(), so=BASE + (4 << 24)) == INVALID  # window over y
+    # nothing to do: no launch
+    assert conv_status(conv_desc(batch=0)) == OK
+    assert conv_status(conv_desc(seqlen=0), so=0) == OK
+
+
+def test_conv_step_errors():
+    d = conv_desc(seqlen=123456)   # the step does not read seqlen
+    assert lib.ssd_conv1d_step(None, *([None] * 6)) == INVALID
+    assert conv_step_status(conv_desc(io_dtype=7)) == DTYPE
+    assert conv_step_status(conv_desc(width=6)) == UNSUP
+    assert conv_step_status(d, state=0) == INVALID
+    assert conv_step_status(d, bias=BASE + (3 << 24) + 1) == ALIGN
+    assert conv_step_status(d, y=BASE + 16) == INVALID            # y over the window
+    assert conv_step_status(d, x=BASE + 32) == INVALID            # x inside the window
+    assert conv_step_status(conv_desc(batch=0)) == OK
 
 
 def test_binding_refuses_cpu_tensors():
