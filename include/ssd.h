@@ -238,8 +238,9 @@ typedef struct {
  * (each part seeded with the previous part's state_out) or run token by
  * token gives bitwise the same outputs.  The window is kept in io_dtype: it
  * holds past inputs, which that type represents exactly.  Supported: k in
- * {2, 3, 4}; any D (D a multiple of 8 for bfloat16 or of 4 for float32 takes
- * the 16-byte vector path).  y may not overlap any input or state.
+ * {2, 3, 4}; any D (a multiple of 4 takes the vector path, 4 channels per
+ * lane); batch <= 65535 and T <= 2097120 (grid limits).
+ * y may not overlap any input or state.
  */
 ssd_status ssd_conv1d(const ssd_conv_desc* desc, const void* x, const float* w,
                       const float* bias, const void* state_in, void* y, void* state_out,

@@ -206,8 +206,7 @@ ssd_status check_conv_desc(const ssd_conv_desc* d, bool step, ConvSizes* s) {
       !mul_ok(d->batch, d->channels, &bd) || !mul_ok(bd, d->width - 1, &s->n_state) ||
       !mul_ok(d->channels, d->width, &s->n_w))
     return SSD_ERR_UNSUPPORTED;
-  // one thread per (batch row, channel, token) at most: the grid must fit
-  if (s->n_x > (int64_t)INT32_MAX * 64 || bd > (int64_t)INT32_MAX * 64) return SSD_ERR_UNSUPPORTED;
+  if (!ssd::conv_shape_supported(d->batch, T, d->channels)) return SSD_ERR_UNSUPPORTED;
   s->es = (int64_t)io_size(d->io_dtype);
   return SSD_OK;
 }

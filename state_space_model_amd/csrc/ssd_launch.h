@@ -88,6 +88,7 @@ hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
 // Depthwise causal convolution: the sequence kernel (step == false) or the
 // one-token kernel (step == true, window in state_out, updated in place).
 bool conv_width_supported(int64_t K);
+bool conv_shape_supported(int64_t Bt, int64_t T, int64_t D);
 hipError_t launch_conv(const ConvArgs& a, bool io_bf16, bool step, hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < n (float4 granularity; n % 4 == 0).
