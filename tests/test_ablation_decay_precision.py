@@ -1,0 +1,112 @@
+"""Ablation of decay precision, on the CPU.
+
+Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
+Caching", Implementation, precision management: decay parameters are kept in
+float32 and exponentiated at compute time; exponentiating the decay in
+bfloat16 alone shifts the model's outputs measurably (the pages' Table 8).
+
+Kernel analogue: the GPU kernels form every decay factor in float32.  These
+tests evaluate the chunked algorithm with the decay factors rounded to
+bfloat16 and to float32 and compare both with the fp64 oracle on the
+130M-shaped value distributions.  Within one chunk of 256 tokens, bfloat16
+decay costs 7.8e-5 in y (float32: 1.5e-9); over 4096 tokens in 16 chunks the
+rounded chunk decays compound through the state to 1.8e-3, 18 times the
+float32 bar of 1e-4 (float32 decay: 1.7e-8).  This is why the kernels never
+round a decay factor, only matrix operands of bfloat16 inputs.
+"""
+import numpy as np
+import torch
+
+import oracle
+from oracle.metrics import state_err, y_err
+from ssd_inputs import as_f32_numpy, make_inputs, make_tiny
+
+
+def chunked_rounded_decay(inp, L, round_to):
+    """y and final state of the chunked algorithm (Background, Eq. 3 within a
+    chunk, the recurrence h_c = alpha_c h_{c-1} + S_c across chunks) with
+    every decay factor -- exp(cum_i - cum_j) inside a chunk, exp(cum_i) on
+    the entering state, exp(cum_last - cum_l) in the chunk state and
+    alpha_c = exp(cum_last) -- rounded to `round_to` (a torch dtype);
+    everything else in float64."""
+    def r(v):
+        return torch.from_numpy(np.asarray(v, np.float64)).to(round_to).to(torch.float64).numpy()
+    x = inp["x"].astype(np.float64)
+    Bt, T, H, P = x.shape
+    N = inp["B"].shape[3]
+    y = np.zeros_like(x)
+    fin = np.zeros((Bt, H, P, N))
+    for b in range(Bt):
+        for h in range(H):
+            z = inp["dt"][b, :, h].astype(np.float64) + float(inp["dt_bias"][h])
+            d = np.clip(np.maximum(z, 0) + np.log1p(np.exp(-np.abs(z))),
+                        float(np.float32(1e-4)), float(np.float32(0.5)))
+            a = d * float(inp["A"][h])
+            hs = np.zeros((P, N))
+            for c0 in range(0, T, L):
+                sl = slice(c0, min(c0 + L, T))
+                cum = np.cumsum(a[sl])
+                n = len(cum)
+                mask = np.tril(np.ones((n, n), bool))
+                dec = np.where(mask, r(np.exp(np.where(mask, cum[:, None] - cum[None, :], 0.0))), 0.0)
+                Bg = inp["B"][b, sl, 0].astype(np.float64)
+                Cg = inp["C"][b, sl, 0].astype(np.float64)
+                X = x[b, sl, h]
+                yy = ((Cg @ Bg.T) * dec * d[sl][None, :]) @ X
+                yy += r(np.exp(cum))[:, None] * (Cg @ hs.T)
+                y[b, sl, h] = yy + float(inp["D"][h]) * X
+                wl = r(np.exp(cum[-1] - cum)) * d[sl]
+                hs = float(r(np.exp(cum[-1]))) * hs + (X * wl[:, None]).T @ Bg
+            fin[b, h] = hs
+    return y, fin
+
+
+def test_bf16_decay_error_compounds_across_chunks():
+    """4096 tokens of the 130M-shaped distributions in 16 chunks of 256."""
+    w = make_tiny(1, 4096, 4, 64, 128, 1, 256, "f32", seed=4300)
+    inp = {k: as_f32_numpy(v) for k, v in make_inputs(w).items()}
+    y_ref, f_ref = oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                               inp["dt_bias"])
+    y32, f32 = chunked_rounded_decay(inp, 256, torch.float32)
+    y16, f16 = chunked_rounded_decay(inp, 256, torch.bfloat16)
+    e32 = max(y_err(y32, y_ref), state_err(f32, f_ref))
+    e16 = max(y_err(y16, y_ref), state_err(f16, f_ref))
+    print(f"4096 tokens: error vs oracle with fp32 decay {e32:.2e}, bf16 decay {e16:.2e}")
+    assert e32 <= 1e-6
+    assert e16 > 1e-4      # over the float32 bar
+
+
+def dual_form_rounded_decay(inp, round_to):
+    """y of one (b, h) sequence per head from the dual form, with each decay
+    factor exp(sum of A*Delta over j+1..i) rounded to `round_to` (a torch
+    dtype) before it multiplies the scores; everything else in float64."""
+    x = inp["x"].astype(np.float64)
+    Bt, T, H, P = x.shape
+    y = np.zeros_like(x)
+    for b in range(Bt):
+        for h in range(H):
+            z = inp["dt"][b, :, h].astype(np.float64) + float(inp["dt_bias"][h])
+            d = np.clip(np.maximum(z, 0) + np.log1p(np.exp(-np.abs(z))),
+                        float(np.float32(1e-4)), float(np.float32(0.5)))
+            cum = np.cumsum(d * float(inp["A"][h]))
+            seg = cum[:, None] - cum[None, :]
+            mask = np.tril(np.ones((T, T), bool))
+            decay = np.where(mask, np.exp(np.where(mask, seg, 0.0)), 0.0)
+            decay = torch.from_numpy(decay).to(round_to).to(torch.float64).numpy()
+            Bg = inp["B"][b, :, 0].astype(np.float64)
+            Cg = inp["C"][b, :, 0].astype(np.float64)
+            M = (Cg @ Bg.T) * decay * d[None, :]
+            y[b, :, h] = M @ x[b, :, h] + float(inp["D"][h]) * x[b, :, h]
+    return y
+
+
+def test_bf16_decay_within_one_chunk():
+    w = make_tiny(1, 256, 4, 64, 128, 1, 256, "f32", seed=4300)
+    inp = {k: as_f32_numpy(v) for k, v in make_inputs(w).items()}
+    y_ref, _ = oracle.scan(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                           inp["dt_bias"])
+    e32 = y_err(dual_form_rounded_decay(inp, torch.float32), y_ref)
+    e16 = y_err(dual_form_rounded_decay(inp, torch.bfloat16), y_ref)
+    print(f"one chunk: y error vs oracle with fp32 decay {e32:.2e}, bf16 decay {e16:.2e}")
+    assert e32 <= 1e-6
+    assert e16 > 100 * e32

@@ -165,6 +165,66 @@ def test_chain_and_phased_schedules_agree_bitwise():
         assert torch.equal(ya, y1[b:b + 1]) and torch.equal(fa, f1[b:b + 1]), b
 
 
+@pytest.mark.parametrize("case", [
+    # (Bt, T, H, G, io): groups of 8 heads sharing B/C, at layer scale
+    (1, 4096, 64, 8, "f32"),
+    (1, 4096, 64, 8, "bf16"),
+    (4, 1024, 64, 8, "bf16"),     # batch x heads = 256: the chain schedule
+], ids=lambda c: "_".join(map(str, c)))
+def test_scan_groups_at_scale(case):
+    """G > 1 at layer scale (8 B/C groups of 8 heads, P = 64, N = 128,
+    L = 256) against the oracle in full."""
+    need_gpu()
+    Bt, T, H, G, io = case
+    w = make_tiny(Bt, T, H, 64, 128, G, 256, io, seed=4100 + T + Bt)
+    inp = make_inputs(w, with_initial_state=True)
+    import state_space_model_amd as ssd
+    sched = ssd.ssd_chunk_scan_schedule(inp["x"], inp["B"], 256)
+    assert sched == (ssd.SSD_SCHEDULE_CHAIN if Bt * H >= 256 and io == "bf16"
+                     else ssd.SSD_SCHEDULE_PHASED)
+    announce(f"scan groups at scale {case} schedule {sched}")
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    ey, ef = y_err(y, y_ref), state_err(fin, f_ref)
+    print(f"groups {case}: y err {ey:.3e}  final-state err {ef:.3e}")
+    assert ey <= TOL[io] and ef <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_scan_chunked_prefill_chain(io):
+    """Chunked prefill ([SSD] O(1) cache: the prefill's final state seeds what
+    follows): the 4096-token sequence run as pieces of 1000, 1, 1000, 2047 and
+    48 tokens (chunk boundaries not aligned with the pieces), each seeded with
+    the previous piece's final state, against the oracle over the whole
+    sequence, and against the one-shot GPU scan."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = make_tiny(2, 4096, 24, 64, 128, 1, 256, io, seed=4200)
+    inp = make_inputs(w, with_initial_state=True)
+    d = to_dev(inp)
+    announce(f"scan chunked prefill chain {io}")
+    y_one, f_one = run_gpu(inp, w)
+    state = d["h0"]
+    ys = []
+    lo = 0
+    for n in (1000, 1, 1000, 2047, 48):
+        sl = {k: (v[:, lo:lo + n].contiguous() if k in ("x", "dt", "B", "C") else v)
+              for k, v in d.items()}
+        y, state = ssd.ssd_chunk_scan(sl["x"], sl["dt"], sl["A"], sl["B"], sl["C"], sl["D"],
+                                      chunk=w.chunk, dt_bias=sl["dt_bias"], initial_state=state)
+        ys.append(y)
+        lo += n
+    assert lo == 4096
+    torch.cuda.synchronize()
+    y_chain = torch.cat(ys, 1)
+    y_ref, f_ref = oracle_scan(inp, w)
+    ey, ef = y_err(y_chain, y_ref), state_err(state, f_ref)
+    print(f"chain {io}: y err {ey:.3e}  final-state err {ef:.3e}")
+    assert ey <= TOL[io] and ef <= TOL[io]
+    assert y_err(y_chain, y_one.double().cpu().numpy()) <= TOL[io]
+    assert state_err(state, f_one.double().cpu().numpy()) <= TOL[io]
+
+
 def test_scan_options_off():
     """No D, no dt_bias, softplus off, no initial state, no final state requested."""
     need_gpu()
