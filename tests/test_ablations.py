@@ -1,4 +1,4 @@
-"""Ablation of decay precision, on the CPU.
+"""Ablations of decay precision and mask placement, on the CPU.
 
 Source: "Compiler-First State Space Duality and Portable O(1) Autoregressive
 Caching", Implementation, precision management: decay parameters are kept in
@@ -110,3 +110,31 @@ def test_bf16_decay_within_one_chunk():
     print(f"one chunk: y error vs oracle with fp32 decay {e32:.2e}, bf16 decay {e16:.2e}")
     assert e32 <= 1e-6
     assert e16 > 100 * e32
+
+
+def test_mask_must_be_a_select_before_the_exponential():
+    """Implementation, static masking: the prefix sum, subtraction, mask and
+    exponentiation are fused.  The order matters: above the diagonal the
+    segment sum cum_i - cum_j is positive and, over a 256-token chunk of the
+    130M-shaped distributions (Delta up to 0.5, |A| up to 16), exceeds the
+    float32 exponent range, so a multiplicative mask applied after exp turns
+    0 * inf into NaN.  The kernels select before exponentiating."""
+    w = make_tiny(1, 256, 4, 64, 128, 1, 256, "f32", seed=4301)
+    inp = {k: as_f32_numpy(v) for k, v in make_inputs(w).items()}
+    worst_seg, nan_mult, nan_select = 0.0, 0, 0
+    for h in range(4):
+        z = inp["dt"][0, :, h] + inp["dt_bias"][h]
+        d = np.clip(np.logaddexp(np.float32(0), z), np.float32(1e-4), np.float32(0.5)).astype(np.float32)
+        cum = np.cumsum(d * inp["A"][h], dtype=np.float32)
+        seg = (cum[:, None] - cum[None, :]).astype(np.float32)
+        mask = np.tril(np.ones((256, 256), bool))
+        with np.errstate(over="ignore", invalid="ignore"):
+            mult = mask.astype(np.float32) * np.exp(seg)
+        sel = np.exp(np.where(mask, seg, np.float32(0))) * mask
+        worst_seg = max(worst_seg, float(seg.max()))
+        nan_mult += int(np.isnan(mult).sum())
+        nan_select += int(np.isnan(sel).sum())
+    print(f"largest upper-triangle segment sum {worst_seg:.1f}; NaN entries: "
+          f"mask after exp {nan_mult}, select before exp {nan_select}")
+    assert worst_seg > 88.8          # past log(float32 max)
+    assert nan_mult > 0 and nan_select == 0
