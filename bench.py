@@ -51,12 +51,16 @@ KERNEL_SOURCES = {
     "chunk_out/f32": ["ssd_prefill_f32.hip", "ssd_prefill_common.h", "ssd_device.h"],
     "chunk_out/bf16": ["ssd_prefill_bf16.hip", "ssd_prefill_common.h", "ssd_device.h"],
     "decode": ["ssd_step.hip", "ssd_device.h"],
+    "conv1d": ["ssd_conv.hip", "ssd_device.h"],
 }
 # HBM bytes per launch from the counter runs: (kernel key, workload) -> (bytes, digest)
 TRAFFIC = {
     # counter runs and calibration: profiles/chunk_out_f32_m130_f32_decode_m2p7_b64_hbm_bytes.txt
-    ("chunk_out/f32", "m130_f32"): (41.17e6 + 30.55e6, "461d061fb242ece3"),
-    ("decode", "m2p7_decode_b64"): (169.12e6 + 168.48e6, "a9cd5d42c984beb1"),
+    ("chunk_out/f32", "m130_f32"): (41.13e6 + 30.56e6, "d8501d574f6938aa"),
+    ("decode", "m2p7_decode_b64"): (169.12e6 + 168.47e6, "a9cd5d42c984beb1"),
+    # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
+    ("conv1d", "conv_m2p7_bf16"): (49.19e6 + 44.07e6, "9c6f061da92854fb"),
+    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "9c6f061da92854fb"),
 }
 COPY_CALIBRATION_BYTES = 1 << 30
 
@@ -332,7 +336,8 @@ def bench_conv(ssd, torch, warmup, reps=20, steps_n=256):
                       "tokens_per_s": Bt * T / (ms * 1e-3), "bytes_per_launch": nbytes,
                       "rotated_sets": nsets,
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                   "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+                                   "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                   "traffic": traffic_for("conv1d", w.name)}}
     wd = CONV_WORKLOADS["conv_m2p7_decode"]
     inp = make_conv_inputs(wd.with_(seqlen=steps_n), with_state=True)
     dd = {k: v.cuda() for k, v in inp.items()}
@@ -372,7 +377,8 @@ def bench_conv(ssd, torch, warmup, reps=20, steps_n=256):
                    "us_per_step": ms_step * 1e3, "tokens_per_s": Bt / (ms_step * 1e-3),
                    "bytes_per_step": sbytes, "windows": nwin,
                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS,
-                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}}
+                                "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                                "traffic": traffic_for("conv1d", f"{wd.name}_b{Bt}")}}
     return out
 
 
