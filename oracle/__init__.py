@@ -10,6 +10,8 @@ Contents
   conv1d(...)       depthwise causal convolution over time with its k-1 input
                     window carried in and out (C, fp64)
   conv1d_step(...)  the same convolution for one token from a cached window
+  scan_backward(...) gradients of the scan: the adjoint recurrence run
+                    backwards in time from checkpointed states (C, fp64)
   dual_form.py      dense quadratic "dual form" materialisation (numpy, fp64)
   chunked.py        chunked SSD algorithm written step by step (numpy, fp64)
   brute.py          the recurrence at 50 significant digits (mpmath)
@@ -45,6 +47,9 @@ def _load():
                                                            ctypes.c_double, vp, vp, ctypes.c_int]
         lib.ssd_oracle_conv1d.restype = ctypes.c_int
         lib.ssd_oracle_conv1d.argtypes = [i64] * 4 + [vp] * 4 + [ctypes.c_int, vp, vp, ctypes.c_int]
+        lib.ssd_oracle_scan_backward.restype = ctypes.c_int
+        lib.ssd_oracle_scan_backward.argtypes = ([i64] * 6 + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
+                                                 ctypes.c_double] + [vp] * 10 + [ctypes.c_int])
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -152,3 +157,35 @@ def conv1d_step(state, x_t, w, bias=None, *, silu: bool = False
     x_t = _f32(x_t)
     y, st = conv1d(x_t[:, None], w, bias, state, silu=silu)
     return y[:, 0], st
+
+
+def scan_backward(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, dy, dfinal=None,
+                  dt_softplus: bool = True, dt_min: float = 1e-4, dt_max: float = 0.5,
+                  nthreads: int = 0) -> dict:
+    """Gradients of L = sum(dy * y) + sum(dfinal * final_state) of scan(...)
+    with respect to every input, by the adjoint recurrence in fp64.
+
+    dy [Bt,T,H,P] and dfinal [Bt,H,P,N] (None: zeros) are taken in float64.
+    Returns a dict of float64 arrays: dx, ddt (w.r.t. the pre-activation dt),
+    dA, dB, dC, dD, ddt_bias, dh0 (shapes of the inputs; dD, ddt_bias and dA
+    are [H], computed also when D or dt_bias is None)."""
+    x, dt, A, B, C = _f32(x), _f32(dt), _f32(A), _f32(B), _f32(C)
+    D, dt_bias, h0 = _f32(D), _f32(dt_bias), _f64(h0)
+    dy, dfinal = _f64(dy), _f64(dfinal)
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == (Bt, T, H, P)
+    assert dfinal is None or dfinal.shape == (Bt, H, P, N)
+    out = {"dx": np.empty((Bt, T, H, P)), "ddt": np.empty((Bt, T, H)), "dA": np.empty(H),
+           "dB": np.empty((Bt, T, G, N)), "dC": np.empty((Bt, T, G, N)), "dD": np.empty(H),
+           "ddt_bias": np.empty(H), "dh0": np.empty((Bt, H, P, N))}
+    lo = float(np.float32(dt_min))
+    hi = float(np.float32(dt_max))
+    rc = _load().ssd_oracle_scan_backward(
+        Bt, T, H, P, N, G, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(h0), int(bool(dt_softplus)), lo, hi, _ptr(dy), _ptr(dfinal), _ptr(out["dx"]),
+        _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+        _ptr(out["ddt_bias"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_scan_backward failed with code {rc}")
+    return out

@@ -176,3 +176,205 @@ int ssd_oracle_conv1d(int64_t Bt, int64_t T, int64_t D, int64_t K, const float* 
   }
   return failed ? 2 : 0;
 }
+
+/*
+ * Gradients of the scan (the backward pass of a training step; Results and
+ * Setup of "Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching" time the forward only, the training step is the
+ * pages' stated next use).  For the loss L = sum(dy * y) + sum(dfinal * final)
+ * the adjoint of the recurrence above runs backwards in time with
+ * G_t = dL/dh_t:
+ *
+ *   G_{T-1} = dfinal;   for t = T-1 .. 0:
+ *     G      += dy_t (x) C_t                         (G = dL/dh_t)
+ *     dC_t[n] += sum_p dy_t[p] h_t[p,n]              (summed over a group's heads)
+ *     dx_t[p]  = d_t sum_n G[p,n] B_t[n] + D dy_t[p]
+ *     dB_t[n] += d_t sum_p G[p,n] x_t[p]             (summed over a group's heads)
+ *     dd_t     = sum_{p,n} G[p,n] x_t[p] B_t[n] + A abar_t sum_{p,n} G[p,n] h_{t-1}[p,n]
+ *     dA      += d_t abar_t sum_{p,n} G[p,n] h_{t-1}[p,n]
+ *     dD      += sum_p dy_t[p] x_t[p]
+ *     G       *= abar_t                              (G = dL/dh_{t-1})
+ *   dh0 = G;  ddt_t = dd_t * softplus'(z_t) where lo <= softplus(z_t) <= hi, else 0
+ *   (softplus'(z) = 1 / (1 + exp(-z)); without softplus, 1); ddt_bias = sum_t ddt_t.
+ *
+ * The states h_t are recomputed segment by segment (SEG tokens) from
+ * checkpoints taken on a forward pass, all in double.  Per-head partial dB and
+ * dC are summed over the heads of a group after the parallel loop.
+ * Returns 0 on success, 1 on a bad argument, 2 when scratch allocation fails.
+ */
+int ssd_oracle_scan_backward(int64_t Bt, int64_t T, int64_t H, int64_t P, int64_t N, int64_t G,
+                             const float* x, const float* dt, const float* dt_bias,
+                             const float* A, const float* Bm, const float* Cm, const float* D,
+                             const double* h0, int dt_softplus, double dt_min, double dt_max,
+                             const double* dy, const double* dfinal,
+                             double* dx, double* ddt, double* dA, double* dB, double* dC,
+                             double* dD, double* ddt_bias, double* dh0, int nthreads) {
+  enum { SEG = 64 };
+  if (Bt < 0 || T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return 1;
+  if (!A || !dA || !dD || !ddt_bias || !dh0) return 1;
+  if (T > 0 && (!x || !dt || !Bm || !Cm || !dy || !dx || !ddt || !dB || !dC)) return 1;
+  const int64_t hpg = H / G, npairs = Bt * H, PN = P * N;
+  const int64_t nseg = (T + SEG - 1) / SEG;
+  /* per-head partials of dB and dC: [Bt,T,H,N] */
+  double* dBh = (double*)calloc((size_t)(Bt * T * H * N) + 1, sizeof(double));
+  double* dCh = (double*)calloc((size_t)(Bt * T * H * N) + 1, sizeof(double));
+  double* dAh = (double*)calloc((size_t)(Bt * H) + 1, sizeof(double));
+  double* dDh = (double*)calloc((size_t)(Bt * H) + 1, sizeof(double));
+  double* dbh = (double*)calloc((size_t)(Bt * H) + 1, sizeof(double));
+  if (!dBh || !dCh || !dAh || !dDh || !dbh) {
+    free(dBh); free(dCh); free(dAh); free(dDh); free(dbh);
+    return 2;
+  }
+  int failed = 0;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel
+#endif
+  {
+    double* ck = (double*)malloc(sizeof(double) * (size_t)((nseg + 1) * PN));
+    double* hs = (double*)malloc(sizeof(double) * (size_t)((SEG + 1) * PN));
+    double* Gm = (double*)malloc(sizeof(double) * (size_t)PN);
+    double* dv = (double*)malloc(sizeof(double) * (size_t)(T + 1));
+    double* zv = (double*)malloc(sizeof(double) * (size_t)(T + 1));
+    if (!ck || !hs || !Gm || !dv || !zv) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    }
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 1)
+#endif
+    for (int64_t pair = 0; pair < npairs; ++pair) {
+      if (!ck || !hs || !Gm || !dv || !zv) continue;
+      const int64_t b = pair / H, h = pair % H, g = h / hpg;
+      const double Ah = (double)A[h];
+      const double Dh = D ? (double)D[h] : 0.0;
+      const double bias = dt_bias ? (double)dt_bias[h] : 0.0;
+      for (int64_t t = 0; t < T; ++t) {
+        const double z = (double)dt[(b * T + t) * H + h] + bias;
+        double d = dt_softplus ? softplus_exact(z) : z;
+        zv[t] = z;
+        if (d < dt_min) d = dt_min;
+        if (d > dt_max) d = dt_max;
+        dv[t] = d;
+      }
+      /* forward: checkpoint the state entering every segment */
+      double* hcur = ck;
+      if (h0)
+        memcpy(hcur, h0 + (size_t)((b * H + h) * PN), sizeof(double) * (size_t)PN);
+      else
+        memset(hcur, 0, sizeof(double) * (size_t)PN);
+      for (int64_t s = 0; s < nseg; ++s) {
+        double* hn = ck + (s + 1) * PN;
+        memcpy(hn, ck + s * PN, sizeof(double) * (size_t)PN);
+        for (int64_t t = s * SEG; t < T && t < (s + 1) * SEG; ++t) {
+          const double abar = exp(dv[t] * Ah);
+          const float* xt = x + (size_t)(((b * T + t) * H + h) * P);
+          const float* Bt_ = Bm + (size_t)(((b * T + t) * G + g) * N);
+          for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+              hn[p * N + n] = abar * hn[p * N + n] + dv[t] * (double)xt[p] * (double)Bt_[n];
+        }
+      }
+      /* reverse */
+      if (dfinal)
+        memcpy(Gm, dfinal + (size_t)((b * H + h) * PN), sizeof(double) * (size_t)PN);
+      else
+        memset(Gm, 0, sizeof(double) * (size_t)PN);
+      double dA_acc = 0.0, dD_acc = 0.0, db_acc = 0.0;
+      for (int64_t s = nseg - 1; s >= 0; --s) {
+        const int64_t t0 = s * SEG, t1 = (T < (s + 1) * SEG ? T : (s + 1) * SEG);
+        /* hs[k] = state after token t0 + k - 1 (hs[0] = entering state) */
+        memcpy(hs, ck + s * PN, sizeof(double) * (size_t)PN);
+        for (int64_t t = t0; t < t1; ++t) {
+          const double abar = exp(dv[t] * Ah);
+          const float* xt = x + (size_t)(((b * T + t) * H + h) * P);
+          const float* Bt_ = Bm + (size_t)(((b * T + t) * G + g) * N);
+          const double* hp = hs + (t - t0) * PN;
+          double* hn = hs + (t - t0 + 1) * PN;
+          for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n)
+              hn[p * N + n] = abar * hp[p * N + n] + dv[t] * (double)xt[p] * (double)Bt_[n];
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+          const double abar = exp(dv[t] * Ah);
+          const double d = dv[t];
+          const float* xt = x + (size_t)(((b * T + t) * H + h) * P);
+          const float* Bt_ = Bm + (size_t)(((b * T + t) * G + g) * N);
+          const float* Ct_ = Cm + (size_t)(((b * T + t) * G + g) * N);
+          const double* dyt = dy + (size_t)(((b * T + t) * H + h) * P);
+          const double* hprev = hs + (t - t0) * PN;
+          const double* hcur2 = hs + (t - t0 + 1) * PN;
+          double* dxt = dx + (size_t)(((b * T + t) * H + h) * P);
+          double* dBt = dBh + (size_t)(((b * T + t) * H + h) * N);
+          double* dCt = dCh + (size_t)(((b * T + t) * H + h) * N);
+          for (int64_t p = 0; p < P; ++p)
+            for (int64_t n = 0; n < N; ++n) Gm[p * N + n] += dyt[p] * (double)Ct_[n];
+          for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t p = 0; p < P; ++p) acc += dyt[p] * hcur2[p * N + n];
+            dCt[n] = acc;
+          }
+          double din = 0.0, dec = 0.0;
+          for (int64_t p = 0; p < P; ++p) {
+            double gb = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+              gb += Gm[p * N + n] * (double)Bt_[n];
+              dec += Gm[p * N + n] * hprev[p * N + n];
+            }
+            dxt[p] = d * gb + Dh * dyt[p];
+            din += gb * (double)xt[p];
+            dD_acc += dyt[p] * (double)xt[p];
+          }
+          for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t p = 0; p < P; ++p) acc += Gm[p * N + n] * (double)xt[p];
+            dBt[n] = d * acc;
+          }
+          const double dd = din + Ah * abar * dec;
+          dA_acc += d * abar * dec;
+          double pre = dt_softplus ? softplus_exact(zv[t]) : zv[t];
+          double gate = (pre >= dt_min && pre <= dt_max) ? 1.0 : 0.0;
+          if (dt_softplus) gate *= 1.0 / (1.0 + exp(-zv[t]));
+          const double g_dt = dd * gate;
+          ddt[(b * T + t) * H + h] = g_dt;
+          db_acc += g_dt;
+          for (int64_t k = 0; k < PN; ++k) Gm[k] *= abar;
+        }
+      }
+      memcpy(dh0 + (size_t)((b * H + h) * PN), Gm, sizeof(double) * (size_t)PN);
+      dAh[pair] = dA_acc;
+      dDh[pair] = dD_acc;
+      dbh[pair] = db_acc;
+    }
+    free(ck); free(hs); free(Gm); free(dv); free(zv);
+  }
+  if (!failed) {
+    for (int64_t h = 0; h < H; ++h) {
+      double a = 0.0, dd = 0.0, bb = 0.0;
+      for (int64_t b = 0; b < Bt; ++b) {
+        a += dAh[b * H + h];
+        dd += dDh[b * H + h];
+        bb += dbh[b * H + h];
+      }
+      dA[h] = a;
+      dD[h] = dd;
+      ddt_bias[h] = bb;
+    }
+    for (int64_t b = 0; b < Bt; ++b)
+      for (int64_t t = 0; t < T; ++t)
+        for (int64_t g = 0; g < G; ++g)
+          for (int64_t n = 0; n < N; ++n) {
+            double sb = 0.0, sc = 0.0;
+            for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
+              sb += dBh[((b * T + t) * H + h) * N + n];
+              sc += dCh[((b * T + t) * H + h) * N + n];
+            }
+            dB[((b * T + t) * G + g) * N + n] = sb;
+            dC[((b * T + t) * G + g) * N + n] = sc;
+          }
+  }
+  free(dBh); free(dCh); free(dAh); free(dDh); free(dbh);
+  return failed ? 2 : 0;
+}
