@@ -293,6 +293,57 @@ def bench_cached_vs_recompute(ssd, torch, context=4096, reps=20):
             "recompute_us": t_re, "cached_step_us": t_st, "speedup": t_re / t_st}
 
 
+def bench_backward(ssd, torch, w, reps=10):
+    """The scan's gradients (ssd_chunk_scan_backward) on the headline layer:
+    time per call and per token, against the forward scan of the same
+    inputs timed the same way (eager launches, inputs resident)."""
+    from ssd_inputs import make_inputs
+    inp = make_inputs(w, with_initial_state=True)
+    d = {k: v.cuda() for k, v in inp.items()}
+    g = torch.Generator(device="cpu").manual_seed(6500)
+    dy = torch.randn(d["x"].shape, generator=g).to(d["x"].dtype).cuda()
+    dfinal = torch.randn(d["h0"].shape, generator=g).cuda()
+    ws = torch.empty(ssd.ssd_chunk_scan_backward_workspace_bytes(d["x"], d["B"], w.chunk),
+                     dtype=torch.uint8, device="cuda")
+    fws = torch.empty(ssd.ssd_chunk_scan_workspace_bytes(d["x"], d["B"], w.chunk),
+                      dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(d["x"])
+    fin = torch.empty_like(d["h0"])
+    grads = ssd.ssd_chunk_scan_backward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], dy=dy,
+                                        dfinal_state=dfinal, chunk=w.chunk, dt_bias=d["dt_bias"],
+                                        initial_state=d["h0"], workspace=ws)
+
+    def bwd():
+        ssd.ssd_chunk_scan_backward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], dy=dy,
+                                    dfinal_state=dfinal, chunk=w.chunk, dt_bias=d["dt_bias"],
+                                    initial_state=d["h0"], workspace=ws, grads=grads)
+
+    def fwd():
+        ssd.ssd_chunk_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], chunk=w.chunk,
+                           dt_bias=d["dt_bias"], initial_state=d["h0"], y=y, final_state=fin,
+                           workspace=fws)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_b = timed(bwd)
+    ms_f = timed(fwd)
+    tokens = w.batch * w.seqlen
+    return {"workload": w.name, "ms": ms_b, "tokens_per_s": tokens / (ms_b * 1e-3),
+            "forward_ms_same_inputs": ms_f, "backward_over_forward": ms_b / ms_f,
+            "workspace_bytes": ws.numel(),
+            "note": "gradients of every input; recomputes the forward in float32"}
+
+
 def conv_bytes(Bt, T, D, K, es):
     """Algorithmic bytes of one conv1d call: x read and y written once, the
     window read and written once, weights and bias read once."""
@@ -488,6 +539,8 @@ def main():
         out["cached_vs_recompute"] = bench_cached_vs_recompute(ssd, torch)
         print("[bench] conv1d prefill and step", file=sys.stderr, flush=True)
         out["conv1d"] = bench_conv(ssd, torch, args.warmup)
+        print("[bench] backward", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(ssd, torch, w)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

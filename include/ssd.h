@@ -14,6 +14,9 @@
  *                   the depthwise causal convolution that precedes the scan
  *                   in a Mamba-2 block, over a sequence and for one token
  *                   from its cached window (O(1) cache section; Setup: k = 4).
+ *   ssd_chunk_scan_backward
+ *                   the gradients of ssd_chunk_scan with respect to all of
+ *                   its inputs (the backward pass of a training step).
  *
  * Both compute, for every batch row b and head h (g = h / (H/G) is the B/C
  * group of head h), the selective diagonal SSM
@@ -68,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
   SSD_OK = 0,
@@ -161,6 +164,47 @@ ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float*
                           const float* D, const float* initial_state, void* y,
                           float* final_state, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
+
+/*
+ * Gradients of ssd_chunk_scan (same descriptor and inputs) for the loss
+ * L = sum(dy * y) + sum(dfinal_state * final_state), with respect to every
+ * input: the backward pass of a training step over the recurrence of
+ * "Compiler-First State Space Duality and Portable O(1) Autoregressive
+ * Caching", Background, Eq. 2-3.
+ *
+ * The adjoint state G_t = dL/dh_t obeys the same recurrence backwards in
+ * time (G_t = dy_t (x) C_t + abar_{t+1} G_{t+1}), so the library computes the
+ * gradients with the scan's own kernels: the forward scan (recomputed), a
+ * scan over reversed time with B and C exchanged (dx, dt, dA, dh0), a scan
+ * with the roles of P and N exchanged (dC), a reversed one of that kind (dB),
+ * and element-wise and reduction kernels (no atomics: results are
+ * deterministic).
+ *
+ *   inputs as ssd_chunk_scan; dy [Bt,T,H,P] io_dtype;
+ *   dfinal_state [Bt,H,P,N] f32 or NULL (zero)
+ *   gradients, all float32 (written): dx [Bt,T,H,P]; ddt [Bt,T,H] with
+ *   respect to the pre-activation dt (zero where Delta is clipped); dA [H];
+ *   dB, dC [Bt,T,G,N]; dD [H] or NULL; ddt_bias [H] or NULL;
+ *   dinitial_state [Bt,H,P,N] or NULL (not returned)
+ *   workspace: at least ssd_chunk_scan_backward_workspace_bytes(desc)
+ *
+ * Shapes: those of ssd_chunk_scan whose exchanged form (headdim N, dstate P,
+ * one group per head) is also supported (N * L <= 32768; P >= 32 for
+ * bfloat16); other valid shapes return SSD_ERR_UNSUPPORTED.  With bfloat16
+ * io the internal operands (dy / Delta, replicated B and C) and the scans'
+ * outputs are rounded to bfloat16 as in the forward scan.  Gradients may not
+ * overlap any input, the workspace or each other.  batch == 0 writes zeros
+ * to dA, dD and ddt_bias; seqlen == 0 also copies dfinal_state (or zeros) to
+ * dinitial_state.
+ */
+size_t ssd_chunk_scan_backward_workspace_bytes(const ssd_scan_desc* desc);
+ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* desc, const void* x, const float* dt,
+                                   const float* dt_bias, const float* A, const void* B,
+                                   const void* C, const float* D, const float* initial_state,
+                                   const void* dy, const float* dfinal_state, float* dx,
+                                   float* ddt, float* dA, float* dB, float* dC, float* dD,
+                                   float* ddt_bias, float* dinitial_state, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * ssd_chunk_scan with timing instrumentation: when `phase_events` is not NULL

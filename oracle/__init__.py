@@ -49,7 +49,7 @@ def _load():
         lib.ssd_oracle_conv1d.argtypes = [i64] * 4 + [vp] * 4 + [ctypes.c_int, vp, vp, ctypes.c_int]
         lib.ssd_oracle_scan_backward.restype = ctypes.c_int
         lib.ssd_oracle_scan_backward.argtypes = ([i64] * 6 + [vp] * 8 + [ctypes.c_int, ctypes.c_double,
-                                                 ctypes.c_double] + [vp] * 10 + [ctypes.c_int])
+                                                 ctypes.c_double] + [vp] * 11 + [ctypes.c_int])
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -168,7 +168,8 @@ def scan_backward(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, dy, dfinal=N
     dy [Bt,T,H,P] and dfinal [Bt,H,P,N] (None: zeros) are taken in float64.
     Returns a dict of float64 arrays: dx, ddt (w.r.t. the pre-activation dt),
     dA, dB, dC, dD, ddt_bias, dh0 (shapes of the inputs; dD, ddt_bias and dA
-    are [H], computed also when D or dt_bias is None)."""
+    are [H], computed also when D or dt_bias is None), and dlda [Bt,T,H] =
+    dL/d(Delta_t A), whose Delta-weighted sum over (b, t) is dA."""
     x, dt, A, B, C = _f32(x), _f32(dt), _f32(A), _f32(B), _f32(C)
     D, dt_bias, h0 = _f32(D), _f32(dt_bias), _f64(h0)
     dy, dfinal = _f64(dy), _f64(dfinal)
@@ -178,14 +179,14 @@ def scan_backward(x, dt, A, B, C, D=None, dt_bias=None, h0=None, *, dy, dfinal=N
     assert dfinal is None or dfinal.shape == (Bt, H, P, N)
     out = {"dx": np.empty((Bt, T, H, P)), "ddt": np.empty((Bt, T, H)), "dA": np.empty(H),
            "dB": np.empty((Bt, T, G, N)), "dC": np.empty((Bt, T, G, N)), "dD": np.empty(H),
-           "ddt_bias": np.empty(H), "dh0": np.empty((Bt, H, P, N))}
+           "ddt_bias": np.empty(H), "dh0": np.empty((Bt, H, P, N)), "dlda": np.empty((Bt, T, H))}
     lo = float(np.float32(dt_min))
     hi = float(np.float32(dt_max))
     rc = _load().ssd_oracle_scan_backward(
         Bt, T, H, P, N, G, _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
         _ptr(h0), int(bool(dt_softplus)), lo, hi, _ptr(dy), _ptr(dfinal), _ptr(out["dx"]),
         _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-        _ptr(out["ddt_bias"]), _ptr(out["dh0"]), int(nthreads))
+        _ptr(out["ddt_bias"]), _ptr(out["dh0"]), _ptr(out["dlda"]), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_scan_backward failed with code {rc}")
     return out

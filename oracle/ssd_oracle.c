@@ -195,6 +195,7 @@ int ssd_oracle_conv1d(int64_t Bt, int64_t T, int64_t D, int64_t K, const float* 
  *     dD      += sum_p dy_t[p] x_t[p]
  *     G       *= abar_t                              (G = dL/dh_{t-1})
  *   dh0 = G;  ddt_t = dd_t * softplus'(z_t) where lo <= softplus(z_t) <= hi, else 0
+ *   (dlda, if not NULL, receives dL/d(d_t A) = abar_t sum G h_{t-1} per token)
  *   (softplus'(z) = 1 / (1 + exp(-z)); without softplus, 1); ddt_bias = sum_t ddt_t.
  *
  * The states h_t are recomputed segment by segment (SEG tokens) from
@@ -208,7 +209,8 @@ int ssd_oracle_scan_backward(int64_t Bt, int64_t T, int64_t H, int64_t P, int64_
                              const double* h0, int dt_softplus, double dt_min, double dt_max,
                              const double* dy, const double* dfinal,
                              double* dx, double* ddt, double* dA, double* dB, double* dC,
-                             double* dD, double* ddt_bias, double* dh0, int nthreads) {
+                             double* dD, double* ddt_bias, double* dh0, double* dlda,
+                             int nthreads) {
   enum { SEG = 64 };
   if (Bt < 0 || T < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0) return 1;
   if (!A || !dA || !dD || !ddt_bias || !dh0) return 1;
@@ -334,6 +336,7 @@ int ssd_oracle_scan_backward(int64_t Bt, int64_t T, int64_t H, int64_t P, int64_
           }
           const double dd = din + Ah * abar * dec;
           dA_acc += d * abar * dec;
+          if (dlda) dlda[(b * T + t) * H + h] = abar * dec;
           double pre = dt_softplus ? softplus_exact(zv[t]) : zv[t];
           double gate = (pre >= dt_min && pre <= dt_max) ? 1.0 : 0.0;
           if (dt_softplus) gate *= 1.0 / (1.0 + exp(-zv[t]));

@@ -34,6 +34,7 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "S
                 7: "SSD_ERR_HIP"}
 EXPORTED = ("ssd_chunk_scan", "ssd_chunk_scan_timed", "ssd_chunk_scan_workspace_bytes",
             "ssd_chunk_scan_schedule", "ssd_step", "ssd_conv1d", "ssd_conv1d_step",
+            "ssd_chunk_scan_backward", "ssd_chunk_scan_backward_workspace_bytes",
             "ssd_status_string", "ssd_abi_version")
 
 
@@ -86,6 +87,10 @@ def _load() -> ctypes.CDLL:
     L.ssd_chunk_scan_schedule.argtypes = [ctypes.POINTER(ScanDesc)]
     L.ssd_step.restype = i32
     L.ssd_step.argtypes = [ctypes.POINTER(StepDesc)] + [vp] * 9 + [vp]
+    L.ssd_chunk_scan_backward.restype = i32
+    L.ssd_chunk_scan_backward.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 19 + [sz, vp]
+    L.ssd_chunk_scan_backward_workspace_bytes.restype = sz
+    L.ssd_chunk_scan_backward_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     L.ssd_conv1d.restype = i32
     L.ssd_conv1d.argtypes = [ctypes.POINTER(ConvDesc)] + [vp] * 6 + [vp]
     L.ssd_conv1d_step.restype = i32
@@ -239,6 +244,62 @@ def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torc
     if st != SSD_OK:
         raise SSDError(st, "ssd_step")
     return y_t
+
+
+def ssd_chunk_scan_backward_workspace_bytes(x: torch.Tensor, B: torch.Tensor,
+                                            chunk: int = 256) -> int:
+    d = scan_desc(x, B, chunk, True, (1e-4, 0.5))
+    return int(lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(d)))
+
+
+def ssd_chunk_scan_backward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                            C: torch.Tensor, D: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
+                            dfinal_state: Optional[torch.Tensor] = None, chunk: int = 256,
+                            dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True,
+                            dt_limit: Sequence[float] = (1e-4, 0.5),
+                            initial_state: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None,
+                            grads: Optional[dict] = None) -> dict:
+    """Gradients of ssd_chunk_scan for L = sum(dy * y) + sum(dfinal_state *
+    final_state), on the current stream.  dy has x's shape and dtype;
+    dfinal_state [Bt,H,P,N] float32 or None.  Returns a dict of float32
+    tensors dx, ddt, dA, dB, dC, dD, ddt_bias, dinitial_state (the last three
+    always computed here)."""
+    for t, n, dt_ in ((x, "x", None), (dt, "dt", torch.float32), (A, "A", torch.float32),
+                      (B, "B", x.dtype), (C, "C", x.dtype), (D, "D", torch.float32),
+                      (dt_bias, "dt_bias", torch.float32), (initial_state, "initial_state", torch.float32),
+                      (dy, "dy", x.dtype), (dfinal_state, "dfinal_state", torch.float32)):
+        _check(t, n, dt_)
+    desc = scan_desc(x, B, chunk, dt_softplus, dt_limit)
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    dev = x.device
+    f32 = torch.float32
+    g = grads or {}
+    out = {
+        "dx": g.get("dx", torch.empty(Bt, T, H, P, device=dev, dtype=f32)),
+        "ddt": g.get("ddt", torch.empty(Bt, T, H, device=dev, dtype=f32)),
+        "dA": g.get("dA", torch.empty(H, device=dev, dtype=f32)),
+        "dB": g.get("dB", torch.empty(Bt, T, G, N, device=dev, dtype=f32)),
+        "dC": g.get("dC", torch.empty(Bt, T, G, N, device=dev, dtype=f32)),
+        "dD": g.get("dD", torch.empty(H, device=dev, dtype=f32)),
+        "ddt_bias": g.get("ddt_bias", torch.empty(H, device=dev, dtype=f32)),
+        "dinitial_state": g.get("dinitial_state", torch.empty(Bt, H, P, N, device=dev, dtype=f32)),
+    }
+    for k, v in out.items():
+        _check(v, k, f32)
+    need = int(lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.ssd_chunk_scan_backward(
+        ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(initial_state), _ptr(dy), _ptr(dfinal_state), _ptr(out["dx"]), _ptr(out["ddt"]),
+        _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["ddt_bias"]),
+        _ptr(out["dinitial_state"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        _stream(dev))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_scan_backward")
+    return out
 
 
 def ssd_conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, *,

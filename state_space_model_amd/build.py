@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 
 SOURCES = ["ssd_api.cpp", "ssd_step.hip", "ssd_state_pass.hip", "ssd_prefill_f32.hip",
-           "ssd_prefill_bf16.hip", "ssd_conv.hip"]
+           "ssd_prefill_bf16.hip", "ssd_conv.hip", "ssd_backward.hip"]
 ARCH = "gfx950"
 
 

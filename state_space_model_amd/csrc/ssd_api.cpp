@@ -6,6 +6,7 @@
 // synchronisation, no global mutable state.
 #include "ssd.h"
 
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -221,6 +222,111 @@ ssd::ConvArgs conv_args(const ssd_conv_desc* d, int64_t T) {
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------------------
+// Backward pass: descriptors of the three internal scans and the workspace.
+// ---------------------------------------------------------------------------
+enum BwdRegion {
+  kScanWs, kScanWsR1, kY, kFinal, kWd, kDtr, kDtr1, kR1x, kR1b, kR1c, kR1h0, kR1y, kR1final, kF2x,
+  kF2h0, kF2y, kR3x, kR3b, kR3c, kR3h0, kR3y, kDdin, kDlda, kDdp, kPart, kX32, kB32, kC32,
+  kNumRegions
+};
+
+struct BwdPlan {
+  ssd_scan_desc fw, r1, f2, r3; // forward and reversed (dx) in float32, forward (dC), reversed (dB)
+  size_t scan_ws = 0;          // scan workspace: F0, then F2 and R3 (after F0's states are used)
+  size_t scan_ws_r1 = 0;       // R1's own (its entering states are read with F0's)
+  size_t fwd_cb_off = 0;       // offset of C B^T in F0's workspace (after states and decays)
+  int64_t pad = 0;             // empty leading positions of R1
+  size_t off[kNumRegions] = {0};
+  size_t total = 0;
+};
+
+ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
+  ScanSizes s0, s1, s2, s3, sf;
+  ssd_status st = check_scan_desc(d, &s0);
+  if (st != SSD_OK) return st;
+  // the recomputed forward and R1 run in float32 (their outputs enter the
+  // Delta gradient through a cancelling sum over the sequence)
+  pl->fw = *d;
+  pl->fw.io_dtype = SSD_F32;
+  // reversed scans read Delta' directly: no softplus, no bias, no clip
+  // the straddle kernel stages one chunk per workgroup of 256 threads
+  if (d->chunk > 256) return SSD_ERR_UNSUPPORTED;
+  const int64_t Nc = (d->seqlen + d->chunk - 1) / d->chunk;
+  pl->pad = Nc * d->chunk - d->seqlen;
+  pl->r1 = pl->fw;
+  pl->r1.seqlen = d->seqlen + pl->pad;
+  pl->r1.dt_softplus = 0;
+  pl->r1.dt_min = 0.0f;
+  pl->r1.dt_max = FLT_MAX;
+  // the state-side scans exchange the roles of P and N, one B/C group per head
+  pl->f2 = *d;
+  pl->f2.headdim = d->dstate;
+  pl->f2.dstate = d->headdim;
+  pl->f2.ngroups = d->nheads;
+  pl->r3 = pl->f2;
+  pl->r3.dt_softplus = 0;
+  pl->r3.dt_min = 0.0f;
+  pl->r3.dt_max = FLT_MAX;
+  if ((st = check_scan_desc(&pl->fw, &sf)) != SSD_OK) return st;
+  if ((st = check_scan_desc(&pl->r1, &s1)) != SSD_OK) return st;
+  if ((st = check_scan_desc(&pl->f2, &s2)) != SSD_OK) return st;
+  if ((st = check_scan_desc(&pl->r3, &s3)) != SSD_OK) return st;
+  if (sf.chain || s1.chain) return SSD_ERR_UNSUPPORTED;   // float32 scans are phased
+  size_t ws = sf.ws_total;
+  if (s2.ws_total > ws) ws = s2.ws_total;
+  if (s3.ws_total > ws) ws = s3.ws_total;
+  pl->scan_ws = ws;
+  pl->scan_ws_r1 = s1.ws_total;
+  pl->fwd_cb_off = sf.ws_state_bytes + sf.ws_alpha_bytes;
+  const size_t es = io_size(d->io_dtype);
+  const bool bf = d->io_dtype == SSD_BF16;
+  const size_t nx = (size_t)s0.n_x, nbc = (size_t)s0.n_bc, nst = (size_t)s0.n_state;
+  const size_t ndt = (size_t)s0.n_dt, nxn = (size_t)s2.n_x;      // [Bt,T,H,N]
+  const size_t nx1 = (size_t)s1.n_x, nbc1 = (size_t)s1.n_bc, ndt1 = (size_t)s1.n_dt;  // R1, padded
+  const size_t bh = (size_t)(d->batch * d->nheads);
+  size_t sizes[kNumRegions];
+  sizes[kScanWs] = ws;
+  sizes[kScanWsR1] = pl->scan_ws_r1;
+  sizes[kY] = nx * 4;
+  sizes[kFinal] = nst * 4;
+  sizes[kWd] = ndt * 4;
+  sizes[kDtr] = ndt * 4;
+  sizes[kDtr1] = ndt1 * 4;
+  sizes[kR1x] = nx1 * 4;
+  sizes[kR1b] = nbc1 * 4;
+  sizes[kR1c] = nbc1 * 4;
+  sizes[kR1h0] = nst * 4;
+  sizes[kR1y] = nx1 * 4;
+  sizes[kR1final] = nst * 4;
+  sizes[kF2x] = nxn * es;
+  sizes[kF2h0] = nst * 4;
+  sizes[kF2y] = nxn * es;
+  sizes[kR3x] = nxn * es;
+  sizes[kR3b] = nx * es;
+  sizes[kR3c] = nx * es;
+  sizes[kR3h0] = nst * 4;
+  sizes[kR3y] = nxn * es;
+  sizes[kDdin] = ndt * 4;
+  sizes[kDlda] = ndt * 4;
+  sizes[kDdp] = ndt * 4;
+  sizes[kPart] = 3 * bh * 4;
+  sizes[kX32] = bf ? nx * 4 : 0;
+  sizes[kB32] = bf ? nbc * 4 : 0;
+  sizes[kC32] = bf ? nbc * 4 : 0;
+  size_t at = 0;
+  for (int k = 0; k < kNumRegions; ++k) {
+    pl->off[k] = at;
+    at += round_up(sizes[k], kAlign);
+  }
+  pl->total = at;
+  return SSD_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc) {
@@ -353,6 +459,127 @@ ssd_status ssd_conv1d_step(const ssd_conv_desc* d, void* state, const void* x_t,
   a.x = x_t; a.w = w; a.bias = bias; a.state_in = state; a.y = y_t; a.state_out = state;
   const hipError_t e = ssd::launch_conv(a, d->io_dtype == SSD_BF16, true, stream);
   return e == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+size_t ssd_chunk_scan_backward_workspace_bytes(const ssd_scan_desc* desc) {
+  BwdPlan pl;
+  if (plan_backward(desc, &pl) != SSD_OK) return 0;
+  return pl.total;
+}
+
+ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* d, const void* x, const float* dt,
+                                   const float* dt_bias, const float* A, const void* B,
+                                   const void* C, const float* D, const float* initial_state,
+                                   const void* dy, const float* dfinal_state, float* dx,
+                                   float* ddt, float* dA, float* dB, float* dC, float* dD,
+                                   float* ddt_bias, float* dinitial_state, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  BwdPlan pl;
+  ssd_status st = plan_backward(d, &pl);
+  if (st != SSD_OK) return st;
+  ScanSizes s;
+  check_scan_desc(d, &s);
+  const bool tokens = d->batch > 0 && d->seqlen > 0;
+  if (d->batch > 0 && (!A || !dA)) return SSD_ERR_INVALID_ARG;
+  if (tokens && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC))
+    return SSD_ERR_INVALID_ARG;
+  const void* vec[] = {x, B, C, initial_state, dy, dfinal_state, dx, dB, dC, dinitial_state,
+                       workspace};
+  for (const void* p : vec)
+    if (p && !aligned16(p)) return SSD_ERR_ALIGNMENT;
+  const void* scal[] = {dt, dt_bias, A, D, ddt, dA, dD, ddt_bias};
+  for (const void* p : scal)
+    if (p && !aligned4(p)) return SSD_ERR_ALIGNMENT;
+  if (tokens && (!workspace || workspace_bytes < pl.total)) return SSD_ERR_WORKSPACE;
+  // gradients must not overlap any input, the workspace or each other
+  const int64_t es = (int64_t)io_size(d->io_dtype), H = d->nheads;
+  const Range outs[] = {range_of(dx, tokens ? s.n_x * 4 : 0),
+                        range_of(ddt, tokens ? s.n_dt * 4 : 0), range_of(dA, H * 4),
+                        range_of(dB, tokens ? s.n_bc * 4 : 0),
+                        range_of(dC, tokens ? s.n_bc * 4 : 0), range_of(dD, H * 4),
+                        range_of(ddt_bias, H * 4), range_of(dinitial_state, s.n_state * 4)};
+  const Range ins[] = {range_of(x, tokens ? s.n_x * es : 0),
+                       range_of(dt, tokens ? s.n_dt * 4 : 0), range_of(dt_bias, H * 4),
+                       range_of(A, H * 4), range_of(B, tokens ? s.n_bc * es : 0),
+                       range_of(C, tokens ? s.n_bc * es : 0), range_of(D, H * 4),
+                       range_of(initial_state, s.n_state * 4),
+                       range_of(dy, tokens ? s.n_x * es : 0),
+                       range_of(dfinal_state, s.n_state * 4),
+                       range_of(workspace, tokens ? (int64_t)pl.total : 0)};
+  const int nouts = (int)(sizeof(outs) / sizeof(outs[0]));
+  for (int i = 0; i < nouts; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return SSD_ERR_INVALID_ARG;
+    for (int j = i + 1; j < nouts; ++j)
+      if (overlap(outs[i], outs[j])) return SSD_ERR_INVALID_ARG;
+  }
+  if (d->batch == 0) {
+    if (!dA && !dD && !ddt_bias) return SSD_OK;
+    if (!dA) return SSD_ERR_INVALID_ARG;
+    return ssd::launch_backward_zero_heads(dA, ddt_bias, dD, H, stream) == hipSuccess
+               ? SSD_OK : SSD_ERR_HIP;
+  }
+  if (!tokens) {
+    // no token: the parameters get no gradient, the initial state passes dfinal on
+    if (ssd::launch_backward_zero_heads(dA, ddt_bias, dD, H, stream) != hipSuccess)
+      return SSD_ERR_HIP;
+    if (dinitial_state &&
+        ssd::launch_copy_or_zero(dinitial_state, dfinal_state, s.n_state, stream) != hipSuccess)
+      return SSD_ERR_HIP;
+    return SSD_OK;
+  }
+
+  char* w = static_cast<char*>(workspace);
+  auto at = [&](int k) { return static_cast<void*>(w + pl.off[k]); };
+  auto atf = [&](int k) { return reinterpret_cast<float*>(w + pl.off[k]); };
+  void* scan_ws = at(kScanWs);
+
+  ssd::BwdArgs a;
+  a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
+  a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state;
+  a.y = atf(kY); a.fwd_final = atf(kFinal);
+  const bool bf = d->io_dtype == SSD_BF16;
+  a.x32 = bf ? atf(kX32) : nullptr; a.b32 = bf ? atf(kB32) : nullptr;
+  a.c32 = bf ? atf(kC32) : nullptr;
+  a.wd = atf(kWd); a.dtr = atf(kDtr); a.dtr1 = atf(kDtr1);
+  a.r1_x = atf(kR1x); a.r1_b = atf(kR1b); a.r1_c = atf(kR1c); a.r1_h0 = atf(kR1h0);
+  a.r1_y = atf(kR1y); a.r1_final = atf(kR1final);
+  a.f2_x = at(kF2x); a.f2_h0 = atf(kF2h0); a.f2_y = at(kF2y);
+  a.r3_x = at(kR3x); a.r3_b = at(kR3b); a.r3_c = at(kR3c); a.r3_h0 = atf(kR3h0);
+  a.r3_y = at(kR3y);
+  a.ddin = atf(kDdin); a.dlda = atf(kDlda); a.dDp = atf(kDdp); a.part = atf(kPart);
+  a.fwd_state = atf(kScanWs);
+  a.fwd_cb = reinterpret_cast<const float*>(w + pl.off[kScanWs] + pl.fwd_cb_off);
+  a.r1_state = atf(kScanWsR1);
+  a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
+  a.ddt_bias_out = ddt_bias; a.dh0 = dinitial_state;
+  a.Bt = d->batch; a.T = d->seqlen; a.H = d->nheads; a.G = d->ngroups;
+  a.L = d->chunk; a.Nc = s.Nc; a.pad = pl.pad;
+  a.P = (int32_t)d->headdim; a.N = (int32_t)d->dstate;
+  a.softplus = d->dt_softplus ? 1 : 0;
+  a.dt_min = d->dt_min; a.dt_max = d->dt_max;
+
+  if (ssd::launch_backward_phase(a, bf, 0, stream) != hipSuccess) return SSD_ERR_HIP;
+  // forward in float32: y and the final state
+  st = ssd_chunk_scan(&pl.fw, bf ? a.x32 : x, dt, dt_bias, A, bf ? a.b32 : B, bf ? a.c32 : C, D,
+                      initial_state, at(kY), atf(kFinal), scan_ws, pl.scan_ws, stream);
+  if (st != SSD_OK) return st;
+  // R1: sum_n G B over reversed time; its final state is dL/dh_{-1} / abar_0
+  st = ssd_chunk_scan(&pl.r1, a.r1_x, a.dtr1, nullptr, A, a.r1_b, a.r1_c, nullptr, a.r1_h0,
+                      at(kR1y), atf(kR1final), at(kScanWsR1), pl.scan_ws_r1, stream);
+  if (st != SSD_OK) return st;
+  if (ssd::launch_backward_phase(a, bf, 1, stream) != hipSuccess) return SSD_ERR_HIP;
+  // F2: sum_p dy h (input B per head, B'' = x, C'' = dy)
+  st = ssd_chunk_scan(&pl.f2, a.f2_x, dt, dt_bias, A, x, dy, nullptr,
+                      initial_state ? a.f2_h0 : nullptr, at(kF2y), nullptr, scan_ws, pl.scan_ws,
+                      stream);
+  if (st != SSD_OK) return st;
+  // R3: sum_p G x over reversed time (input C / Delta' per head, B''' = dy, C''' = x)
+  st = ssd_chunk_scan(&pl.r3, a.r3_x, a.dtr, nullptr, A, a.r3_b, a.r3_c, nullptr, a.r3_h0,
+                      at(kR3y), nullptr, scan_ws, pl.scan_ws, stream);
+  if (st != SSD_OK) return st;
+  if (ssd::launch_backward_phase(a, bf, 2, stream) != hipSuccess) return SSD_ERR_HIP;
+  return SSD_OK;
 }
 
 const char* ssd_status_string(ssd_status s) {

@@ -57,6 +57,70 @@ struct ConvArgs {
   int32_t silu;
 };
 
+// Arguments of the element-wise, transform and reduction kernels of the
+// scan's backward pass (ssd_backward.hip).  Device pointers.
+struct BwdArgs {
+  // inputs of the forward scan and the cotangents
+  const void* x;            // [Bt,T,H,P] io
+  const float* dt;          // [Bt,T,H]
+  const float* dt_bias;     // [H] or null
+  const float* A;           // [H]
+  const void* B;            // [Bt,T,G,N] io
+  const void* C;            // [Bt,T,G,N] io
+  const float* D;           // [H] or null
+  const float* h0;          // [Bt,H,P,N] or null
+  const void* dy;           // [Bt,T,H,P] io
+  const float* dfinal;      // [Bt,H,P,N] or null
+  // forward results (recomputed, float32)
+  const float* y;           // [Bt,T,H,P]
+  const float* fwd_final;   // [Bt,H,P,N]
+  // float32 copies of x, B, C for the float32 scans (bfloat16 io only, else null)
+  float* x32;               // [Bt,T,H,P]
+  float* b32;               // [Bt,T,G,N]
+  float* c32;               // [Bt,T,G,N]
+  // workspace: Delta, the reversed Delta', and the three scans' operands and results
+  float* wd;                // [Bt,T,H] Delta
+  float* dtr;               // [Bt,T,H] Delta at reversed positions, shifted by one step (R3)
+  float* dtr1;              // [Bt,T+pad,H] the same after R1's pad positions
+  float* r1_x;              // [Bt,T+pad,H,P] f32 reversed dy / Delta'
+  float* r1_b;              // [Bt,T+pad,G,N] f32 reversed C
+  float* r1_c;              // [Bt,T+pad,G,N] f32 reversed B
+  float* r1_h0;             // [Bt,H,P,N]     dfinal + dy_{T-1} (x) C_{T-1}
+  const float* r1_y;        // [Bt,T+pad,H,P] f32 sum_n G B (reversed positions)
+  const float* r1_final;    // [Bt,H,P,N]     dL/dh_{-1} / abar_0
+  void* f2_x;               // [Bt,T,H,N] io  B per head
+  float* f2_h0;             // [Bt,H,N,P]     initial state transposed
+  const void* f2_y;         // [Bt,T,H,N] io  sum_p dy h
+  void* r3_x;               // [Bt,T,H,N] io  reversed C / Delta' per head
+  void* r3_b;               // [Bt,T,H,P] io  reversed dy
+  void* r3_c;               // [Bt,T,H,P] io  reversed x
+  float* r3_h0;             // [Bt,H,N,P]     (dfinal + dy_{T-1} (x) C_{T-1}) transposed
+  const void* r3_y;         // [Bt,T,H,N] io  sum_p G x (reversed positions)
+  // entering states and C B^T tiles the float32 scans leave in their workspaces
+  const float* fwd_state;   // [Bt,H,Nc,P,N] state entering forward chunk c (H_c)
+  const float* fwd_cb;      // [Bt,Nc,G,L,L] C B^T of each forward chunk
+  const float* r1_state;    // [Bt,H,Nc,P,N] state entering reversed chunk c' (G at (Nc-c')L)
+  float* ddin;              // [Bt,T,H]  x_t . (sum_n G B)
+  float* dlda;              // [Bt,T,H]  dL/d(Delta_t A)
+  float* dDp;               // [Bt,T,H]  dy_t . x_t
+  float* part;              // [3][Bt,H] parts of dA, ddt_bias, dD
+  // gradients
+  float* dx;                // [Bt,T,H,P]
+  float* ddt;               // [Bt,T,H]
+  float* dA;                // [H]
+  float* dB;                // [Bt,T,G,N]
+  float* dC;                // [Bt,T,G,N]
+  float* dD;                // [H] or null
+  float* ddt_bias_out;      // [H] or null
+  float* dh0;               // [Bt,H,P,N] or null
+  int64_t Bt, T, H, G;
+  int64_t L, Nc;            // chunk and chunks of the forward partition
+  int64_t pad;              // leading empty positions of the reversed scan R1 (Nc L - T)
+  int32_t P, N;
+  int32_t softplus;
+  float dt_min, dt_max;
+};
+
 // Compiled shape variants.
 bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16);
 
@@ -90,6 +154,14 @@ hipError_t launch_step_bf16(const StepArgs& a, hipStream_t stream);
 bool conv_width_supported(int64_t K);
 bool conv_shape_supported(int64_t Bt, int64_t T, int64_t D);
 hipError_t launch_conv(const ConvArgs& a, bool io_bf16, bool step, hipStream_t stream);
+
+// Backward pass pieces: phase 0 prepares the reversed / replicated operands
+// and initial states of the three scans, phase 1 (after the float32 forward
+// and reversed scans) forms dL/d(Delta A), dx, dt, dA, ddt_bias, dD and dh0,
+// phase 2 forms dB and dC.
+hipError_t launch_backward_phase(const BwdArgs& a, bool io_bf16, int phase, hipStream_t stream);
+hipError_t launch_backward_zero_heads(float* dA, float* ddt_bias, float* dD, int64_t H,
+                                      hipStream_t stream);
 
 // dst[i] = src ? src[i] : 0 for i < n (float4 granularity; n % 4 == 0).
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert ssd.abi_version() == 3
+    assert ssd.abi_version() == 4
     for code in range(8):
         s = lib.ssd_status_string(code).decode()
         assert s.startswith(ssd.STATUS_NAMES[code])
@@ -277,6 +277,42 @@ def test_conv_step_errors():
     assert conv_step_status(d, y=BASE + 16) == INVALID            # y over the window
     assert conv_step_status(d, x=BASE + 32) == INVALID            # x inside the window
     assert conv_step_status(conv_desc(batch=0)) == OK
+
+
+def bwd_status(d, ws_bytes=None, **over):
+    ptr = {k: BASE + (i << 26) for i, k in enumerate(
+        ["x", "dt", "bias", "A", "B", "C", "D", "h0", "dy", "df", "dx", "ddt", "dA", "dB", "dC",
+         "dD", "dbias", "dh0", "ws"])}
+    ptr.update(over)
+    P = ctypes.c_void_p
+    need = lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(d))
+    return lib.ssd_chunk_scan_backward(
+        ctypes.byref(d), *[P(ptr[k]) for k in ["x", "dt", "bias", "A", "B", "C", "D", "h0", "dy",
+                                               "df", "dx", "ddt", "dA", "dB", "dC", "dD", "dbias",
+                                               "dh0", "ws"]],
+        ctypes.c_size_t(need if ws_bytes is None else ws_bytes), P(0))
+
+
+def test_backward_workspace_and_errors():
+    d = desc()
+    need = lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(d))
+    assert need > lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
+    assert need % 256 == 0
+    # the exchanged form of the shape must be supported too
+    assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(dstate=128, chunk=512, headdim=32))) == 0
+    assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(io_dtype=1, headdim=16, dstate=32))) == 0
+    assert bwd_status(desc(dstate=128, chunk=512, headdim=32)) == UNSUP
+    assert bwd_status(desc(io_dtype=5)) == DTYPE
+    assert bwd_status(d, dy=0) == INVALID
+    assert bwd_status(d, dx=0) == INVALID
+    assert bwd_status(d, dA=0) == INVALID
+    assert bwd_status(d, dy=BASE + (8 << 26) + 4) == ALIGN
+    assert bwd_status(d, ddt=BASE + (11 << 26) + 2) == ALIGN
+    assert bwd_status(d, ws=0) == WS
+    assert bwd_status(d, ws_bytes=1024) == WS
+    assert bwd_status(d, dx=BASE) == INVALID                 # gradient over x
+    assert bwd_status(d, dB=BASE + (10 << 26)) == INVALID    # two gradients overlap
+    assert bwd_status(d, dh0=BASE + (18 << 26) + 4096) == INVALID  # inside the workspace
 
 
 def test_binding_refuses_cpu_tensors():

@@ -28,6 +28,17 @@ def test_backward_oracle_thread_count_bitwise():
         assert np.array_equal(g1[k], g8[k]), k
 
 
+def test_backward_oracle_dA_is_the_delta_weighted_sum_of_dlda():
+    from backward_pins import call, case_inputs
+    for i in range(4):
+        inp, dy, dfinal, kw = case_inputs(i)
+        g = call(oracle.scan_backward, inp, dy, dfinal, kw)
+        z = inp["dt"].astype(np.float64) + inp["dt_bias"][None, None, :]
+        pre = np.logaddexp(0.0, z) if kw["dt_softplus"] else z
+        d = np.clip(pre, float(np.float32(kw["dt_min"])), float(np.float32(kw["dt_max"])))
+        assert np.allclose(g["dA"], (d * g["dlda"]).sum(axis=(0, 1)), rtol=1e-12, atol=1e-12)
+
+
 MUTATIONS = ["decay_uses_h_t", "decay_before_add", "no_dfinal", "dB_no_delta", "dC_prev_state",
              "no_clip_gate", "softplus_grad_wrong", "dD_missing", "dA_missing_delta"]
 
