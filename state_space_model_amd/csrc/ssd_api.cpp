@@ -252,8 +252,9 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   pl->fw = *d;
   pl->fw.io_dtype = SSD_F32;
   // reversed scans read Delta' directly: no softplus, no bias, no clip
-  // the straddle kernel stages one chunk per workgroup of 256 threads
-  if (d->chunk > 256) return SSD_ERR_UNSUPPORTED;
+  // the straddle kernel stages one chunk per workgroup of 256 threads; the
+  // element-wise kernels index (batch, token, head) rows in 32 bits
+  if (d->chunk > 256 || s0.n_dt > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
   const int64_t Nc = (d->seqlen + d->chunk - 1) / d->chunk;
   pl->pad = Nc * d->chunk - d->seqlen;
   pl->r1 = pl->fw;

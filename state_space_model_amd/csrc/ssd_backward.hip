@@ -51,11 +51,14 @@ __device__ __forceinline__ float delta_at(const BwdArgs& a, int64_t b, int64_t t
 // positions of R1 are zeroed by k_bwd_zero_pad.
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep(BwdArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t row32 = blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= a.Bt * a.T * a.H) return;
-  const int64_t h = row % a.H, bt = row / a.H, t = bt % a.T, b = bt / a.T;
-  const int64_t hpg = a.H / a.G, g = h / hpg;
+  if ((int64_t)row32 >= a.Bt * a.T * a.H) return;
+  // rows fit 32 bits (checked on the host): 32-bit divisions
+  const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T, hpg32 = (uint32_t)(a.H / a.G);
+  const uint32_t bt32 = row32 / H32;
+  const int64_t row = row32, h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
+  const int64_t hpg = hpg32, g = (uint32_t)h / hpg32;
   const int64_t tr = a.T - 1 - t;                     // reversed position of token t (R3)
   const int64_t T1 = a.T + a.pad, tr1 = a.pad + tr;    // R1: after pad empty positions
   const int P = a.P, N = a.N;
@@ -229,7 +232,7 @@ __device__ __forceinline__ f32x4 mfma4(float4 a, float4 b, f32x4 c) {
 // Row sums of Q are kept per (row tile, column tile) and added in column
 // order; column sums are owned by one wavefront per column tile: the result
 // does not depend on scheduling.
-template <typename T>
+template <typename T, int P, int N>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
   constexpr int LMAX = kBwdThreads, NRT = LMAX / 16;
   __shared__ double s_cum[LMAX];
@@ -245,7 +248,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
   const int64_t L = a.L, t0 = c * L;
   const int Lc = (int)(a.T - t0 < L ? a.T - t0 : L);
   const int nrt = (Lc + 15) / 16;
-  const int P = a.P, N = a.N;
   const float Ah = a.A[h];
 
   // Delta and the chunk's cumulative log-decay, in double
@@ -283,15 +285,27 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
     const bool jok = j < Lc;
     const float dj = jok ? s_d[j] : 0.0f;
     const double cj = s_cum[jok ? j : 0];
+    // this lane's x row (column j of the tiles), loaded once for the column tile
+    float4 xr[P / 16];
+#pragma unroll
+    for (int pb = 0; pb < P / 16; ++pb)
+      xr[pb] = ld4_io<T>(xg + (jok ? j : Lc - 1) * xrs + 16 * pb + 4 * q, jok);
     float colacc = 0.0f;
     for (int I = J; I < nrt; ++I) {
       const int ia = 16 * I + r16;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int pb = 0; pb < P / 16; ++pb) {
-        const float4 av = ld4_io<T>(dyg + (ia < Lc ? ia : Lc - 1) * xrs + 16 * pb + 4 * q, ia < Lc);
-        const float4 bv = ld4_io<T>(xg + (jok ? j : Lc - 1) * xrs + 16 * pb + 4 * q, jok);
-        acc = mfma4(av, bv, acc);
+      float4 dr[P / 16];
+#pragma unroll
+      for (int pb = 0; pb < P / 16; ++pb)
+        dr[pb] = ld4_io<T>(dyg + (ia < Lc ? ia : Lc - 1) * xrs + 16 * pb + 4 * q, ia < Lc);
+      float sv[4];
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int i = 16 * I + 4 * q + rr;
+        sv[rr] = (jok && i > j && i < Lc) ? S[(int64_t)i * L + j] : 0.0f;
       }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pb = 0; pb < P / 16; ++pb) acc = mfma4(dr[pb], xr[pb], acc);
       float colpart = 0.0f;
       float rowv[4];
 #pragma unroll
@@ -300,7 +314,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
         float qv = 0.0f;
         if (jok && i > j && i < Lc) {
           const float dec = expf((float)(s_cum[i] - cj));
-          qv = acc[rr] * S[(int64_t)i * L + j] * dec * dj;
+          qv = acc[rr] * sv[rr] * dec * dj;
         }
         rowv[rr] = qv;
         colpart += qv;
@@ -319,7 +333,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
   }
 
   // ---- state terms: C H_c^T against dy, B Ghat_c^T against x ----
-  const int64_t PN = (int64_t)P * N;
+  constexpr int64_t PN = (int64_t)P * N;
   const float* Hc = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
   const float* Gh = nullptr;
   float gs = 1.0f;
@@ -332,18 +346,26 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
   for (int I = wave; I < nrt; I += kBwdThreads / 64) {
     const int ia = 16 * I + r16;
     const bool iok = ia < Lc;
+    // this lane's C and B rows (row i = 16 I + r16), loaded once for all p tiles
+    float4 cr[N / 16], br[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) {
+      cr[nb] = ld4_io<T>(Cg + (iok ? ia : Lc - 1) * brs + 16 * nb + 4 * q, iok);
+      br[nb] = ld4_io<T>(Bg + (iok ? ia : Lc - 1) * brs + 16 * nb + 4 * q, iok);
+    }
     float qp[4] = {0.f, 0.f, 0.f, 0.f}, rp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
     for (int pt = 0; pt < P / 16; ++pt) {
       f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
-      for (int nb = 0; nb < N / 16; ++nb) {
-        const float4 cv = ld4_io<T>(Cg + (iok ? ia : Lc - 1) * brs + 16 * nb + 4 * q, iok);
-        const float4 bv = ld4_io<T>(Bg + (iok ? ia : Lc - 1) * brs + 16 * nb + 4 * q, iok);
-        const float4 hv = *reinterpret_cast<const float4*>(Hc + (16 * pt + r16) * N + 16 * nb + 4 * q);
-        ay = mfma4(cv, hv, ay);
-        if (Gh) {
-          const float4 gv = *reinterpret_cast<const float4*>(Gh + (16 * pt + r16) * N + 16 * nb + 4 * q);
-          ag = mfma4(bv, gv, ag);
-        }
+      const float* hrow = Hc + (16 * pt + r16) * N + 4 * q;
+#pragma unroll
+      for (int nb = 0; nb < N / 16; ++nb)
+        ay = mfma4(cr[nb], *reinterpret_cast<const float4*>(hrow + 16 * nb), ay);
+      if (Gh) {
+        const float* grow = Gh + (16 * pt + r16) * N + 4 * q;
+#pragma unroll
+        for (int nb = 0; nb < N / 16; ++nb)
+          ag = mfma4(br[nb], *reinterpret_cast<const float4*>(grow + 16 * nb), ag);
       }
       // lane holds rows i = 16 I + 4 q + rr, column p = 16 pt + r16
 #pragma unroll
@@ -374,7 +396,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
   // s_c = e^{cum_last} <Ghat_c, H_c>
   float sc = 0.0f;
   if (Gh)
-    for (int64_t e = tid; e < PN; e += kBwdThreads) sc = __fmaf_rn(Gh[e], Hc[e], sc);
+    for (int e = tid; e < P * N; e += kBwdThreads) sc = __fmaf_rn(Gh[e], Hc[e], sc);
   sc = group_sum(sc, 64);
   if (lane == 0) s_w[wave] = sc;
   __syncthreads();
@@ -481,9 +503,20 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
                          dim3(blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads)),
                          dim3(kBwdThreads), 0, s, a);
       break;
-    case 1:
-      hipLaunchKernelGGL(k_bwd_dlda<T>, dim3((unsigned)(a.Bt * a.Nc * a.H)), dim3(kBwdThreads), 0,
-                         s, a);
+    case 1: {
+      const dim3 grid((unsigned)(a.Bt * a.Nc * a.H));
+      hipError_t e = hipErrorInvalidValue;
+#define SSD_BWD_DLDA(PP, NN)                                                          \
+  if (a.P == PP && a.N == NN) {                                                       \
+    hipLaunchKernelGGL((k_bwd_dlda<T, PP, NN>), grid, dim3(kBwdThreads), 0, s, a);     \
+    e = hipSuccess;                                                                   \
+  }
+      SSD_BWD_DLDA(16, 16) SSD_BWD_DLDA(16, 32) SSD_BWD_DLDA(16, 64) SSD_BWD_DLDA(16, 128)
+      SSD_BWD_DLDA(32, 16) SSD_BWD_DLDA(32, 32) SSD_BWD_DLDA(32, 64) SSD_BWD_DLDA(32, 128)
+      SSD_BWD_DLDA(64, 16) SSD_BWD_DLDA(64, 32) SSD_BWD_DLDA(64, 64) SSD_BWD_DLDA(64, 128)
+      SSD_BWD_DLDA(128, 16) SSD_BWD_DLDA(128, 32) SSD_BWD_DLDA(128, 64) SSD_BWD_DLDA(128, 128)
+#undef SSD_BWD_DLDA
+      if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_bwd_dx<T>, dim3(blocks_of(rows, kBwdThreads / 64)), dim3(kBwdThreads),
                          0, s, a);
       hipLaunchKernelGGL(k_bwd_dt, dim3((unsigned)(a.Bt * a.H)), dim3(kBwdThreads), 0, s, a);
@@ -493,6 +526,7 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
         hipLaunchKernelGGL(k_bwd_dh0, dim3(blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads)),
                            dim3(kBwdThreads), 0, s, a);
       break;
+    }
     case 2:
       hipLaunchKernelGGL(k_bwd_dbdc<T>, dim3(blocks_of(a.Bt * a.T * a.G * (int64_t)a.N, kBwdThreads)),
                          dim3(kBwdThreads), 0, s, a);
