@@ -477,6 +477,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time the scan's gradients (ssd_chunk_scan_backward) on the workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the known-size copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
@@ -498,6 +500,10 @@ def main():
     w = WORKLOADS[args.workload]
     if args.chunk:
         w = w.with_(chunk=args.chunk)
+    if args.backward_only:
+        print(f"[bench] backward {w.name} L={w.chunk}", file=sys.stderr, flush=True)
+        print(json.dumps(bench_backward(ssd, torch, w)))
+        return
     print(f"[bench] prefill {w.name} L={w.chunk} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
     pf = bench_prefill(ssd, torch, w, args.steps, args.warmup)

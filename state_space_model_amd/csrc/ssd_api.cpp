@@ -106,17 +106,20 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
                      const float* dt_bias, const float* A, const void* B, const void* C,
                      const float* D, const float* initial_state, void* y, float* final_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream,
-                     hipEvent_t* events, int n_events) {
+                     hipEvent_t* events, int n_events, bool states_only = false) {
   ScanSizes s;
   ssd_status st = check_scan_desc(desc, &s);
   if (st != SSD_OK) return st;
+  // phases 0-2 alone (entering states and C B^T left in the workspace, no y):
+  // float32 phased schedule only
+  if (states_only && (desc->io_dtype != SSD_F32 || s.chain)) return SSD_ERR_UNSUPPORTED;
   if (events) {
     if (n_events < SSD_SCAN_PHASES + 1) return SSD_ERR_INVALID_ARG;
     for (int k = 0; k <= SSD_SCAN_PHASES; ++k)
       if (!events[k]) return SSD_ERR_INVALID_ARG;
   }
   const bool work = desc->batch > 0 && desc->seqlen > 0;
-  if (work && (!x || !dt || !A || !B || !C || !y)) return SSD_ERR_INVALID_ARG;
+  if (work && (!x || !dt || !A || !B || !C || (!y && !states_only))) return SSD_ERR_INVALID_ARG;
   if (!work && desc->batch > 0 && !A) return SSD_ERR_INVALID_ARG;
   // tensors read or written in 16-byte vectors, and per-token/per-head scalars
   const void* vec[] = {x, B, C, initial_state, y, final_state, workspace};
@@ -129,7 +132,7 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
 
   // outputs must not overlap any input, the workspace or each other
   const int64_t es = (int64_t)io_size(desc->io_dtype);
-  const Range r_y = work ? range_of(y, s.n_x * es) : Range{0, 0};
+  const Range r_y = work && y ? range_of(y, s.n_x * es) : Range{0, 0};
   const Range r_f = final_state ? range_of(final_state, s.n_state * 4) : Range{0, 0};
   const Range ins[] = {
       range_of(x, work ? s.n_x * es : 0), range_of(dt, work ? s.n_dt * 4 : 0),
@@ -169,6 +172,7 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   a.softplus = desc->dt_softplus ? 1 : 0;
   a.dt_min = desc->dt_min; a.dt_max = desc->dt_max;
   a.chain = s.chain ? 1 : 0;
+  a.states_only = states_only ? 1 : 0;
   hipError_t e = desc->io_dtype == SSD_BF16
                      ? ssd::launch_scan_bf16(a, (int)desc->headdim, (int)desc->dstate, stream, events)
                      : ssd::launch_scan_f32(a, (int)desc->headdim, (int)desc->dstate, stream, events);
@@ -228,73 +232,78 @@ namespace {
 // Backward pass: descriptors of the three internal scans and the workspace.
 // ---------------------------------------------------------------------------
 enum BwdRegion {
-  kScanWs, kScanWsR1, kY, kFinal, kWd, kDtr, kDtr1, kR1x, kR1b, kR1c, kR1h0, kR1y, kR1final, kF2x,
-  kF2h0, kF2y, kR3x, kR3b, kR3c, kR3h0, kR3y, kDdin, kDlda, kDdp, kPart, kX32, kB32, kC32,
-  kNumRegions
+  kScanWs, kScanWsR1, kWd, kCum, kDtr1, kR1x, kR1b, kR1c, kR1h0, kR1y, kR1final, kMix, kQrow,
+  kQcol, kUv, kDbcPart, kDdin, kDdp, kPart, kX32, kB32, kC32, kNumRegions
 };
 
 struct BwdPlan {
-  ssd_scan_desc fw, r1, f2, r3; // forward and reversed (dx) in float32, forward (dC), reversed (dB)
-  size_t scan_ws = 0;          // scan workspace: F0, then F2 and R3 (after F0's states are used)
+  ssd_scan_desc fw, r1;        // forward state scan and reversed scan R1, both float32
+  size_t scan_ws = 0;          // F0's workspace (entering states, decays, C B^T)
   size_t scan_ws_r1 = 0;       // R1's own (its entering states are read with F0's)
   size_t fwd_cb_off = 0;       // offset of C B^T in F0's workspace (after states and decays)
   int64_t pad = 0;             // empty leading positions of R1
+  int32_t NB = 0, LP = 0, HS = 1, hpw = 1, HSD = 1, hpwd = 1, NS = 1;
   size_t off[kNumRegions] = {0};
   size_t total = 0;
 };
 
+// Splits of a group's heads over workgroups: enough workgroups to fill the
+// device (`target`), each with at least one head.
+inline void head_split(int64_t hpg, int64_t units, int64_t target, int32_t* splits,
+                       int32_t* per) {
+  int64_t want = units > 0 ? (target + units - 1) / units : 1;
+  if (want < 1) want = 1;
+  if (want > hpg) want = hpg;
+  const int64_t p = (hpg + want - 1) / want;
+  *per = (int32_t)p;
+  *splits = (int32_t)((hpg + p - 1) / p);
+}
+
 ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
-  ScanSizes s0, s1, s2, s3, sf;
+  ScanSizes s0, s1, sf;
   ssd_status st = check_scan_desc(d, &s0);
   if (st != SSD_OK) return st;
-  // the recomputed forward and R1 run in float32 (their outputs enter the
-  // Delta gradient through a cancelling sum over the sequence)
+  // the kernels of the gradient stage one chunk per workgroup of 256 threads
+  // and index (batch, token, head) rows in 32 bits
+  if (d->chunk > 256 || s0.n_dt > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
+  // the forward states and R1 run in float32 whatever the io type
   pl->fw = *d;
   pl->fw.io_dtype = SSD_F32;
-  // reversed scans read Delta' directly: no softplus, no bias, no clip
-  // the straddle kernel stages one chunk per workgroup of 256 threads; the
-  // element-wise kernels index (batch, token, head) rows in 32 bits
-  if (d->chunk > 256 || s0.n_dt > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
   const int64_t Nc = (d->seqlen + d->chunk - 1) / d->chunk;
   pl->pad = Nc * d->chunk - d->seqlen;
+  // R1 reads Delta' directly: no softplus, no bias, no clip
   pl->r1 = pl->fw;
   pl->r1.seqlen = d->seqlen + pl->pad;
   pl->r1.dt_softplus = 0;
   pl->r1.dt_min = 0.0f;
   pl->r1.dt_max = FLT_MAX;
-  // the state-side scans exchange the roles of P and N, one B/C group per head
-  pl->f2 = *d;
-  pl->f2.headdim = d->dstate;
-  pl->f2.dstate = d->headdim;
-  pl->f2.ngroups = d->nheads;
-  pl->r3 = pl->f2;
-  pl->r3.dt_softplus = 0;
-  pl->r3.dt_min = 0.0f;
-  pl->r3.dt_max = FLT_MAX;
   if ((st = check_scan_desc(&pl->fw, &sf)) != SSD_OK) return st;
   if ((st = check_scan_desc(&pl->r1, &s1)) != SSD_OK) return st;
-  if ((st = check_scan_desc(&pl->f2, &s2)) != SSD_OK) return st;
-  if ((st = check_scan_desc(&pl->r3, &s3)) != SSD_OK) return st;
   if (sf.chain || s1.chain) return SSD_ERR_UNSUPPORTED;   // float32 scans are phased
-  size_t ws = sf.ws_total;
-  if (s2.ws_total > ws) ws = s2.ws_total;
-  if (s3.ws_total > ws) ws = s3.ws_total;
-  pl->scan_ws = ws;
+  pl->scan_ws = sf.ws_total;
   pl->scan_ws_r1 = s1.ws_total;
   pl->fwd_cb_off = sf.ws_state_bytes + sf.ws_alpha_bytes;
-  const size_t es = io_size(d->io_dtype);
+
+  const int64_t Bt = d->batch, T = d->seqlen, H = d->nheads, G = d->ngroups, N = d->dstate;
+  const int64_t hpg = H / G;
+  pl->NB = (int32_t)((d->chunk + 63) / 64);
+  pl->LP = 64 * pl->NB;
+  pl->NS = N > 64 ? (int32_t)(N / 64) : 1;
+  const int64_t nbt = (int64_t)pl->NB * (pl->NB + 1) / 2;
+  const int64_t bcg = Bt * Nc * G;
+  head_split(hpg, bcg * nbt, 768, &pl->HS, &pl->hpw);
+  head_split(hpg, bcg * 2 * pl->NS * pl->NB, 512, &pl->HSD, &pl->hpwd);
+
   const bool bf = d->io_dtype == SSD_BF16;
   const size_t nx = (size_t)s0.n_x, nbc = (size_t)s0.n_bc, nst = (size_t)s0.n_state;
-  const size_t ndt = (size_t)s0.n_dt, nxn = (size_t)s2.n_x;      // [Bt,T,H,N]
+  const size_t ndt = (size_t)s0.n_dt;
   const size_t nx1 = (size_t)s1.n_x, nbc1 = (size_t)s1.n_bc, ndt1 = (size_t)s1.n_dt;  // R1, padded
-  const size_t bh = (size_t)(d->batch * d->nheads);
+  const size_t LP = (size_t)pl->LP, NB = (size_t)pl->NB;
   size_t sizes[kNumRegions];
-  sizes[kScanWs] = ws;
+  sizes[kScanWs] = pl->scan_ws;
   sizes[kScanWsR1] = pl->scan_ws_r1;
-  sizes[kY] = nx * 4;
-  sizes[kFinal] = nst * 4;
   sizes[kWd] = ndt * 4;
-  sizes[kDtr] = ndt * 4;
+  sizes[kCum] = ndt * 8;
   sizes[kDtr1] = ndt1 * 4;
   sizes[kR1x] = nx1 * 4;
   sizes[kR1b] = nbc1 * 4;
@@ -302,18 +311,14 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   sizes[kR1h0] = nst * 4;
   sizes[kR1y] = nx1 * 4;
   sizes[kR1final] = nst * 4;
-  sizes[kF2x] = nxn * es;
-  sizes[kF2h0] = nst * 4;
-  sizes[kF2y] = nxn * es;
-  sizes[kR3x] = nxn * es;
-  sizes[kR3b] = nx * es;
-  sizes[kR3c] = nx * es;
-  sizes[kR3h0] = nst * 4;
-  sizes[kR3y] = nxn * es;
+  sizes[kMix] = (size_t)bcg * pl->HS * LP * LP * 4;
+  sizes[kQrow] = (size_t)(Bt * Nc * H) * NB * NB * 128 * 4;
+  sizes[kQcol] = sizes[kQrow];
+  sizes[kUv] = 2 * (size_t)pl->NS * ndt * 4;
+  sizes[kDbcPart] = pl->HSD > 1 ? 2 * (size_t)pl->HSD * nbc * 4 : 0;
   sizes[kDdin] = ndt * 4;
-  sizes[kDlda] = ndt * 4;
   sizes[kDdp] = ndt * 4;
-  sizes[kPart] = 3 * bh * 4;
+  sizes[kPart] = 3 * (size_t)(Bt * Nc * H) * 4;
   sizes[kX32] = bf ? nx * 4 : 0;
   sizes[kB32] = bf ? nbc * 4 : 0;
   sizes[kC32] = bf ? nbc * 4 : 0;
@@ -533,53 +538,43 @@ ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* d, const void* x, const 
   char* w = static_cast<char*>(workspace);
   auto at = [&](int k) { return static_cast<void*>(w + pl.off[k]); };
   auto atf = [&](int k) { return reinterpret_cast<float*>(w + pl.off[k]); };
-  void* scan_ws = at(kScanWs);
 
   ssd::BwdArgs a;
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
   a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state;
-  a.y = atf(kY); a.fwd_final = atf(kFinal);
   const bool bf = d->io_dtype == SSD_BF16;
   a.x32 = bf ? atf(kX32) : nullptr; a.b32 = bf ? atf(kB32) : nullptr;
   a.c32 = bf ? atf(kC32) : nullptr;
-  a.wd = atf(kWd); a.dtr = atf(kDtr); a.dtr1 = atf(kDtr1);
+  a.wd = atf(kWd); a.cum = reinterpret_cast<double*>(w + pl.off[kCum]); a.dtr1 = atf(kDtr1);
   a.r1_x = atf(kR1x); a.r1_b = atf(kR1b); a.r1_c = atf(kR1c); a.r1_h0 = atf(kR1h0);
   a.r1_y = atf(kR1y); a.r1_final = atf(kR1final);
-  a.f2_x = at(kF2x); a.f2_h0 = atf(kF2h0); a.f2_y = at(kF2y);
-  a.r3_x = at(kR3x); a.r3_b = at(kR3b); a.r3_c = at(kR3c); a.r3_h0 = atf(kR3h0);
-  a.r3_y = at(kR3y);
-  a.ddin = atf(kDdin); a.dlda = atf(kDlda); a.dDp = atf(kDdp); a.part = atf(kPart);
   a.fwd_state = atf(kScanWs);
   a.fwd_cb = reinterpret_cast<const float*>(w + pl.off[kScanWs] + pl.fwd_cb_off);
   a.r1_state = atf(kScanWsR1);
+  a.mix = atf(kMix); a.qrow = atf(kQrow); a.qcol = atf(kQcol); a.uv = atf(kUv);
+  a.dbc_part = pl.HSD > 1 ? atf(kDbcPart) : nullptr;
+  a.ddin = atf(kDdin); a.dDp = atf(kDdp); a.part = atf(kPart);
   a.dx = dx; a.ddt = ddt; a.dA = dA; a.dB = dB; a.dC = dC; a.dD = dD;
   a.ddt_bias_out = ddt_bias; a.dh0 = dinitial_state;
   a.Bt = d->batch; a.T = d->seqlen; a.H = d->nheads; a.G = d->ngroups;
   a.L = d->chunk; a.Nc = s.Nc; a.pad = pl.pad;
   a.P = (int32_t)d->headdim; a.N = (int32_t)d->dstate;
+  a.NB = pl.NB; a.LP = pl.LP; a.HS = pl.HS; a.hpw = pl.hpw; a.HSD = pl.HSD; a.hpwd = pl.hpwd;
+  a.NS = pl.NS;
   a.softplus = d->dt_softplus ? 1 : 0;
   a.dt_min = d->dt_min; a.dt_max = d->dt_max;
 
   if (ssd::launch_backward_phase(a, bf, 0, stream) != hipSuccess) return SSD_ERR_HIP;
-  // forward in float32: y and the final state
-  st = ssd_chunk_scan(&pl.fw, bf ? a.x32 : x, dt, dt_bias, A, bf ? a.b32 : B, bf ? a.c32 : C, D,
-                      initial_state, at(kY), atf(kFinal), scan_ws, pl.scan_ws, stream);
+  // forward states in float32: C B^T and the state entering each chunk
+  st = scan_impl(&pl.fw, bf ? a.x32 : x, dt, dt_bias, A, bf ? a.b32 : B, bf ? a.c32 : C, D,
+                 initial_state, nullptr, nullptr, at(kScanWs), pl.scan_ws, stream, nullptr, 0,
+                 true);
   if (st != SSD_OK) return st;
   // R1: sum_n G B over reversed time; its final state is dL/dh_{-1} / abar_0
   st = ssd_chunk_scan(&pl.r1, a.r1_x, a.dtr1, nullptr, A, a.r1_b, a.r1_c, nullptr, a.r1_h0,
                       at(kR1y), atf(kR1final), at(kScanWsR1), pl.scan_ws_r1, stream);
   if (st != SSD_OK) return st;
   if (ssd::launch_backward_phase(a, bf, 1, stream) != hipSuccess) return SSD_ERR_HIP;
-  // F2: sum_p dy h (input B per head, B'' = x, C'' = dy)
-  st = ssd_chunk_scan(&pl.f2, a.f2_x, dt, dt_bias, A, x, dy, nullptr,
-                      initial_state ? a.f2_h0 : nullptr, at(kF2y), nullptr, scan_ws, pl.scan_ws,
-                      stream);
-  if (st != SSD_OK) return st;
-  // R3: sum_p G x over reversed time (input C / Delta' per head, B''' = dy, C''' = x)
-  st = ssd_chunk_scan(&pl.r3, a.r3_x, a.dtr, nullptr, A, a.r3_b, a.r3_c, nullptr, a.r3_h0,
-                      at(kR3y), nullptr, scan_ws, pl.scan_ws, stream);
-  if (st != SSD_OK) return st;
-  if (ssd::launch_backward_phase(a, bf, 2, stream) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;
 }
 

@@ -1,35 +1,41 @@
-// Gradients of the chunked scan for gfx950: the element-wise, transform and
-// reduction kernels around the scans that ssd_chunk_scan_backward runs.
+// Gradients of the chunked scan for gfx950 (ssd_chunk_scan_backward): the
+// kernels around the two float32 scans the host runs.
 //
 // Source: "Compiler-First State Space Duality and Portable O(1)
 // Autoregressive Caching", Background (Eq. 2-3: the recurrence and its
 // chunked dual form) and Implementation (softplus and clip on Delta).
 //
-// The adjoint G_t = dL/dh_t of h_t = abar_t h_{t-1} + d_t x_t (x) B_t,
-// y_t = h_t C_t + D x_t runs backwards in time:
-//   G_t = dy_t (x) C_t + abar_{t+1} G_{t+1},   G_{T-1} = dfinal + dy_{T-1} (x) C_{T-1}.
-// Every product of G with B_t or x_t is therefore the same chunked scan run
-// over reversed time, with the decay of step t+1 at reversed position T-1-t
-// and the input divided by that decay step's Delta (the scan multiplies its
-// input by its Delta).  The host launches:
-//   forward F0 in float32 (the entering states H_c and C B^T stay in its workspace)
-//   scan R1 (reversed, float32): input dy/Delta', B' = C, C' = B  -> sum_n G[p,n] B_t[n];
-//        pad = Nc L - T empty leading positions align its chunks with F0's, so that
-//        its entering states are G at the forward chunk boundaries
-//   scan F2 (forward):   input B (per head), B'' = x, C'' = dy   -> sum_p dy_t[p] h_t[p,n]
-//   scan R3 (reversed):  input C/Delta', B''' = dy, C''' = x     -> sum_p G[p,n] x_t[p]
-// and these kernels form the rest:
-//   dx_t = d_t (R1)_t + D dy_t;  dB = sum over a group's heads of d_t (R3)_t;
-//   dC = sum over a group's heads of (F2)_t;  dD = sum_t dy_t . x_t;
-//   dL/d(d_t A) = abar_t sum_{p,n} G_t h_{t-1}, per forward chunk c (token t,
-//   chunk-local cumulative log-decay cum, in double):
-//     sum_{i >= t > j in c} Q_ij                 Q_ij = (dy_i.x_j)(C_i.B_j) e^{cum_i - cum_j} d_j
-//   + sum_{i >= t in c} e^{cum_i} dy_i . (C_i H_c^T)
-//   + sum_{j < t in c} d_j e^{cum_last - cum_j} x_j . (B_j Ghat_c^T)
-//   + e^{cum_last} <Ghat_c, H_c>,                Ghat_c = dL/dh at the end of chunk c
-//   (no term of this sum cancels against another across the sequence);
-//   dd_t = A dL/d(d_t A) + x_t . (R1)_t;  ddt_t = dd_t softplus'(z_t) where Delta
-//   is not clipped;  dA = sum_t d_t dL/d(d_t A);  dh0 = abar_0 (final state of R1).
+// Per (b, h), with Delta d_t, a_t = d_t A, abar_t = e^{a_t}, the recurrence
+// h_t = abar_t h_{t-1} + d_t x_t (x) B_t, y_t = h_t C_t + D x_t has the adjoint
+//   G_t = dL/dh_t = dy_t (x) C_t + abar_{t+1} G_{t+1},  G_{T-1} = dfinal + dy_{T-1} (x) C_{T-1}.
+// In forward chunk c (local tokens i, j; cum = chunk-local inclusive prefix
+// sum of a; H_c = state entering the chunk; Ghat_c = abar of the next
+// chunk's first token times G there, dfinal for the last chunk):
+//   h_i = e^{cum_i} H_c + sum_{j<=i} e^{cum_i - cum_j} d_j x_j (x) B_j
+//   G_j = sum_{i>=j} e^{cum_i - cum_j} dy_i (x) C_i + e^{cum_last - cum_j} Ghat_c
+// The gradients, with M^h_ij = (dy_i . x_j) e^{cum_i - cum_j} d_j for j <= i
+// and M = sum of M^h over a group's heads (the heads share B and C, so the
+// products with B and C are taken once per group):
+//   dx_j = d_j G_j B_j + D dy_j                       (G_j B_j from R1, below)
+//   dC_i = sum_{j<=i} M_ij B_j + sum_h e^{cum_i} dy_i H_c
+//   dB_j = sum_{i>=j} M_ij C_i + sum_h d_j e^{cum_last - cum_j} x_j Ghat_c
+//   dL/da_t = sum_{i>=t>j} Q_ij + sum_{i>=t} u_i + sum_{j<t} v_j + e^{cum_last} <Ghat_c, H_c>
+//     Q_ij = M^h_ij (C_i . B_j),  u_i = C_i . (e^{cum_i} dy_i H_c),
+//     v_j = B_j . (d_j e^{cum_last - cum_j} x_j Ghat_c)
+//   (sums inside the chunk only: no term cancels against another across the sequence)
+//   dd_t = A dL/da_t + x_t . (G_t B_t),  ddt_t = dd_t softplus'(z_t) where Delta is not clipped,
+//   dA = sum_t d_t dL/da_t,  dD = sum_t dy_t . x_t,  dh0 = abar_0 G_0.
+// The host runs the forward scan's state phases in float32 (H_c and C B^T
+// stay in its workspace) and R1, the scan itself over reversed time: reversed
+// position T-1-t has the decay of step t+1 and the input dy_t / d_{t+1} (the
+// scan multiplies its input by its Delta), with B and C exchanged, so its
+// outputs are G_t B_t and its entering states the G at chunk boundaries; pad =
+// Nc L - T empty leading positions align its chunks with the forward ones.
+//
+// Matrix-core tiles: v_mfma_f32_16x16x4_f32, lane l holds A[l%16][k],
+// B[k][l%16] and D[4(l/16)+r][l%16]; the contraction index of four
+// consecutive instructions is k = 16 blk + 4 (l/16) + e, e = 0..3, so each
+// lane reads one float4 of a row-major operand per four instructions.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -38,17 +44,87 @@ namespace {
 
 constexpr int kBwdThreads = 256;
 
-template <typename T>
-__device__ __forceinline__ T io_of(float v) { return to_io<T>(v); }
-
 __device__ __forceinline__ float delta_at(const BwdArgs& a, int64_t b, int64_t t, int64_t h) {
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   return delta_of(a.dt[(b * a.T + t) * a.H + h] + bias, a.softplus, a.dt_min, a.dt_max);
 }
 
-// One wavefront per (b, t, h) row: Delta, the reversed Delta', and the
-// reversed / replicated / rescaled inputs of the three scans.  The pad
-// positions of R1 are zeroed by k_bwd_zero_pad.
+__device__ __forceinline__ int chunk_tokens(const BwdArgs& a, int64_t c) {
+  const int64_t t0 = c * a.L;
+  return (int)(a.T - t0 < a.L ? a.T - t0 : a.L);
+}
+
+template <typename T>
+__device__ __forceinline__ float4 ld4_io(const T* p, bool ok) {
+  if constexpr (sizeof(T) == 4) {
+    return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
+    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+  }
+}
+
+// KK consecutive elements (KK = 1, 2 or 4; aligned to KK elements) as float32.
+template <int KK, typename T>
+__device__ __forceinline__ void ldk(const T* p, bool ok, float (&v)[KK]) {
+  if constexpr (KK == 4) {
+    const float4 f = ld4_io<T>(p, ok);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else if constexpr (KK == 2) {
+    if constexpr (sizeof(T) == 4) {
+      const float2 f = ok ? *reinterpret_cast<const float2*>(p) : make_float2(0.f, 0.f);
+      v[0] = f.x; v[1] = f.y;
+    } else {
+      v[0] = ok ? to_f32(p[0]) : 0.f;
+      v[1] = ok ? to_f32(p[1]) : 0.f;
+    }
+  } else {
+    v[0] = ok ? to_f32(p[0]) : 0.f;
+  }
+}
+
+__device__ __forceinline__ f32x4 mma(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma4(float4 a, float4 b, f32x4 c) {
+  c = mma(a.x, b.x, c);
+  c = mma(a.y, b.y, c);
+  c = mma(a.z, b.z, c);
+  return mma(a.w, b.w, c);
+}
+
+// Inclusive prefix sum over the 256 threads of a workgroup (fixed order).
+__device__ __forceinline__ float block_inclusive_scan(float v, float* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float inc = wave_inclusive_scan(v);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  float before = 0.0f;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  __syncthreads();
+  return inc + before;
+}
+
+// Sum over the 256 threads of a workgroup (fixed order), returned to all.
+__device__ __forceinline__ float block_sum(float v, float* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = group_sum(v, 64);
+  if (lane == 0) wsum[wave] = v;
+  __syncthreads();
+  const float s = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  __syncthreads();
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Phase 0
+// ---------------------------------------------------------------------------
+
+// One wavefront per (b, t, h) row: Delta, R1's Delta' and reversed operands,
+// and the float32 copies of bfloat16 inputs for the state scan.  R1's pad
+// positions are zeroed by k_bwd_zero_pad.
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep(BwdArgs a) {
   const uint32_t row32 = blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
@@ -58,19 +134,15 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep(BwdArgs a) {
   const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T, hpg32 = (uint32_t)(a.H / a.G);
   const uint32_t bt32 = row32 / H32;
   const int64_t row = row32, h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
-  const int64_t hpg = hpg32, g = (uint32_t)h / hpg32;
-  const int64_t tr = a.T - 1 - t;                     // reversed position of token t (R3)
-  const int64_t T1 = a.T + a.pad, tr1 = a.pad + tr;    // R1: after pad empty positions
+  const int64_t g = (uint32_t)h / hpg32;
+  const int64_t T1 = a.T + a.pad, tr1 = a.pad + (a.T - 1 - t);   // R1 position of token t
   const int P = a.P, N = a.N;
   const float d = delta_at(a, b, t, h);
   const bool has_next = t + 1 < a.T;
   const float dn = has_next ? delta_at(a, b, t + 1, h) : 1.0f;
   if (lane == 0) {
     a.wd[row] = d;
-    // Delta' at reversed position T - t is d_t (positions 1..T-1); position 0 gets 0
-    if (t >= 1) a.dtr[(b * a.T + (a.T - t)) * a.H + h] = d;
-    else a.dtr[(b * a.T + 0) * a.H + h] = 0.0f;
-    // R1: the same one position later than its pad; the pad and its first position get 0
+    // Delta' at R1 position pad + T - t is d_t (t >= 1); the pad and position pad get 0
     if (t >= 1) a.dtr1[(b * T1 + (a.pad + a.T - t)) * a.H + h] = d;
     else
       for (int64_t k = 0; k <= a.pad; ++k) a.dtr1[(b * T1 + k) * a.H + h] = 0.0f;
@@ -79,36 +151,41 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep(BwdArgs a) {
   const T* dy = reinterpret_cast<const T*>(a.dy);
   const T* Bm = reinterpret_cast<const T*>(a.B);
   const T* Cm = reinterpret_cast<const T*>(a.C);
-  const int64_t rp = ((b * a.T + t) * a.H + h) * P, rpr = ((b * a.T + tr) * a.H + h) * P;
-  const int64_t rpr1 = ((b * T1 + tr1) * a.H + h) * P;
-  const int64_t rn = ((b * a.T + t) * a.H + h) * N, rnr = ((b * a.T + tr) * a.H + h) * N;
-  const int64_t gn = ((b * a.T + t) * a.G + g) * N;
-  const int64_t gnr1 = ((b * T1 + tr1) * a.G + g) * N;
+  const int64_t rp = row * P, rpr1 = ((b * T1 + tr1) * a.H + h) * P;
   for (int p = lane; p < P; p += 64) {
-    const float v = to_f32(dy[rp + p]);
-    // input of R1 at reversed position T-1-t: dy_t / Delta_{t+1} (0 for t = T-1)
-    a.r1_x[rpr1 + p] = has_next ? v / dn : 0.0f;
-    reinterpret_cast<T*>(a.r3_b)[rpr + p] = dy[rp + p];
-    reinterpret_cast<T*>(a.r3_c)[rpr + p] = x[rp + p];
+    // input of R1 for token t: dy_t / Delta_{t+1} (0 for the last token)
+    a.r1_x[rpr1 + p] = has_next ? to_f32(dy[rp + p]) / dn : 0.0f;
     if (a.x32) a.x32[rp + p] = to_f32(x[rp + p]);
   }
-  for (int n = lane; n < N; n += 64) {
-    const T bv = Bm[gn + n], cv = Cm[gn + n];
-    reinterpret_cast<T*>(a.f2_x)[rn + n] = bv;
-    reinterpret_cast<T*>(a.r3_x)[rnr + n] = io_of<T>(has_next ? to_f32(cv) / dn : 0.0f);
-    if (h % hpg == 0) {
-      a.r1_b[gnr1 + n] = to_f32(cv);
-      a.r1_c[gnr1 + n] = to_f32(bv);
+  if ((uint32_t)h % hpg32 == 0) {
+    const int64_t gn = ((b * a.T + t) * a.G + g) * N;
+    const int64_t gnr1 = ((b * T1 + tr1) * a.G + g) * N;
+    for (int n = lane; n < N; n += 64) {
+      const float bv = to_f32(Bm[gn + n]), cv = to_f32(Cm[gn + n]);
+      a.r1_b[gnr1 + n] = cv;
+      a.r1_c[gnr1 + n] = bv;
       if (a.b32) {
-        a.b32[gn + n] = to_f32(bv);
-        a.c32[gn + n] = to_f32(cv);
+        a.b32[gn + n] = bv;
+        a.c32[gn + n] = cv;
       }
     }
   }
 }
 
-// Initial states of the reversed scans (dfinal + dy_{T-1} (x) C_{T-1}, as
-// [P][N] for R1 and [N][P] for R3) and of F2 (initial_state transposed).
+// The pad positions of R1 (reversed positions 0 .. pad-1) hold no token.
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_zero_pad(BwdArgs a, int64_t per_b) {
+  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+  if (e >= a.Bt * per_b) return;
+  const int64_t b = e / per_b, r = e % per_b;
+  const int64_t T1 = a.T + a.pad;
+  if (r < a.pad * a.H * a.P) a.r1_x[b * T1 * a.H * a.P + r] = 0.0f;
+  if (r < a.pad * a.G * a.N) {
+    a.r1_b[b * T1 * a.G * a.N + r] = 0.0f;
+    a.r1_c[b * T1 * a.G * a.N + r] = 0.0f;
+  }
+}
+
+// Initial state of R1: dfinal + dy_{T-1} (x) C_{T-1}.
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_init_states(BwdArgs a) {
   const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
@@ -119,15 +196,393 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_init_states(BwdArgs a) {
   const int64_t tl = a.T - 1;
   const float dyv = to_f32(reinterpret_cast<const T*>(a.dy)[((b * a.T + tl) * a.H + h) * P + p]);
   const float cv = to_f32(reinterpret_cast<const T*>(a.C)[((b * a.T + tl) * a.G + g) * N + n]);
-  const float v = __fmaf_rn(dyv, cv, a.dfinal ? a.dfinal[e] : 0.0f);
-  a.r1_h0[e] = v;
-  const int64_t et = (bh * N + n) * P + p;   // [b][h][n][p]
-  a.r3_h0[et] = v;
-  if (a.h0) a.f2_h0[et] = a.h0[e];
+  a.r1_h0[e] = __fmaf_rn(dyv, cv, a.dfinal ? a.dfinal[e] : 0.0f);
+}
+
+// Chunk-local inclusive prefix sum of Delta A, in double: one wavefront per
+// (b, c, h).  (Runs after k_bwd_prep, which writes Delta.)
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
+  const int64_t w = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= a.Bt * a.Nc * a.H) return;
+  const int64_t h = w % a.H, bc = w / a.H, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t t0 = c * a.L;
+  const int Lc = chunk_tokens(a, c);
+  const double Ah = (double)a.A[h];
+  double carry = 0.0;
+  for (int l0 = 0; l0 < Lc; l0 += 64) {
+    const int l = l0 + lane;
+    const int64_t row = (b * a.T + t0 + l) * a.H + h;
+    double v = l < Lc ? (double)a.wd[row] * Ah : 0.0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const double o = __shfl_up(v, off, 64);
+      if (lane >= off) v += o;
+    }
+    v += carry;
+    if (l < Lc) a.cum[row] = v;
+    carry = __shfl(v, 63, 64);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Phase 1
+// ---------------------------------------------------------------------------
+
+// One workgroup per (b, c, g, head split, 64x64 block (I, J) of the chunk's
+// token pairs, J <= I).  For each head of the split: S = dy_I x_J^T on the
+// matrix cores, M^h = S o e^{cum_i - cum_j} o d_j (j <= i), the block's part
+// of M = sum_h M^h, and the row and column sums of Q = M^h o C B^T (j < i)
+// over the block's halves.  Wavefront (wr, wc) owns rows 32 wr .. +31 and
+// columns 32 wc .. +31 of the block.  Nothing is shared between wavefronts:
+// every partial sum has one writer, and the consumers add them in a fixed
+// order.
+template <typename T, int P>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
+  constexpr int PB = P / 16 < 4 ? P / 16 : 4;   // 16-wide p blocks loaded per round
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int NB = a.NB, nbt = NB * (NB + 1) / 2;
+  int64_t u = blockIdx.x;
+  const int blk = (int)(u % nbt);
+  u /= nbt;
+  const int hs = (int)(u % a.HS);
+  u /= a.HS;
+  const int64_t g = u % a.G, bc = u / a.G, c = bc % a.Nc, b = bc / a.Nc;
+  int I = 0;
+  while ((I + 1) * (I + 2) / 2 <= blk) ++I;
+  const int J = blk - I * (I + 1) / 2;
+  const int64_t L = a.L, t0 = c * L;
+  const int Lc = chunk_tokens(a, c);
+  if (64 * I >= Lc) return;
+  const int64_t hpg = a.H / a.G;
+  const int64_t hb = g * hpg + (int64_t)hs * a.hpw;
+  const int64_t he = min(hb + (int64_t)a.hpw, (g + 1) * hpg);
+
+  int ia[2], jb[2];        // A-operand rows (dy) and B-operand / output columns (x)
+  int io[2][4];            // output rows
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    ia[s] = 64 * I + 32 * wr + 16 * s + r16;
+    jb[s] = 64 * J + 32 * wc + 16 * s + r16;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) io[s][r] = 64 * I + 32 * wr + 16 * s + 4 * q + r;
+  }
+  const int64_t xrs = a.H * P;
+  const T* xg = reinterpret_cast<const T*>(a.x) + (b * a.T + t0) * xrs;
+  const T* dyg = reinterpret_cast<const T*>(a.dy) + (b * a.T + t0) * xrs;
+  const double* cumg = a.cum + (b * a.T + t0) * a.H;
+  const float* wdg = a.wd + (b * a.T + t0) * a.H;
+
+  // C B^T of this lane's outputs where j < i (the products Q need), else 0
+  const float* cb = a.fwd_cb + ((b * a.Nc + c) * a.G + g) * L * L;
+  float cbv[2][2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = io[s][r], j = jb[v];
+        cbv[s][v][r] = (i < Lc && j < i) ? cb[(int64_t)i * L + j] : 0.0f;
+      }
+
+  f32x4 mv[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) mv[s][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t bch = (b * a.Nc + c) * a.H;
+#pragma unroll 1
+  for (int64_t h = hb; h < he; ++h) {
+    f32x4 sv[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int v = 0; v < 2; ++v) sv[s][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int pb0 = 0; pb0 < P / 16; pb0 += PB) {
+      float4 dv[2][PB], xv[2][PB];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int k = 0; k < PB; ++k) {
+          const int pp = 16 * (pb0 + k) + 4 * q;
+          dv[s][k] = ld4_io<T>(dyg + (int64_t)min(ia[s], Lc - 1) * xrs + h * P + pp, ia[s] < Lc);
+          xv[s][k] = ld4_io<T>(xg + (int64_t)min(jb[s], Lc - 1) * xrs + h * P + pp, jb[s] < Lc);
+        }
+#pragma unroll
+      for (int k = 0; k < PB; ++k)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int v = 0; v < 2; ++v) sv[s][v] = mfma4(dv[s][k], xv[v][k], sv[s][v]);
+    }
+    double ci[2][4], cj[2];
+    float dj[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ci[s][r] = cumg[(int64_t)min(io[s][r], Lc - 1) * a.H + h];
+      cj[s] = cumg[(int64_t)min(jb[s], Lc - 1) * a.H + h];
+      dj[s] = jb[s] < Lc ? wdg[(int64_t)jb[s] * a.H + h] : 0.0f;
+    }
+    float rowp[2][4], colp[2] = {0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        rowp[s][r] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int i = io[s][r], j = jb[v];
+          // causal mask selected before the exponential
+          const bool ok = i < Lc && j <= i;
+          const float e = ok ? fast_exp((float)(ci[s][r] - cj[v])) : 0.0f;
+          const float m = sv[s][v][r] * e * dj[v];
+          mv[s][v][r] += m;
+          const float qv = m * cbv[s][v][r];
+          rowp[s][r] += qv;
+          colp[v] += qv;
+        }
+      }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rowp[s][r] = group_sum(rowp[s][r], 16);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      colp[v] += __shfl_xor(colp[v], 16, 64);
+      colp[v] += __shfl_xor(colp[v], 32, 64);
+    }
+    const int64_t qo = (((bch + h) * NB + I) * NB + J) * 128;
+    if (r16 == 0) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.qrow[qo + 64 * wc + 32 * wr + 16 * s + 4 * q + r] = rowp[s][r];
+    }
+    if (q == 0) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v) a.qcol[qo + 64 * wr + 32 * wc + 16 * v + r16] = colp[v];
+    }
+  }
+  // this head split's part of M (zeros outside j <= i < Lc)
+  const int64_t LP = a.LP;
+  float* mp = a.mix + (((b * a.Nc + c) * a.G + g) * a.HS + hs) * LP * LP;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mp[(int64_t)io[s][r] * LP + jb[v]] = mv[s][v][r];
+}
+
+// One workgroup per (b, c, g, head split, role, column split, 64-row block):
+// role 0 forms dC for the block's tokens, role 1 dB, over NW = 16 KK of the
+// N state columns.  Wavefront w owns the block's rows 16 w .. +15; lane
+// (q, r16) holds outputs of rows 4q + r and columns KK r16 .. +KK-1 (the
+// KK accumulator tiles interleave their columns, so that the state rows are
+// read as KK-wide vectors).
+//   inter-chunk part, per head of the split: (scale_i row_i) . Z, with
+//     role 0: row = dy_i, scale = e^{cum_i}, Z = H_c;
+//     role 1: row = x_j, scale = d_j e^{cum_last - cum_j}, Z = Ghat_c;
+//     its dot with C_i (role 0) or B_j (role 1) is u_i or v_j (this split's columns);
+//   intra-chunk part (head split 0): M B (role 0, j <= i) or M^T C (role 1, i >= j).
+template <typename T, int P, int KK>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
+  constexpr int NW = 16 * KK;
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int NB = a.NB;
+  int64_t u = blockIdx.x;
+  const int rb = (int)(u % NB);
+  u /= NB;
+  const int ns = (int)(u % a.NS);
+  u /= a.NS;
+  const int role = (int)(u % 2);
+  u /= 2;
+  const int hsd = (int)(u % a.HSD);
+  u /= a.HSD;
+  const int64_t g = u % a.G, bc = u / a.G, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t L = a.L, t0 = c * L;
+  const int Lc = chunk_tokens(a, c);
+  if (64 * rb >= Lc) return;
+  const int N = a.N;
+  const int n0 = ns * NW + KK * r16;          // this lane's columns
+  const int ia = 64 * rb + 16 * wave + r16;   // A-operand row
+  const bool iok = ia < Lc;
+  const int iac = iok ? ia : Lc - 1;
+  int io[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) io[r] = 64 * rb + 16 * wave + 4 * q + r;
+  const int64_t grs = a.G * N;
+  const T* Bg = reinterpret_cast<const T*>(a.B) + ((b * a.T + t0) * a.G + g) * N;
+  const T* Cg = reinterpret_cast<const T*>(a.C) + ((b * a.T + t0) * a.G + g) * N;
+  const T* dotm = role ? Bg : Cg;
+  float dvec[4][KK];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    ldk<KK, T>(dotm + (int64_t)min(io[r], Lc - 1) * grs + n0, io[r] < Lc, dvec[r]);
+
+  f32x4 acc[KK];
+#pragma unroll
+  for (int k = 0; k < KK; ++k) acc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t hpg = a.H / a.G;
+  const int64_t hb = g * hpg + (int64_t)hsd * a.hpwd;
+  const int64_t he = min(hb + (int64_t)a.hpwd, (g + 1) * hpg);
+  const int64_t PN = (int64_t)P * N;
+  const int64_t BtT = a.Bt * a.T;
+  float* uvo = a.uv + ((int64_t)(role * a.NS + ns) * BtT + b * a.T + t0) * a.H;
+#pragma unroll 1
+  for (int64_t h = hb; h < he; ++h) {
+    const int64_t rowi = (b * a.T + t0 + iac) * a.H + h;
+    const double ci = a.cum[rowi];
+    const float* Z;
+    float scale;
+    const T* arow;
+    if (role == 0) {
+      Z = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
+      scale = iok ? fast_exp((float)ci) : 0.0f;
+      arow = reinterpret_cast<const T*>(a.dy) + rowi * P;
+    } else {
+      float gs = 1.0f;
+      if (c + 1 < a.Nc) {
+        Z = a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN;
+        gs = expf(a.wd[(b * a.T + t0 + L) * a.H + h] * a.A[h]);   // abar of the next chunk's first token
+      } else {
+        Z = a.dfinal ? a.dfinal + (b * a.H + h) * PN : nullptr;
+      }
+      const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
+      scale = iok ? gs * a.wd[rowi] * fast_exp((float)(clast - ci)) : 0.0f;
+      arow = reinterpret_cast<const T*>(a.x) + rowi * P;
+    }
+    f32x4 ah[KK];
+#pragma unroll
+    for (int k = 0; k < KK; ++k) ah[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (Z) {   // uniform
+#pragma unroll 2
+      for (int pb = 0; pb < P / 16; ++pb) {
+        float4 av = ld4_io<T>(arow + 16 * pb + 4 * q, true);
+        av.x *= scale; av.y *= scale; av.z *= scale; av.w *= scale;
+        float zv[4][KK];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ldk<KK, float>(Z + (int64_t)(16 * pb + 4 * q + e) * N + n0, true, zv[e]);
+#pragma unroll
+        for (int k = 0; k < KK; ++k) {
+          ah[k] = mma(av.x, zv[0][k], ah[k]);
+          ah[k] = mma(av.y, zv[1][k], ah[k]);
+          ah[k] = mma(av.z, zv[2][k], ah[k]);
+          ah[k] = mma(av.w, zv[3][k], ah[k]);
+        }
+      }
+    }
+    // u_i (role 0) or v_j (role 1) over this split's columns
+    float ds[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float s = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KK; ++k) s = __fmaf_rn(dvec[r][k], ah[k][r], s);
+      ds[r] = group_sum(s, 16);
+    }
+    if (r16 == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (io[r] < Lc) uvo[(int64_t)io[r] * a.H + h] = ds[r];
+    }
+#pragma unroll
+    for (int k = 0; k < KK; ++k) acc[k] += ah[k];
+  }
+
+  if (hsd == 0) {
+    const int64_t LP = a.LP, LP2 = LP * LP;
+    const float* mp = a.mix + ((b * a.Nc + c) * a.G + g) * (int64_t)a.HS * LP2;
+    const int kend = (Lc + 15) / 16;
+    if (role == 0) {
+      // dC_i += sum_{j <= i} M[i][j] B_j
+      const int kb1 = min(4 * (rb + 1), kend);
+#pragma unroll 1
+      for (int kb = 0; kb < kb1; ++kb) {
+        float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < a.HS; ++s) {
+          const float4 v =
+              *reinterpret_cast<const float4*>(mp + s * LP2 + (int64_t)ia * LP + 16 * kb + 4 * q);
+          m4.x += v.x; m4.y += v.y; m4.z += v.z; m4.w += v.w;
+        }
+        float bv[4][KK];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = 16 * kb + 4 * q + e;
+          ldk<KK, T>(Bg + (int64_t)min(j, Lc - 1) * grs + n0, j < Lc, bv[e]);
+        }
+#pragma unroll
+        for (int k = 0; k < KK; ++k) {
+          acc[k] = mma(m4.x, bv[0][k], acc[k]);
+          acc[k] = mma(m4.y, bv[1][k], acc[k]);
+          acc[k] = mma(m4.z, bv[2][k], acc[k]);
+          acc[k] = mma(m4.w, bv[3][k], acc[k]);
+        }
+      }
+    } else {
+      // dB_j += sum_{i >= j} M[i][j] C_i
+#pragma unroll 1
+      for (int kb = 4 * rb; kb < kend; ++kb) {
+        float m4[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < a.HS; ++s) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m4[e] += mp[s * LP2 + (int64_t)(16 * kb + 4 * q + e) * LP + ia];
+        }
+        float cv[4][KK];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 16 * kb + 4 * q + e;
+          ldk<KK, T>(Cg + (int64_t)min(i, Lc - 1) * grs + n0, i < Lc, cv[e]);
+        }
+#pragma unroll
+        for (int k = 0; k < KK; ++k) {
+          acc[k] = mma(m4[0], cv[0][k], acc[k]);
+          acc[k] = mma(m4[1], cv[1][k], acc[k]);
+          acc[k] = mma(m4[2], cv[2][k], acc[k]);
+          acc[k] = mma(m4[3], cv[3][k], acc[k]);
+        }
+      }
+    }
+  }
+
+  float* out = a.HSD > 1 ? a.dbc_part + (int64_t)(role * a.HSD + hsd) * BtT * a.G * N
+                         : (role ? a.dB : a.dC);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    if (io[r] >= Lc) continue;
+    float* o = out + ((b * a.T + t0 + io[r]) * a.G + g) * N + n0;
+    if constexpr (KK == 4) {
+      *reinterpret_cast<float4*>(o) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+    } else if constexpr (KK == 2) {
+      *reinterpret_cast<float2*>(o) = make_float2(acc[0][r], acc[1][r]);
+    } else {
+      o[0] = acc[0][r];
+    }
+  }
+}
+
+// dC, dB: sums over the head splits of their parts (fixed order).
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb_reduce(BwdArgs a) {
+  const int64_t n = a.Bt * a.T * a.G * a.N;
+  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+  if (e >= 2 * n) return;
+  const int role = e >= n ? 1 : 0;
+  const int64_t k = e - role * n;
+  float s = 0.0f;
+  for (int p = 0; p < a.HSD; ++p) s += a.dbc_part[(int64_t)(role * a.HSD + p) * n + k];
+  (role ? a.dB : a.dC)[k] = s;
 }
 
 // One wavefront per (b, t, h): dx, the input-scale part of the Delta gradient
-// (x . R1) and the per-token part of dD.
+// (x . G B) and the per-token part of dD.
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a) {
   const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
@@ -157,321 +612,95 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a) {
   }
 }
 
-// One workgroup per (b, h): the dt gradient and this (b, h)'s parts of dA,
-// ddt_bias and dD (block sums in a fixed order).
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dt(BwdArgs a) {
-  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float Ah = a.A[h];
-  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  __shared__ float red[3][kBwdThreads / 64];
-  float pA = 0.0f, pB = 0.0f, pD = 0.0f;
-  for (int64_t t = tid; t < a.T; t += kBwdThreads) {
-    const int64_t row = (b * a.T + t) * a.H + h;
-    const float da = a.dlda[row];
-    const float z = a.dt[row] + bias;
-    const float pre = a.softplus ? (fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)))) : z;
-    float gate = (pre >= a.dt_min && pre <= a.dt_max) ? 1.0f : 0.0f;
-    if (a.softplus) gate *= 1.0f / (1.0f + expf(-z));
-    const float g = __fmaf_rn(Ah, da, a.ddin[row]) * gate;
-    a.ddt[row] = g;
-    pA = __fmaf_rn(a.wd[row], da, pA);
-    pB += g;
-    pD += a.dDp[row];
-  }
-  pA = group_sum(pA, 64);
-  pB = group_sum(pB, 64);
-  pD = group_sum(pD, 64);
-  if (lane == 0) {
-    red[0][wave] = pA;
-    red[1][wave] = pB;
-    red[2][wave] = pD;
-  }
-  __syncthreads();
-  if (tid < 3) {
-    float s = 0.0f;
-    for (int w = 0; w < kBwdThreads / 64; ++w) s += red[tid][w];
-    a.part[tid * a.Bt * a.H + bh] = s;
-  }
-}
-
-// Inclusive prefix sum over the 256 threads of a workgroup (fixed order).
-__device__ __forceinline__ float block_inclusive_scan(float v, float* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float inc = wave_inclusive_scan(v);
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  float before = 0.0f;
-  for (int w = 0; w < wave; ++w) before += wsum[w];
-  __syncthreads();
-  return inc + before;
-}
-
-template <typename T>
-__device__ __forceinline__ float4 ld4_io(const T* p, bool ok) {
-  if constexpr (sizeof(T) == 4) {
-    return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-  } else {
-    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
-    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
-  }
-}
-
-__device__ __forceinline__ f32x4 mfma4(float4 a, float4 b, f32x4 c) {
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, c, 0, 0, 0);
-  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, c, 0, 0, 0);
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, c, 0, 0, 0);
-}
-
-// One workgroup per (b, forward chunk c, h): dL/d(Delta_t A) of the chunk's
-// tokens (the four terms in the header).  Matrix-core tiles (16x16x4 fp32,
-// lane l: A[l%16][k], B[k][l%16], D[4(l/16)+r][l%16], k = 16 blk + 4(l/16) + kk):
-//   dy x^T over P for Q, C H_c^T and B Ghat_c^T over N for the state terms.
-// Row sums of Q are kept per (row tile, column tile) and added in column
-// order; column sums are owned by one wavefront per column tile: the result
-// does not depend on scheduling.
-template <typename T, int P, int N>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dlda(BwdArgs a) {
-  constexpr int LMAX = kBwdThreads, NRT = LMAX / 16;
-  __shared__ double s_cum[LMAX];
-  __shared__ double s_dw[kBwdThreads / 64];
-  __shared__ float s_d[LMAX];
-  __shared__ float s_rowp[NRT][NRT][16];
-  __shared__ float s_col[LMAX], s_q[LMAX], s_r[LMAX];
+// One workgroup per (b, c, h), one token per thread (L <= 256): dL/da_t from
+// the block sums of Q and the per-token u, v (prefix and suffix sums within
+// the chunk), the dt gradient, and this chunk's parts of dA, ddt_bias, dD.
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
   __shared__ float s_w[kBwdThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, q = lane >> 4, r16 = lane & 15;
+  const int l = threadIdx.x;
   const int64_t u = blockIdx.x;
   const int64_t h = u % a.H, bc = u / a.H, c = bc % a.Nc, b = bc / a.Nc;
-  const int64_t g = h / (a.H / a.G);
   const int64_t L = a.L, t0 = c * L;
-  const int Lc = (int)(a.T - t0 < L ? a.T - t0 : L);
-  const int nrt = (Lc + 15) / 16;
-  const float Ah = a.A[h];
+  const int Lc = chunk_tokens(a, c);
+  const int NB = a.NB, nbc = (Lc + 63) / 64;
+  const bool ok = l < Lc;
+  const int64_t row = (b * a.T + t0 + (ok ? l : 0)) * a.H + h;
+  const int64_t BtT = a.Bt * a.T;
 
-  // Delta and the chunk's cumulative log-decay, in double
-  {
-    const float dv = tid < Lc ? a.wd[(b * a.T + t0 + tid) * a.H + h] : 0.0f;
-    s_d[tid] = dv;
-    double v = (double)dv * (double)Ah;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(v, off, 64);
-      if (lane >= off) v += o;
+  float dv = 0.0f, uu = 0.0f, vv = 0.0f;
+  if (ok) {
+    // R_t = sum_{s<t} (column sum of s below the diagonal - row sum of s left of it)
+    const int K = l >> 6, s = l & 63;
+    const float* qr = a.qrow + ((b * a.Nc + c) * a.H + h) * (int64_t)NB * NB * 128;
+    const float* qc = a.qcol + ((b * a.Nc + c) * a.H + h) * (int64_t)NB * NB * 128;
+    float rs = 0.0f, cs = 0.0f;
+    for (int Jb = 0; Jb <= K; ++Jb) rs += qr[(K * NB + Jb) * 128 + s] + qr[(K * NB + Jb) * 128 + 64 + s];
+    for (int Ib = K; Ib < nbc; ++Ib) cs += qc[(Ib * NB + K) * 128 + s] + qc[(Ib * NB + K) * 128 + 64 + s];
+    dv = cs - rs;
+    for (int ns = 0; ns < a.NS; ++ns) {
+      uu += a.uv[((int64_t)ns * BtT + b * a.T + t0 + l) * a.H + h];
+      vv += a.uv[((int64_t)(a.NS + ns) * BtT + b * a.T + t0 + l) * a.H + h];
     }
-    if (lane == 63) s_dw[wave] = v;
-    __syncthreads();
-    double before = 0.0;
-    for (int w = 0; w < wave; ++w) before += s_dw[w];
-    s_cum[tid] = v + before;
-    s_col[tid] = 0.0f;
-    s_q[tid] = 0.0f;
-    s_r[tid] = 0.0f;
   }
-  __syncthreads();
-  const double cum_last = s_cum[Lc - 1];
+  const float inc_d = block_inclusive_scan(dv, s_w);
+  const float inc_v = block_inclusive_scan(vv, s_w);
+  const float inc_u = block_inclusive_scan(uu, s_w);
+  const float tot_u = block_sum(uu, s_w);
 
-  const T* xg = reinterpret_cast<const T*>(a.x) + ((b * a.T + t0) * a.H + h) * P;
-  const T* dyg = reinterpret_cast<const T*>(a.dy) + ((b * a.T + t0) * a.H + h) * P;
-  const T* Bg = reinterpret_cast<const T*>(a.B) + ((b * a.T + t0) * a.G + g) * N;
-  const T* Cg = reinterpret_cast<const T*>(a.C) + ((b * a.T + t0) * a.G + g) * N;
-  const int64_t xrs = a.H * P, brs = a.G * N;
-
-  // ---- Q_ij, i > j: row sums per (I, J) tile, column sums per column tile ----
-  const float* S = a.fwd_cb + ((b * a.Nc + c) * a.G + g) * L * L;
-  for (int J = wave; J < nrt; J += kBwdThreads / 64) {
-    const int j = 16 * J + r16;
-    const bool jok = j < Lc;
-    const float dj = jok ? s_d[j] : 0.0f;
-    const double cj = s_cum[jok ? j : 0];
-    // this lane's x row (column j of the tiles), loaded once for the column tile
-    float4 xr[P / 16];
-#pragma unroll
-    for (int pb = 0; pb < P / 16; ++pb)
-      xr[pb] = ld4_io<T>(xg + (jok ? j : Lc - 1) * xrs + 16 * pb + 4 * q, jok);
-    float colacc = 0.0f;
-    for (int I = J; I < nrt; ++I) {
-      const int ia = 16 * I + r16;
-      float4 dr[P / 16];
-#pragma unroll
-      for (int pb = 0; pb < P / 16; ++pb)
-        dr[pb] = ld4_io<T>(dyg + (ia < Lc ? ia : Lc - 1) * xrs + 16 * pb + 4 * q, ia < Lc);
-      float sv[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = 16 * I + 4 * q + rr;
-        sv[rr] = (jok && i > j && i < Lc) ? S[(int64_t)i * L + j] : 0.0f;
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pb = 0; pb < P / 16; ++pb) acc = mfma4(dr[pb], xr[pb], acc);
-      float colpart = 0.0f;
-      float rowv[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = 16 * I + 4 * q + rr;
-        float qv = 0.0f;
-        if (jok && i > j && i < Lc) {
-          const float dec = expf((float)(s_cum[i] - cj));
-          qv = acc[rr] * sv[rr] * dec * dj;
-        }
-        rowv[rr] = qv;
-        colpart += qv;
-      }
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) rowv[rr] = group_sum(rowv[rr], 16);
-      if (r16 == 0) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s_rowp[I][J][4 * q + rr] = rowv[rr];
-      }
-      colpart += __shfl_xor(colpart, 16, 64);
-      colpart += __shfl_xor(colpart, 32, 64);
-      colacc += colpart;
-    }
-    if (q == 0 && jok) s_col[j] = colacc;
-  }
-
-  // ---- state terms: C H_c^T against dy, B Ghat_c^T against x ----
-  constexpr int64_t PN = (int64_t)P * N;
+  // e^{cum_last} <Ghat_c, H_c>
+  const int64_t PN = (int64_t)a.P * a.N;
   const float* Hc = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
   const float* Gh = nullptr;
   float gs = 1.0f;
   if (c + 1 < a.Nc) {
     Gh = a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN;
-    gs = expf(a.wd[(b * a.T + t0 + L) * a.H + h] * Ah);   // abar of the next chunk's first token
+    gs = expf(a.wd[(b * a.T + t0 + L) * a.H + h] * a.A[h]);
   } else if (a.dfinal) {
     Gh = a.dfinal + (b * a.H + h) * PN;
   }
-  for (int I = wave; I < nrt; I += kBwdThreads / 64) {
-    const int ia = 16 * I + r16;
-    const bool iok = ia < Lc;
-    // this lane's C and B rows (row i = 16 I + r16), loaded once for all p tiles
-    float4 cr[N / 16], br[N / 16];
-#pragma unroll
-    for (int nb = 0; nb < N / 16; ++nb) {
-      cr[nb] = ld4_io<T>(Cg + (iok ? ia : Lc - 1) * brs + 16 * nb + 4 * q, iok);
-      br[nb] = ld4_io<T>(Bg + (iok ? ia : Lc - 1) * brs + 16 * nb + 4 * q, iok);
-    }
-    float qp[4] = {0.f, 0.f, 0.f, 0.f}, rp[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int pt = 0; pt < P / 16; ++pt) {
-      f32x4 ay = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
-      const float* hrow = Hc + (16 * pt + r16) * N + 4 * q;
-#pragma unroll
-      for (int nb = 0; nb < N / 16; ++nb)
-        ay = mfma4(cr[nb], *reinterpret_cast<const float4*>(hrow + 16 * nb), ay);
-      if (Gh) {
-        const float* grow = Gh + (16 * pt + r16) * N + 4 * q;
-#pragma unroll
-        for (int nb = 0; nb < N / 16; ++nb)
-          ag = mfma4(br[nb], *reinterpret_cast<const float4*>(grow + 16 * nb), ag);
-      }
-      // lane holds rows i = 16 I + 4 q + rr, column p = 16 pt + r16
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = 16 * I + 4 * q + rr;
-        if (i < Lc) {
-          qp[rr] = __fmaf_rn(ay[rr], to_f32(dyg[(int64_t)i * xrs + 16 * pt + r16]), qp[rr]);
-          rp[rr] = __fmaf_rn(ag[rr], to_f32(xg[(int64_t)i * xrs + 16 * pt + r16]), rp[rr]);
-        }
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      qp[rr] = group_sum(qp[rr], 16);
-      rp[rr] = group_sum(rp[rr], 16);
-    }
-    if (r16 == 0) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int i = 16 * I + 4 * q + rr;
-        if (i < Lc) {
-          s_q[i] = (float)exp(s_cum[i]) * qp[rr];
-          s_r[i] = s_d[i] * gs * (float)exp(cum_last - s_cum[i]) * rp[rr];
-        }
-      }
-    }
-  }
-  // s_c = e^{cum_last} <Ghat_c, H_c>
   float sc = 0.0f;
   if (Gh)
-    for (int e = tid; e < P * N; e += kBwdThreads) sc = __fmaf_rn(Gh[e], Hc[e], sc);
-  sc = group_sum(sc, 64);
-  if (lane == 0) s_w[wave] = sc;
-  __syncthreads();
-  float s_c = 0.0f;
-  for (int w = 0; w < kBwdThreads / 64; ++w) s_c += s_w[w];
-  s_c *= gs * (float)exp(cum_last);
-  __syncthreads();
+    for (int64_t e = l; e < PN; e += kBwdThreads) sc = __fmaf_rn(Gh[e], Hc[e], sc);
+  sc = block_sum(sc, s_w);
+  const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
+  sc *= gs * (float)exp(clast);
 
-  // ---- assemble: R_t = sum_{v<t} (col_v - row_v), suffix of q, prefix of r ----
-  const int l = tid;
-  float rowsum = 0.0f;
-  if (l < Lc) {
-    const int I = l >> 4;
-    for (int J = 0; J <= I; ++J) rowsum += s_rowp[I][J][l & 15];
+  float pA = 0.0f, pB = 0.0f, pD = 0.0f;
+  if (ok) {
+    const float da = (inc_d - dv) + (tot_u - (inc_u - uu)) + (inc_v - vv) + sc;
+    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+    const float z = a.dt[row] + bias;
+    const float pre = a.softplus ? (fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)))) : z;
+    float gate = (pre >= a.dt_min && pre <= a.dt_max) ? 1.0f : 0.0f;
+    if (a.softplus) gate *= 1.0f / (1.0f + expf(-z));
+    const float gd = __fmaf_rn(a.A[h], da, a.ddin[row]) * gate;
+    a.ddt[row] = gd;
+    pA = a.wd[row] * da;
+    pB = gd;
+    pD = a.dDp[row];
   }
-  const float dv = l < Lc ? s_col[l] - rowsum : 0.0f;
-  const float qv = s_q[l], rv = s_r[l];
-  const float inc_d = block_inclusive_scan(dv, s_w);
-  const float inc_q = block_inclusive_scan(qv, s_w);
-  const float inc_r = block_inclusive_scan(rv, s_w);
-  // totals: the last thread's inclusive sums
-  __shared__ float s_tot;
-  if (tid == kBwdThreads - 1) s_tot = inc_q;
-  __syncthreads();
-  if (l < Lc) {
-    const float R = inc_d - dv;                 // sum over v < t
-    const float Sq = s_tot - (inc_q - qv);      // sum over i >= t
-    const float Pr = inc_r - rv;                // sum over j < t
-    a.dlda[(b * a.T + t0 + l) * a.H + h] = R + Sq + Pr + s_c;
+  pA = block_sum(pA, s_w);
+  pB = block_sum(pB, s_w);
+  pD = block_sum(pD, s_w);
+  if (l == 0) {
+    const int64_t n = a.Bt * a.Nc * a.H, k = (b * a.Nc + c) * a.H + h;
+    a.part[k] = pA;
+    a.part[n + k] = pB;
+    a.part[2 * n + k] = pD;
   }
 }
 
-// The pad positions of R1 (reversed positions 0 .. pad-1) hold no token.
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_zero_pad(BwdArgs a, int64_t per_b) {
-  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
-  if (e >= a.Bt * per_b) return;
-  const int64_t b = e / per_b, r = e % per_b;
-  const int64_t T1 = a.T + a.pad;
-  if (r < a.pad * a.H * a.P) a.r1_x[b * T1 * a.H * a.P + r] = 0.0f;
-  if (r < a.pad * a.G * a.N) {
-    a.r1_b[b * T1 * a.G * a.N + r] = 0.0f;
-    a.r1_c[b * T1 * a.G * a.N + r] = 0.0f;
-  }
-}
-
-// dA, ddt_bias, dD: sums over the batch of the (b, h) parts (fixed order).
+// dA, ddt_bias, dD: sums over the batch and the chunks of the parts (fixed order).
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_reduce_heads(BwdArgs a) {
   const int64_t h = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
   if (h >= a.H) return;
+  const int64_t n = a.Bt * a.Nc;
   float s[3] = {0.0f, 0.0f, 0.0f};
-  for (int64_t b = 0; b < a.Bt; ++b)
-    for (int k = 0; k < 3; ++k) s[k] += a.part[k * a.Bt * a.H + b * a.H + h];
+  for (int64_t k = 0; k < n; ++k)
+    for (int m = 0; m < 3; ++m) s[m] += a.part[(m * n + k) * a.H + h];
   a.dA[h] = s[0];
   if (a.ddt_bias_out) a.ddt_bias_out[h] = s[1];
   if (a.dD) a.dD[h] = s[2];
-}
-
-// dB and dC: sums over a group's heads (fixed order) of d_t R3 and of F2.
-template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dbdc(BwdArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
-  const int N = a.N;
-  if (e >= a.Bt * a.T * a.G * N) return;
-  const int64_t n = e % N, btg = e / N, g = btg % a.G, bt = btg / a.G, t = bt % a.T, b = bt / a.T;
-  const int64_t hpg = a.H / a.G;
-  const int64_t tr = a.T - 1 - t;
-  const T* f2 = reinterpret_cast<const T*>(a.f2_y);
-  const T* r3 = reinterpret_cast<const T*>(a.r3_y);
-  float sb = 0.0f, sc = 0.0f;
-  for (int64_t h = g * hpg; h < (g + 1) * hpg; ++h) {
-    sc += to_f32(f2[((b * a.T + t) * a.H + h) * N + n]);
-    sb = __fmaf_rn(a.wd[(b * a.T + t) * a.H + h], to_f32(r3[((b * a.T + tr) * a.H + h) * N + n]), sb);
-  }
-  a.dB[e] = sb;
-  a.dC[e] = sc;
 }
 
 // dh0 = abar_0 * (final state of R1).
@@ -485,6 +714,27 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh0(BwdArgs a) {
 }
 
 inline unsigned blocks_of(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
+
+template <typename T, int P>
+hipError_t launch_mix_dcdb(const BwdArgs& a, hipStream_t s) {
+  const int64_t bcg = a.Bt * a.Nc * a.G;
+  const int64_t nbt = (int64_t)a.NB * (a.NB + 1) / 2;
+  hipLaunchKernelGGL((k_bwd_mix<T, P>), dim3((unsigned)(bcg * a.HS * nbt)), dim3(kBwdThreads), 0,
+                     s, a);
+  const dim3 grid((unsigned)(bcg * a.HSD * 2 * a.NS * a.NB));
+  switch (a.N) {
+    case 16: hipLaunchKernelGGL((k_bwd_dcdb<T, P, 1>), grid, dim3(kBwdThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((k_bwd_dcdb<T, P, 2>), grid, dim3(kBwdThreads), 0, s, a); break;
+    case 64:
+    case 128: hipLaunchKernelGGL((k_bwd_dcdb<T, P, 4>), grid, dim3(kBwdThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (a.HSD > 1)
+    hipLaunchKernelGGL(k_bwd_dcdb_reduce,
+                       dim3(blocks_of(2 * a.Bt * a.T * a.G * (int64_t)a.N, kBwdThreads)),
+                       dim3(kBwdThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
@@ -502,24 +752,23 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
       hipLaunchKernelGGL(k_bwd_init_states<T>,
                          dim3(blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads)),
                          dim3(kBwdThreads), 0, s, a);
+      hipLaunchKernelGGL(k_bwd_cum, dim3(blocks_of(a.Bt * a.Nc * a.H, kBwdThreads / 64)),
+                         dim3(kBwdThreads), 0, s, a);
       break;
     case 1: {
-      const dim3 grid((unsigned)(a.Bt * a.Nc * a.H));
-      hipError_t e = hipErrorInvalidValue;
-#define SSD_BWD_DLDA(PP, NN)                                                          \
-  if (a.P == PP && a.N == NN) {                                                       \
-    hipLaunchKernelGGL((k_bwd_dlda<T, PP, NN>), grid, dim3(kBwdThreads), 0, s, a);     \
-    e = hipSuccess;                                                                   \
-  }
-      SSD_BWD_DLDA(16, 16) SSD_BWD_DLDA(16, 32) SSD_BWD_DLDA(16, 64) SSD_BWD_DLDA(16, 128)
-      SSD_BWD_DLDA(32, 16) SSD_BWD_DLDA(32, 32) SSD_BWD_DLDA(32, 64) SSD_BWD_DLDA(32, 128)
-      SSD_BWD_DLDA(64, 16) SSD_BWD_DLDA(64, 32) SSD_BWD_DLDA(64, 64) SSD_BWD_DLDA(64, 128)
-      SSD_BWD_DLDA(128, 16) SSD_BWD_DLDA(128, 32) SSD_BWD_DLDA(128, 64) SSD_BWD_DLDA(128, 128)
-#undef SSD_BWD_DLDA
+      hipError_t e;
+      switch (a.P) {
+        case 16: e = launch_mix_dcdb<T, 16>(a, s); break;
+        case 32: e = launch_mix_dcdb<T, 32>(a, s); break;
+        case 64: e = launch_mix_dcdb<T, 64>(a, s); break;
+        case 128: e = launch_mix_dcdb<T, 128>(a, s); break;
+        default: e = hipErrorInvalidValue;
+      }
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(k_bwd_dx<T>, dim3(blocks_of(rows, kBwdThreads / 64)), dim3(kBwdThreads),
                          0, s, a);
-      hipLaunchKernelGGL(k_bwd_dt, dim3((unsigned)(a.Bt * a.H)), dim3(kBwdThreads), 0, s, a);
+      hipLaunchKernelGGL(k_bwd_assemble, dim3((unsigned)(a.Bt * a.Nc * a.H)), dim3(kBwdThreads),
+                         0, s, a);
       hipLaunchKernelGGL(k_bwd_reduce_heads, dim3(blocks_of(a.H, kBwdThreads)), dim3(kBwdThreads),
                          0, s, a);
       if (a.dh0)
@@ -527,10 +776,6 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
                            dim3(kBwdThreads), 0, s, a);
       break;
     }
-    case 2:
-      hipLaunchKernelGGL(k_bwd_dbdc<T>, dim3(blocks_of(a.Bt * a.T * a.G * (int64_t)a.N, kBwdThreads)),
-                         dim3(kBwdThreads), 0, s, a);
-      break;
     default:
       return hipErrorInvalidValue;
   }

@@ -27,6 +27,7 @@ struct ScanArgs {
   int32_t softplus;
   float dt_min, dt_max;
   int32_t chain;          // 1: chain schedule (bfloat16 only), 0: phased
+  int32_t states_only;    // 1: phases 0-2 only (C B^T, chunk and entering states; no y)
 };
 
 struct StepArgs {
@@ -57,8 +58,8 @@ struct ConvArgs {
   int32_t silu;
 };
 
-// Arguments of the element-wise, transform and reduction kernels of the
-// scan's backward pass (ssd_backward.hip).  Device pointers.
+// Arguments of the kernels of the scan's backward pass (ssd_backward.hip).
+// Device pointers.
 struct BwdArgs {
   // inputs of the forward scan and the cotangents
   const void* x;            // [Bt,T,H,P] io
@@ -71,39 +72,33 @@ struct BwdArgs {
   const float* h0;          // [Bt,H,P,N] or null
   const void* dy;           // [Bt,T,H,P] io
   const float* dfinal;      // [Bt,H,P,N] or null
-  // forward results (recomputed, float32)
-  const float* y;           // [Bt,T,H,P]
-  const float* fwd_final;   // [Bt,H,P,N]
-  // float32 copies of x, B, C for the float32 scans (bfloat16 io only, else null)
+  // float32 copies of x, B, C for the float32 state scan (bfloat16 io only, else null)
   float* x32;               // [Bt,T,H,P]
   float* b32;               // [Bt,T,G,N]
   float* c32;               // [Bt,T,G,N]
-  // workspace: Delta, the reversed Delta', and the three scans' operands and results
+  // Delta, its chunk-local prefix, and the operands and results of the reversed scan R1
   float* wd;                // [Bt,T,H] Delta
-  float* dtr;               // [Bt,T,H] Delta at reversed positions, shifted by one step (R3)
-  float* dtr1;              // [Bt,T+pad,H] the same after R1's pad positions
-  float* r1_x;              // [Bt,T+pad,H,P] f32 reversed dy / Delta'
-  float* r1_b;              // [Bt,T+pad,G,N] f32 reversed C
-  float* r1_c;              // [Bt,T+pad,G,N] f32 reversed B
+  double* cum;              // [Bt,T,H] sum of Delta A from the chunk start to the token (inclusive)
+  float* dtr1;              // [Bt,T+pad,H] Delta' of R1: d_t at reversed position pad+T-t
+  float* r1_x;              // [Bt,T+pad,H,P] reversed dy_t / Delta_{t+1}
+  float* r1_b;              // [Bt,T+pad,G,N] reversed C
+  float* r1_c;              // [Bt,T+pad,G,N] reversed B
   float* r1_h0;             // [Bt,H,P,N]     dfinal + dy_{T-1} (x) C_{T-1}
-  const float* r1_y;        // [Bt,T+pad,H,P] f32 sum_n G B (reversed positions)
+  const float* r1_y;        // [Bt,T+pad,H,P] sum_n G B (reversed positions)
   const float* r1_final;    // [Bt,H,P,N]     dL/dh_{-1} / abar_0
-  void* f2_x;               // [Bt,T,H,N] io  B per head
-  float* f2_h0;             // [Bt,H,N,P]     initial state transposed
-  const void* f2_y;         // [Bt,T,H,N] io  sum_p dy h
-  void* r3_x;               // [Bt,T,H,N] io  reversed C / Delta' per head
-  void* r3_b;               // [Bt,T,H,P] io  reversed dy
-  void* r3_c;               // [Bt,T,H,P] io  reversed x
-  float* r3_h0;             // [Bt,H,N,P]     (dfinal + dy_{T-1} (x) C_{T-1}) transposed
-  const void* r3_y;         // [Bt,T,H,N] io  sum_p G x (reversed positions)
   // entering states and C B^T tiles the float32 scans leave in their workspaces
   const float* fwd_state;   // [Bt,H,Nc,P,N] state entering forward chunk c (H_c)
   const float* fwd_cb;      // [Bt,Nc,G,L,L] C B^T of each forward chunk
   const float* r1_state;    // [Bt,H,Nc,P,N] state entering reversed chunk c' (G at (Nc-c')L)
+  // intermediate results
+  float* mix;               // [Bt,Nc,G,HS,LP,LP] per head split: sum_h (dy x^T) o decay o Delta_j
+  float* qrow;              // [Bt,Nc,H,NB,NB,2,64] row sums of the decay-gradient products
+  float* qcol;              // [Bt,Nc,H,NB,NB,2,64] column sums of the same
+  float* uv;                // [2][NS][Bt,T,H] per-token state terms of the decay gradient
+  float* dbc_part;          // [2][HSD][Bt,T,G,N] head-split parts of dC, dB (HSD > 1)
   float* ddin;              // [Bt,T,H]  x_t . (sum_n G B)
-  float* dlda;              // [Bt,T,H]  dL/d(Delta_t A)
   float* dDp;               // [Bt,T,H]  dy_t . x_t
-  float* part;              // [3][Bt,H] parts of dA, ddt_bias, dD
+  float* part;              // [3][Bt,Nc,H] parts of dA, ddt_bias, dD
   // gradients
   float* dx;                // [Bt,T,H,P]
   float* ddt;               // [Bt,T,H]
@@ -117,6 +112,10 @@ struct BwdArgs {
   int64_t L, Nc;            // chunk and chunks of the forward partition
   int64_t pad;              // leading empty positions of the reversed scan R1 (Nc L - T)
   int32_t P, N;
+  int32_t NB, LP;           // 64-token blocks per chunk, and NB * 64
+  int32_t HS, hpw;          // head splits of the mix kernel and heads per split
+  int32_t HSD, hpwd;        // head splits of the dC/dB kernel and heads per split
+  int32_t NS;               // column splits of N in the dC/dB kernel
   int32_t softplus;
   float dt_min, dt_max;
 };
@@ -155,10 +154,9 @@ bool conv_width_supported(int64_t K);
 bool conv_shape_supported(int64_t Bt, int64_t T, int64_t D);
 hipError_t launch_conv(const ConvArgs& a, bool io_bf16, bool step, hipStream_t stream);
 
-// Backward pass pieces: phase 0 prepares the reversed / replicated operands
-// and initial states of the three scans, phase 1 (after the float32 forward
-// and reversed scans) forms dL/d(Delta A), dx, dt, dA, ddt_bias, dD and dh0,
-// phase 2 forms dB and dC.
+// Backward pass pieces: phase 0 prepares Delta, its chunk-local prefix and the
+// reversed operands and initial state of R1; phase 1 (after the float32
+// forward state scan and R1) forms every gradient.
 hipError_t launch_backward_phase(const BwdArgs& a, bool io_bf16, int phase, hipStream_t stream);
 hipError_t launch_backward_zero_heads(float* dA, float* ddt_bias, float* dD, int64_t H,
                                       hipStream_t stream);

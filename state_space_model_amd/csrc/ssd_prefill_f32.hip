@@ -540,8 +540,9 @@ hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
   // phase 2: inter-chunk recurrence
   if ((e = rec(2)) != hipSuccess) return e;
   if ((e = launch_state_pass(a, P, N, stream, false)) != hipSuccess) return e;
-  // phase 3: outputs
+  // phase 3: outputs (skipped when only the entering states are wanted)
   if ((e = rec(3)) != hipSuccess) return e;
+  if (a.states_only) return rec(4);
   constexpr int PW = P < 32 ? P : 32;
   const int64_t units3 = a.Bt * a.Nc * a.H * (P / PW);
   if (a.L <= 256)

@@ -298,9 +298,11 @@ def test_backward_workspace_and_errors():
     need = lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(d))
     assert need > lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(d))
     assert need % 256 == 0
-    # the exchanged form of the shape must be supported too
+    # chunks of at most 256 tokens (one token per thread of a 256-thread workgroup)
     assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(dstate=128, chunk=512, headdim=32))) == 0
-    assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(io_dtype=1, headdim=16, dstate=32))) == 0
+    assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(chunk=288))) == 0
+    assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(chunk=256))) > 0
+    assert lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc(io_dtype=1, headdim=16, dstate=32))) > 0
     assert bwd_status(desc(dstate=128, chunk=512, headdim=32)) == UNSUP
     assert bwd_status(desc(io_dtype=5)) == DTYPE
     assert bwd_status(d, dy=0) == INVALID

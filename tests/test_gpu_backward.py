@@ -72,6 +72,11 @@ CASES = [
     (2, 96, 4, 32, 64, 1, 32, "bf16"),
     (1, 200, 2, 64, 128, 1, 64, "bf16"),
     (1, 257, 4, 64, 128, 2, 256, "bf16"),
+    # chunks that end in a partial 64-token block, P = 128 with N = 16, P = 16 in bfloat16
+    (1, 250, 4, 128, 16, 2, 96, "f32"),
+    (2, 130, 8, 16, 32, 2, 160, "bf16"),
+    # 16 heads per group over 3 chunks: heads split over many workgroups
+    (1, 384, 16, 32, 64, 1, 128, "f32"),
 ]
 
 
