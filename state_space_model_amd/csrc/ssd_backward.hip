@@ -54,16 +54,22 @@ __device__ __forceinline__ int chunk_tokens(const BwdArgs& a, int64_t c) {
   return (int)(a.T - t0 < a.L ? a.T - t0 : a.L);
 }
 
+// Branch-free masked loads: `p` must be a valid address whether or not `ok`
+// (callers clamp rows to the chunk); the value is replaced by zeros when !ok.
+// A plain `ok ? load : 0` becomes one exec-masked branch, and a wait, per load.
 template <typename T>
 __device__ __forceinline__ float4 ld4_io(const T* p, bool ok) {
+  float4 v;
   if constexpr (sizeof(T) == 4) {
-    return ok ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+    v = *reinterpret_cast<const float4*>(p);
   } else {
-    if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
-    const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-    return make_float4((float)v[0], (float)v[1], (float)v[2], (float)v[3]);
+    const bf16x4 w = *reinterpret_cast<const bf16x4*>(p);
+    v = make_float4((float)w[0], (float)w[1], (float)w[2], (float)w[3]);
   }
+  return ok ? v : make_float4(0.f, 0.f, 0.f, 0.f);
 }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // KK consecutive elements (KK = 1, 2 or 4; aligned to KK elements) as float32.
 template <int KK, typename T>
@@ -72,15 +78,18 @@ __device__ __forceinline__ void ldk(const T* p, bool ok, float (&v)[KK]) {
     const float4 f = ld4_io<T>(p, ok);
     v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
   } else if constexpr (KK == 2) {
+    float2 f;
     if constexpr (sizeof(T) == 4) {
-      const float2 f = ok ? *reinterpret_cast<const float2*>(p) : make_float2(0.f, 0.f);
-      v[0] = f.x; v[1] = f.y;
+      f = *reinterpret_cast<const float2*>(p);
     } else {
-      v[0] = ok ? to_f32(p[0]) : 0.f;
-      v[1] = ok ? to_f32(p[1]) : 0.f;
+      const bf16x2 w = *reinterpret_cast<const bf16x2*>(p);
+      f = make_float2((float)w[0], (float)w[1]);
     }
+    v[0] = ok ? f.x : 0.f;
+    v[1] = ok ? f.y : 0.f;
   } else {
-    v[0] = ok ? to_f32(p[0]) : 0.f;
+    const float f = to_f32(p[0]);
+    v[0] = ok ? f : 0.f;
   }
 }
 
@@ -93,6 +102,22 @@ __device__ __forceinline__ f32x4 mfma4(float4 a, float4 b, f32x4 c) {
   c = mma(a.y, b.y, c);
   c = mma(a.z, b.z, c);
   return mma(a.w, b.w, c);
+}
+
+// Sum over each aligned group of 16 lanes (a DPP row), returned to all 16,
+// with data-parallel moves instead of LDS permutes: lane pairs xor 1 and xor
+// 2 (quad permutes), then the mirrored half row and the mirrored row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF,
+                                                            0xF, false));
+}
+__device__ __forceinline__ float sum16(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141>(v);   // row_half_mirror
+  v += dpp_mov<0x140>(v);   // row_mirror
+  return v;
 }
 
 // Inclusive prefix sum over the 256 threads of a workgroup (fixed order).
@@ -122,53 +147,70 @@ __device__ __forceinline__ float block_sum(float v, float* wsum) {
 // Phase 0
 // ---------------------------------------------------------------------------
 
-// One wavefront per (b, t, h) row: Delta, R1's Delta' and reversed operands,
-// and the float32 copies of bfloat16 inputs for the state scan.  R1's pad
-// positions are zeroed by k_bwd_zero_pad.
-template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_prep(BwdArgs a) {
-  const uint32_t row32 = blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+// One thread per (b, t, h) row: Delta and R1's Delta' (d_t at R1 position
+// pad + T - t; the pad and position pad get 0).
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_delta(BwdArgs a) {
+  const uint32_t row32 = blockIdx.x * kBwdThreads + threadIdx.x;
   if ((int64_t)row32 >= a.Bt * a.T * a.H) return;
   // rows fit 32 bits (checked on the host): 32-bit divisions
-  const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T, hpg32 = (uint32_t)(a.H / a.G);
+  const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T;
   const uint32_t bt32 = row32 / H32;
-  const int64_t row = row32, h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
-  const int64_t g = (uint32_t)h / hpg32;
-  const int64_t T1 = a.T + a.pad, tr1 = a.pad + (a.T - 1 - t);   // R1 position of token t
-  const int P = a.P, N = a.N;
+  const int64_t h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
+  const int64_t T1 = a.T + a.pad;
   const float d = delta_at(a, b, t, h);
+  a.wd[row32] = d;
+  if (t >= 1) a.dtr1[(b * T1 + (a.pad + a.T - t)) * a.H + h] = d;
+  else
+    for (int64_t k = 0; k <= a.pad; ++k) a.dtr1[(b * T1 + k) * a.H + h] = 0.0f;
+}
+
+// One thread per four head columns of a (b, t, h) row: R1's input
+// dy_t / Delta_{t+1} (0 for the last token) at R1 position pad + T-1-t, and
+// the float32 copy of x for the state scan (bfloat16 io).  `sh` = log2(P/4).
+template <typename T>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_x(BwdArgs a, int sh) {
+  const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
+  const uint32_t row32 = e >> sh, pq = e & ((1u << sh) - 1u);
+  if ((int64_t)row32 >= a.Bt * a.T * a.H) return;
+  const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T;
+  const uint32_t bt32 = row32 / H32;
+  const int64_t h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
+  const int64_t T1 = a.T + a.pad, tr1 = a.pad + (a.T - 1 - t);
+  const int P = a.P;
+  const int64_t rp = (int64_t)row32 * P + 4 * pq;
   const bool has_next = t + 1 < a.T;
-  const float dn = has_next ? delta_at(a, b, t + 1, h) : 1.0f;
-  if (lane == 0) {
-    a.wd[row] = d;
-    // Delta' at R1 position pad + T - t is d_t (t >= 1); the pad and position pad get 0
-    if (t >= 1) a.dtr1[(b * T1 + (a.pad + a.T - t)) * a.H + h] = d;
-    else
-      for (int64_t k = 0; k <= a.pad; ++k) a.dtr1[(b * T1 + k) * a.H + h] = 0.0f;
-  }
-  const T* x = reinterpret_cast<const T*>(a.x);
-  const T* dy = reinterpret_cast<const T*>(a.dy);
-  const T* Bm = reinterpret_cast<const T*>(a.B);
-  const T* Cm = reinterpret_cast<const T*>(a.C);
-  const int64_t rp = row * P, rpr1 = ((b * T1 + tr1) * a.H + h) * P;
-  for (int p = lane; p < P; p += 64) {
-    // input of R1 for token t: dy_t / Delta_{t+1} (0 for the last token)
-    a.r1_x[rpr1 + p] = has_next ? to_f32(dy[rp + p]) / dn : 0.0f;
-    if (a.x32) a.x32[rp + p] = to_f32(x[rp + p]);
-  }
-  if ((uint32_t)h % hpg32 == 0) {
-    const int64_t gn = ((b * a.T + t) * a.G + g) * N;
-    const int64_t gnr1 = ((b * T1 + tr1) * a.G + g) * N;
-    for (int n = lane; n < N; n += 64) {
-      const float bv = to_f32(Bm[gn + n]), cv = to_f32(Cm[gn + n]);
-      a.r1_b[gnr1 + n] = cv;
-      a.r1_c[gnr1 + n] = bv;
-      if (a.b32) {
-        a.b32[gn + n] = bv;
-        a.c32[gn + n] = cv;
-      }
-    }
+  const float wn = a.wd[has_next ? row32 + (uint32_t)a.H : row32];   // a valid row either way
+  const float dn = has_next ? wn : 1.0f;
+  const float4 v = ld4_io<T>(reinterpret_cast<const T*>(a.dy) + rp, true);
+  const float4 r = has_next ? make_float4(v.x / dn, v.y / dn, v.z / dn, v.w / dn)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+  *reinterpret_cast<float4*>(a.r1_x + ((b * T1 + tr1) * a.H + h) * P + 4 * pq) = r;
+  if (a.x32)
+    *reinterpret_cast<float4*>(a.x32 + rp) = ld4_io<T>(reinterpret_cast<const T*>(a.x) + rp, true);
+}
+
+// One thread per four state columns of a (b, t, g) row: R1's B and C (C and
+// B, reversed), and the float32 copies of B and C (bfloat16 io).
+// `sh` = log2(N/4).
+template <typename T>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_bc(BwdArgs a, int sh) {
+  const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
+  const uint32_t row32 = e >> sh, nq = e & ((1u << sh) - 1u);
+  if ((int64_t)row32 >= a.Bt * a.T * a.G) return;
+  const uint32_t G32 = (uint32_t)a.G, T32 = (uint32_t)a.T;
+  const uint32_t bt32 = row32 / G32;
+  const int64_t g = row32 - bt32 * G32, t = bt32 % T32, b = bt32 / T32;
+  const int64_t T1 = a.T + a.pad, tr1 = a.pad + (a.T - 1 - t);
+  const int N = a.N;
+  const int64_t rn = (int64_t)row32 * N + 4 * nq;
+  const int64_t rn1 = ((b * T1 + tr1) * a.G + g) * N + 4 * nq;
+  const float4 bv = ld4_io<T>(reinterpret_cast<const T*>(a.B) + rn, true);
+  const float4 cv = ld4_io<T>(reinterpret_cast<const T*>(a.C) + rn, true);
+  *reinterpret_cast<float4*>(a.r1_b + rn1) = cv;
+  *reinterpret_cast<float4*>(a.r1_c + rn1) = bv;
+  if (a.b32) {
+    *reinterpret_cast<float4*>(a.b32 + rn) = bv;
+    *reinterpret_cast<float4*>(a.c32 + rn) = cv;
   }
 }
 
@@ -200,7 +242,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_init_states(BwdArgs a) {
 }
 
 // Chunk-local inclusive prefix sum of Delta A, in double: one wavefront per
-// (b, c, h).  (Runs after k_bwd_prep, which writes Delta.)
+// (b, c, h).  (Runs after k_bwd_delta, which writes Delta.)
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
   const int64_t w = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -239,12 +281,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
 // order.
 template <typename T, int P>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
-  constexpr int PB = P / 16 < 4 ? P / 16 : 4;   // 16-wide p blocks loaded per round
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
   const int NB = a.NB, nbt = NB * (NB + 1) / 2;
-  int64_t u = blockIdx.x;
+  // the blocks of one (b, c, g, head split) read the same rows: same XCD, same L2
+  int64_t u = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = (int)(u % nbt);
   u /= nbt;
   const int hs = (int)(u % a.HS);
@@ -285,7 +327,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = io[s][r], j = jb[v];
-        cbv[s][v][r] = (i < Lc && j < i) ? cb[(int64_t)i * L + j] : 0.0f;
+        const float cv = cb[(int64_t)min(i, Lc - 1) * L + min(j, Lc - 1)];
+        cbv[s][v][r] = (i < Lc && j < i) ? cv : 0.0f;
       }
 
   f32x4 mv[2][2];
@@ -295,39 +338,64 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
     for (int v = 0; v < 2; ++v) mv[s][v] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t bch = (b * a.Nc + c) * a.H;
-#pragma unroll 1
-  for (int64_t h = hb; h < he; ++h) {
+  // The block's dy rows (I) and x rows (J) of one head go through LDS,
+  // double-buffered: each is read by two wavefronts, and the next head's rows
+  // are loaded into registers while this head's are consumed.  Rows past the
+  // chunk read its last row: finite values whose products the causal select
+  // below discards.
+  constexpr int XS = P + 4;                       // padded LDS row
+  constexpr int RQ = P / 4;                       // float4 per row
+  constexpr int SL = 2 * 64 * RQ / kBwdThreads;   // float4 per thread per head
+  __shared__ __attribute__((aligned(16))) float s_op[2][2 * 64 * XS];
+  auto load_stage = [&](int64_t h, float4 (&st)[SL]) {
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const int e = tid + k * kBwdThreads, which = e / (64 * RQ), rem = e % (64 * RQ);
+      const int row = rem / RQ, p4 = rem % RQ;
+      const int grow = min((which ? 64 * J : 64 * I) + row, Lc - 1);
+      st[k] = ld4_io<T>((which ? xg : dyg) + (int64_t)grow * xrs + h * P + 4 * p4, true);
+    }
+  };
+  auto store_stage = [&](int buf, const float4 (&st)[SL]) {
+#pragma unroll
+    for (int k = 0; k < SL; ++k) {
+      const int e = tid + k * kBwdThreads, which = e / (64 * RQ), rem = e % (64 * RQ);
+      const int row = rem / RQ, p4 = rem % RQ;
+      *reinterpret_cast<float4*>(&s_op[buf][(which * 64 + row) * XS + 4 * p4]) = st[k];
+    }
+  };
+  struct Dec {
+    double ci[2][4], cj[2];
+    float dj[2];
+  };
+  auto load_dec = [&](int64_t h, Dec& o) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o.ci[s][r] = cumg[(int64_t)min(io[s][r], Lc - 1) * a.H + h];
+      o.cj[s] = cumg[(int64_t)min(jb[s], Lc - 1) * a.H + h];
+      o.dj[s] = wdg[(int64_t)min(jb[s], Lc - 1) * a.H + h];   // masked with the decay
+    }
+  };
+  auto process = [&](int64_t h, const float* so, const Dec& o) {
     f32x4 sv[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int v = 0; v < 2; ++v) sv[s][v] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int pb0 = 0; pb0 < P / 16; pb0 += PB) {
-      float4 dv[2][PB], xv[2][PB];
+#pragma unroll
+    for (int pb = 0; pb < P / 16; ++pb) {
+      float4 dv[2], xv[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        dv[s] = *reinterpret_cast<const float4*>(&so[(32 * wr + 16 * s + r16) * XS + 16 * pb + 4 * q]);
+        xv[s] = *reinterpret_cast<const float4*>(
+            &so[(64 + 32 * wc + 16 * s + r16) * XS + 16 * pb + 4 * q]);
+      }
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int k = 0; k < PB; ++k) {
-          const int pp = 16 * (pb0 + k) + 4 * q;
-          dv[s][k] = ld4_io<T>(dyg + (int64_t)min(ia[s], Lc - 1) * xrs + h * P + pp, ia[s] < Lc);
-          xv[s][k] = ld4_io<T>(xg + (int64_t)min(jb[s], Lc - 1) * xrs + h * P + pp, jb[s] < Lc);
-        }
-#pragma unroll
-      for (int k = 0; k < PB; ++k)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int v = 0; v < 2; ++v) sv[s][v] = mfma4(dv[s][k], xv[v][k], sv[s][v]);
-    }
-    double ci[2][4], cj[2];
-    float dj[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ci[s][r] = cumg[(int64_t)min(io[s][r], Lc - 1) * a.H + h];
-      cj[s] = cumg[(int64_t)min(jb[s], Lc - 1) * a.H + h];
-      dj[s] = jb[s] < Lc ? wdg[(int64_t)jb[s] * a.H + h] : 0.0f;
+        for (int v = 0; v < 2; ++v) sv[s][v] = mfma4(dv[s], xv[v], sv[s][v]);
     }
     float rowp[2][4], colp[2] = {0.f, 0.f};
 #pragma unroll
@@ -340,8 +408,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
           const int i = io[s][r], j = jb[v];
           // causal mask selected before the exponential
           const bool ok = i < Lc && j <= i;
-          const float e = ok ? fast_exp((float)(ci[s][r] - cj[v])) : 0.0f;
-          const float m = sv[s][v][r] * e * dj[v];
+          const float e = ok ? fast_exp((float)(o.ci[s][r] - o.cj[v])) : 0.0f;
+          const float m = sv[s][v][r] * e * o.dj[v];
           mv[s][v][r] += m;
           const float qv = m * cbv[s][v][r];
           rowp[s][r] += qv;
@@ -351,7 +419,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rowp[s][r] = group_sum(rowp[s][r], 16);
+      for (int r = 0; r < 4; ++r) rowp[s][r] = sum16(rowp[s][r]);
 #pragma unroll
     for (int v = 0; v < 2; ++v) {
       colp[v] += __shfl_xor(colp[v], 16, 64);
@@ -367,6 +435,28 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
     if (q == 0) {
 #pragma unroll
       for (int v = 0; v < 2; ++v) a.qcol[qo + 64 * wr + 32 * wc + 16 * v + r16] = colp[v];
+    }
+  };
+  {
+    float4 st[SL];
+    Dec cur, nxt;
+    load_stage(hb, st);
+    load_dec(hb, cur);
+    store_stage(0, st);
+    __syncthreads();
+    int buf = 0;
+#pragma unroll 1
+    for (int64_t h = hb; h < he; ++h) {
+      const bool more = h + 1 < he;   // uniform
+      if (more) {
+        load_stage(h + 1, st);
+        load_dec(h + 1, nxt);
+      }
+      process(h, s_op[buf], cur);
+      if (more) store_stage(buf ^ 1, st);
+      __syncthreads();
+      cur = nxt;
+      buf ^= 1;
     }
   }
   // this head split's part of M (zeros outside j <= i < Lc)
@@ -390,14 +480,17 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
 //     role 0: row = dy_i, scale = e^{cum_i}, Z = H_c;
 //     role 1: row = x_j, scale = d_j e^{cum_last - cum_j}, Z = Ghat_c;
 //     its dot with C_i (role 0) or B_j (role 1) is u_i or v_j (this split's columns);
-//   intra-chunk part (head split 0): M B (role 0, j <= i) or M^T C (role 1, i >= j).
+//   intra-chunk part: M B (role 0, j <= i) or M^T C (role 1, i >= j), its 16-token
+//     blocks dealt out over the head splits.
 template <typename T, int P, int KK>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
   constexpr int NW = 16 * KK;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int NB = a.NB;
-  int64_t u = blockIdx.x;
+  // the row blocks of one (b, c, g, head split, role, column split) read the
+  // same state slices: same XCD, same L2
+  int64_t u = xcd_remap(blockIdx.x, gridDim.x);
   const int rb = (int)(u % NB);
   u /= NB;
   const int ns = (int)(u % a.NS);
@@ -437,57 +530,94 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
   const int64_t PN = (int64_t)P * N;
   const int64_t BtT = a.Bt * a.T;
   float* uvo = a.uv + ((int64_t)(role * a.NS + ns) * BtT + b * a.T + t0) * a.H;
-#pragma unroll 1
-  for (int64_t h = hb; h < he; ++h) {
+  // Z = H_c (role 0) or Ghat_c / abar (role 1; null for the last chunk without dfinal)
+  auto zptr = [&](int64_t h) -> const float* {
+    if (role == 0) return a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
+    if (c + 1 < a.Nc) return a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN;
+    return a.dfinal ? a.dfinal + (b * a.H + h) * PN : nullptr;
+  };
+  // The workgroup's NW columns of Z are shared by its four wavefronts: they
+  // go through LDS, double-buffered, the next head's slice loaded into
+  // registers while this head's is consumed.  Each wavefront reads its own A
+  // rows directly.
+  constexpr int ZS = NW + 4;                        // padded LDS row
+  constexpr int ZQ = NW / 4;                        // float4 per Z row
+  constexpr int ZL = (P * ZQ + kBwdThreads - 1) / kBwdThreads;
+  __shared__ __attribute__((aligned(16))) float s_z[2][P * ZS];
+  auto load_z = [&](int64_t h, float4 (&zr)[ZL]) {
+    const float* Z = zptr(h);
+    const bool zok = Z != nullptr;
+    const float* Zs = zok ? Z : a.fwd_state;   // a valid address either way
+#pragma unroll
+    for (int k = 0; k < ZL; ++k) {
+      const int e = tid + k * kBwdThreads, pr = min(e / ZQ, P - 1), cq = e % ZQ;
+      zr[k] = ld4_io<float>(Zs + (int64_t)pr * N + ns * NW + 4 * cq, zok);
+    }
+  };
+  auto store_z = [&](int buf, const float4 (&zr)[ZL]) {
+#pragma unroll
+    for (int k = 0; k < ZL; ++k) {
+      const int e = tid + k * kBwdThreads, pr = e / ZQ, cq = e % ZQ;
+      if (e < P * ZQ) *reinterpret_cast<float4*>(&s_z[buf][pr * ZS + 4 * cq]) = zr[k];
+    }
+  };
+  struct Arow {
+    float4 av[P / 16];
+    double ci, clast;
+    float dj, wn;
+  };
+  const T* amat = reinterpret_cast<const T*>(role ? a.x : a.dy);
+  auto load_a = [&](int64_t h, Arow& o) {
     const int64_t rowi = (b * a.T + t0 + iac) * a.H + h;
-    const double ci = a.cum[rowi];
-    const float* Z;
+    const T* arow = amat + rowi * P;
+#pragma unroll
+    for (int pb = 0; pb < P / 16; ++pb) o.av[pb] = ld4_io<T>(arow + 16 * pb + 4 * q, true);
+    o.ci = a.cum[rowi];
+    o.clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
+    o.dj = a.wd[rowi];
+    o.wn = (role == 1 && c + 1 < a.Nc) ? a.wd[(b * a.T + t0 + L) * a.H + h] : 0.0f;
+  };
+  auto process_h = [&](int64_t h, const Arow& o, const float* sz) {
     float scale;
-    const T* arow;
     if (role == 0) {
-      Z = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
-      scale = iok ? fast_exp((float)ci) : 0.0f;
-      arow = reinterpret_cast<const T*>(a.dy) + rowi * P;
+      scale = iok ? fast_exp((float)o.ci) : 0.0f;
     } else {
-      float gs = 1.0f;
-      if (c + 1 < a.Nc) {
-        Z = a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN;
-        gs = expf(a.wd[(b * a.T + t0 + L) * a.H + h] * a.A[h]);   // abar of the next chunk's first token
-      } else {
-        Z = a.dfinal ? a.dfinal + (b * a.H + h) * PN : nullptr;
-      }
-      const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
-      scale = iok ? gs * a.wd[rowi] * fast_exp((float)(clast - ci)) : 0.0f;
-      arow = reinterpret_cast<const T*>(a.x) + rowi * P;
+      // abar of the next chunk's first token turns R1's entering state into Ghat_c
+      const float gs = c + 1 < a.Nc ? expf(o.wn * a.A[h]) : 1.0f;
+      scale = iok ? gs * o.dj * fast_exp((float)(o.clast - o.ci)) : 0.0f;
     }
     f32x4 ah[KK];
 #pragma unroll
     for (int k = 0; k < KK; ++k) ah[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (Z) {   // uniform
-#pragma unroll 2
-      for (int pb = 0; pb < P / 16; ++pb) {
-        float4 av = ld4_io<T>(arow + 16 * pb + 4 * q, true);
-        av.x *= scale; av.y *= scale; av.z *= scale; av.w *= scale;
-        float zv[4][KK];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ldk<KK, float>(Z + (int64_t)(16 * pb + 4 * q + e) * N + n0, true, zv[e]);
+    for (int pb = 0; pb < P / 16; ++pb) {
+      const float av[4] = {o.av[pb].x * scale, o.av[pb].y * scale, o.av[pb].z * scale,
+                           o.av[pb].w * scale};
 #pragma unroll
-        for (int k = 0; k < KK; ++k) {
-          ah[k] = mma(av.x, zv[0][k], ah[k]);
-          ah[k] = mma(av.y, zv[1][k], ah[k]);
-          ah[k] = mma(av.z, zv[2][k], ah[k]);
-          ah[k] = mma(av.w, zv[3][k], ah[k]);
+      for (int e = 0; e < 4; ++e) {
+        const float* zrow = sz + (16 * pb + 4 * q + e) * ZS + KK * r16;
+        float zv[KK];
+        if constexpr (KK == 4) {
+          const float4 v = *reinterpret_cast<const float4*>(zrow);
+          zv[0] = v.x; zv[1] = v.y; zv[2] = v.z; zv[3] = v.w;
+        } else if constexpr (KK == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(zrow);
+          zv[0] = v.x; zv[1] = v.y;
+        } else {
+          zv[0] = zrow[0];
         }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ah[kk] = mma(av[e], zv[kk], ah[kk]);
       }
     }
     // u_i (role 0) or v_j (role 1) over this split's columns
     float ds[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float s = 0.0f;
+      float sum = 0.0f;
 #pragma unroll
-      for (int k = 0; k < KK; ++k) s = __fmaf_rn(dvec[r][k], ah[k][r], s);
-      ds[r] = group_sum(s, 16);
+      for (int k = 0; k < KK; ++k) sum = __fmaf_rn(dvec[r][k], ah[k][r], sum);
+      ds[r] = sum16(sum);
     }
     if (r16 == 0) {
 #pragma unroll
@@ -496,17 +626,41 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < KK; ++k) acc[k] += ah[k];
+  };
+  {
+    float4 zr[ZL];
+    Arow cur, nxt;
+    load_z(hb, zr);
+    load_a(hb, cur);
+    store_z(0, zr);
+    __syncthreads();
+    int buf = 0;
+#pragma unroll 1
+    for (int64_t h = hb; h < he; ++h) {
+      const bool more = h + 1 < he;   // uniform
+      if (more) {
+        load_z(h + 1, zr);
+        load_a(h + 1, nxt);
+      }
+      process_h(h, cur, s_z[buf]);
+      if (more) store_z(buf ^ 1, zr);
+      __syncthreads();
+      cur = nxt;
+      buf ^= 1;
+    }
   }
 
-  if (hsd == 0) {
+  // intra-chunk part: its 16-token blocks are dealt out over the head splits
+  // (whose parts are summed afterwards), so every workgroup gets a share
+  {
     const int64_t LP = a.LP, LP2 = LP * LP;
     const float* mp = a.mix + ((b * a.Nc + c) * a.G + g) * (int64_t)a.HS * LP2;
     const int kend = (Lc + 15) / 16;
     if (role == 0) {
       // dC_i += sum_{j <= i} M[i][j] B_j
       const int kb1 = min(4 * (rb + 1), kend);
-#pragma unroll 1
-      for (int kb = 0; kb < kb1; ++kb) {
+#pragma unroll 4
+      for (int kb = hsd; kb < kb1; kb += a.HSD) {
         float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s = 0; s < a.HS; ++s) {
           const float4 v =
@@ -516,8 +670,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
         float bv[4][KK];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          // M[i][j] = 0 for j >= Lc: the clamped row needs no mask
           const int j = 16 * kb + 4 * q + e;
-          ldk<KK, T>(Bg + (int64_t)min(j, Lc - 1) * grs + n0, j < Lc, bv[e]);
+          ldk<KK, T>(Bg + (int64_t)min(j, Lc - 1) * grs + n0, true, bv[e]);
         }
 #pragma unroll
         for (int k = 0; k < KK; ++k) {
@@ -529,8 +684,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
       }
     } else {
       // dB_j += sum_{i >= j} M[i][j] C_i
-#pragma unroll 1
-      for (int kb = 4 * rb; kb < kend; ++kb) {
+#pragma unroll 4
+      for (int kb = 4 * rb + hsd; kb < kend; kb += a.HSD) {
         float m4[4] = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < a.HS; ++s) {
 #pragma unroll
@@ -539,8 +694,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
         float cv[4][KK];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+          // M[i][j] = 0 for i >= Lc: the clamped row needs no mask
           const int i = 16 * kb + 4 * q + e;
-          ldk<KK, T>(Cg + (int64_t)min(i, Lc - 1) * grs + n0, i < Lc, cv[e]);
+          ldk<KK, T>(Cg + (int64_t)min(i, Lc - 1) * grs + n0, true, cv[e]);
         }
 #pragma unroll
         for (int k = 0; k < KK; ++k) {
@@ -581,34 +737,45 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb_reduce(BwdArgs a) {
   (role ? a.dB : a.dC)[k] = s;
 }
 
-// One wavefront per (b, t, h): dx, the input-scale part of the Delta gradient
-// (x . G B) and the per-token part of dD.
+// One thread per four head columns of a (b, t, h) row (the P/4 threads of a
+// row are adjacent lanes of one wavefront): dx, the input-scale part of the
+// Delta gradient (x . G B) and the per-token part of dD.  `sh` = log2(P/4).
 template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a) {
-  const int64_t row = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= a.Bt * a.T * a.H) return;
-  const int64_t h = row % a.H, bt = row / a.H, t = bt % a.T, b = bt / a.T;
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a, int sh) {
+  const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
+  const uint32_t row32 = e >> sh, pq = e & ((1u << sh) - 1u);
+  const bool ok = (int64_t)row32 < a.Bt * a.T * a.H;
+  const uint32_t rowc = ok ? row32 : 0u;
+  const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T;
+  const uint32_t bt32 = rowc / H32;
+  const int64_t h = rowc - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
   const int P = a.P;
-  const float d = a.wd[row];
+  const float d = a.wd[rowc];
   const float Dh = a.D ? a.D[h] : 0.0f;
-  const int64_t rp = row * P;
-  const int64_t rpr1 = ((b * (a.T + a.pad) + (a.pad + a.T - 1 - t)) * a.H + h) * P;
-  const T* x = reinterpret_cast<const T*>(a.x);
-  const T* dy = reinterpret_cast<const T*>(a.dy);
-  float s_din = 0.0f, s_dd = 0.0f;
-  for (int p = lane; p < P; p += 64) {
-    const float xv = to_f32(x[rp + p]), dyv = to_f32(dy[rp + p]);
-    const float gb = a.r1_y[rpr1 + p];               // sum_n G[p,n] B_t[n]
-    a.dx[rp + p] = __fmaf_rn(Dh, dyv, d * gb);
-    s_din = __fmaf_rn(xv, gb, s_din);
-    s_dd = __fmaf_rn(dyv, xv, s_dd);
-  }
-  s_din = group_sum(s_din, 64);
-  s_dd = group_sum(s_dd, 64);
-  if (lane == 0) {
-    a.ddin[row] = s_din;
-    a.dDp[row] = s_dd;
+  const int64_t rp = (int64_t)rowc * P + 4 * pq;
+  const int64_t rpr1 = ((b * (a.T + a.pad) + (a.pad + a.T - 1 - t)) * a.H + h) * P + 4 * pq;
+  // threads past the last row read row 0 and store nothing
+  const float4 xv = ld4_io<T>(reinterpret_cast<const T*>(a.x) + rp, true);
+  const float4 dyv = ld4_io<T>(reinterpret_cast<const T*>(a.dy) + rp, true);
+  const float4 gb = ld4_io<float>(a.r1_y + rpr1, true);   // sum_n G[p,n] B_t[n]
+  if (ok)
+    *reinterpret_cast<float4*>(a.dx + rp) =
+        make_float4(__fmaf_rn(Dh, dyv.x, d * gb.x), __fmaf_rn(Dh, dyv.y, d * gb.y),
+                    __fmaf_rn(Dh, dyv.z, d * gb.z), __fmaf_rn(Dh, dyv.w, d * gb.w));
+  float s_din = xv.x * gb.x;
+  s_din = __fmaf_rn(xv.y, gb.y, s_din);
+  s_din = __fmaf_rn(xv.z, gb.z, s_din);
+  s_din = __fmaf_rn(xv.w, gb.w, s_din);
+  float s_dd = dyv.x * xv.x;
+  s_dd = __fmaf_rn(dyv.y, xv.y, s_dd);
+  s_dd = __fmaf_rn(dyv.z, xv.z, s_dd);
+  s_dd = __fmaf_rn(dyv.w, xv.w, s_dd);
+  const int width = 1 << sh;
+  s_din = group_sum(s_din, width);
+  s_dd = group_sum(s_dd, width);
+  if (ok && pq == 0) {
+    a.ddin[row32] = s_din;
+    a.dDp[row32] = s_dd;
   }
 }
 
@@ -715,6 +882,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dh0(BwdArgs a) {
 
 inline unsigned blocks_of(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
 
+inline int log2_of(int v) {   // v a power of two
+  int k = 0;
+  while ((1 << k) < v) ++k;
+  return k;
+}
+
 template <typename T, int P>
 hipError_t launch_mix_dcdb(const BwdArgs& a, hipStream_t s) {
   const int64_t bcg = a.Bt * a.Nc * a.G;
@@ -741,8 +914,13 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
   const int64_t rows = a.Bt * a.T * a.H;
   switch (phase) {
     case 0:
-      hipLaunchKernelGGL(k_bwd_prep<T>, dim3(blocks_of(rows, kBwdThreads / 64)), dim3(kBwdThreads),
-                         0, s, a);
+      hipLaunchKernelGGL(k_bwd_delta, dim3(blocks_of(rows, kBwdThreads)), dim3(kBwdThreads), 0, s,
+                         a);
+      hipLaunchKernelGGL(k_bwd_prep_x<T>, dim3(blocks_of(rows * (a.P / 4), kBwdThreads)),
+                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / 4));
+      hipLaunchKernelGGL(k_bwd_prep_bc<T>,
+                         dim3(blocks_of(a.Bt * a.T * a.G * (int64_t)(a.N / 4), kBwdThreads)),
+                         dim3(kBwdThreads), 0, s, a, log2_of(a.N / 4));
       if (a.pad > 0) {
         const int64_t hp = a.pad * a.H * a.P, gn = a.pad * a.G * a.N;
         const int64_t per_b = hp > gn ? hp : gn;
@@ -765,8 +943,8 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
         default: e = hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_bwd_dx<T>, dim3(blocks_of(rows, kBwdThreads / 64)), dim3(kBwdThreads),
-                         0, s, a);
+      hipLaunchKernelGGL(k_bwd_dx<T>, dim3(blocks_of(rows * (a.P / 4), kBwdThreads)),
+                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / 4));
       hipLaunchKernelGGL(k_bwd_assemble, dim3((unsigned)(a.Bt * a.Nc * a.H)), dim3(kBwdThreads),
                          0, s, a);
       hipLaunchKernelGGL(k_bwd_reduce_heads, dim3(blocks_of(a.H, kBwdThreads)), dim3(kBwdThreads),
