@@ -56,7 +56,7 @@ KERNEL_SOURCES = {
 # HBM bytes per launch from the counter runs: (kernel key, workload) -> (bytes, digest)
 TRAFFIC = {
     # counter runs and calibration: profiles/chunk_out_f32_m130_f32_decode_m2p7_b64_hbm_bytes.txt
-    ("chunk_out/f32", "m130_f32"): (41.13e6 + 30.56e6, "d8501d574f6938aa"),
+    ("chunk_out/f32", "m130_f32"): (41.16e6 + 30.57e6, "1ca538f3919d2260"),
     ("decode", "m2p7_decode_b64"): (169.12e6 + 168.47e6, "a9cd5d42c984beb1"),
     # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
     ("conv1d", "conv_m2p7_bf16"): (49.19e6 + 44.07e6, "9c6f061da92854fb"),
@@ -293,6 +293,23 @@ def bench_cached_vs_recompute(ssd, torch, context=4096, reps=20):
             "recompute_us": t_re, "cached_step_us": t_st, "speedup": t_re / t_st}
 
 
+def backward_flops(w):
+    """Algorithmic FLOP of one ssd_chunk_scan_backward call: the products a
+    chunked backward of the scan must form, causal halves of each L x L block
+    counted as L(L+1)/2, C B^T once per (chunk, group):
+      per (chunk, head): 2LPN each for the recomputed chunk state, the adjoint
+        chunk state, and the state terms of dx, dC and dB (5 x 2LPN); L(L+1)/2 * 2P
+        each for dy x^T and the intra-chunk term of dx;
+      per (chunk, group): L(L+1)/2 * 2N each for C B^T and the intra-chunk
+        terms of dC (M B) and dB (M^T C)."""
+    L, P, N = w.chunk, w.headdim, w.dstate
+    Nc = -(-w.seqlen // L)
+    tri = L * (L + 1) // 2
+    per_head = 5 * 2 * L * P * N + 2 * tri * 2 * P
+    per_group = 3 * tri * 2 * N
+    return w.batch * Nc * (w.nheads * per_head + w.ngroups * per_group)
+
+
 def bench_backward(ssd, torch, w, reps=10):
     """The scan's gradients (ssd_chunk_scan_backward) on the headline layer:
     time per call and per token, against the forward scan of the same
@@ -338,10 +355,15 @@ def bench_backward(ssd, torch, w, reps=10):
     ms_b = timed(bwd)
     ms_f = timed(fwd)
     tokens = w.batch * w.seqlen
+    flops = backward_flops(w)
+    tflops = flops / (ms_b * 1e-3) / 1e12
     return {"workload": w.name, "ms": ms_b, "tokens_per_s": tokens / (ms_b * 1e-3),
             "forward_ms_same_inputs": ms_f, "backward_over_forward": ms_b / ms_f,
+            "flops_per_call": flops, "algorithmic_tflops": tflops,
+            "mfma_fp32_frac": tflops / PEAK_TFLOPS["f32"],
             "workspace_bytes": ws.numel(),
-            "note": "gradients of every input; recomputes the forward in float32"}
+            "note": "gradients of every input; float32 matrix-core products for either io "
+                    "type; recomputes the forward chunk states"}
 
 
 def conv_bytes(Bt, T, D, K, es):
@@ -477,6 +499,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the gradients (their reversed scan reuses the forward kernels)")
     ap.add_argument("--backward-only", action="store_true",
                     help="only time the scan's gradients (ssd_chunk_scan_backward) on the workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -545,8 +569,9 @@ def main():
         out["cached_vs_recompute"] = bench_cached_vs_recompute(ssd, torch)
         print("[bench] conv1d prefill and step", file=sys.stderr, flush=True)
         out["conv1d"] = bench_conv(ssd, torch, args.warmup)
-        print("[bench] backward", file=sys.stderr, flush=True)
-        out["backward"] = bench_backward(ssd, torch, w)
+        if not args.no_backward:
+            print("[bench] backward", file=sys.stderr, flush=True)
+            out["backward"] = bench_backward(ssd, torch, w)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

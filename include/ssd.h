@@ -173,12 +173,15 @@ ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float*
  * Caching", Background, Eq. 2-3.
  *
  * The adjoint state G_t = dL/dh_t obeys the same recurrence backwards in
- * time (G_t = dy_t (x) C_t + abar_{t+1} G_{t+1}), so the library computes the
- * gradients with the scan's own kernels: the forward scan (recomputed), a
- * scan over reversed time with B and C exchanged (dx, dt, dA, dh0), a scan
- * with the roles of P and N exchanged (dC), a reversed one of that kind (dB),
- * and element-wise and reduction kernels (no atomics: results are
- * deterministic).
+ * time (G_t = dy_t (x) C_t + abar_{t+1} G_{t+1}).  The library recomputes the
+ * forward chunk states and C B^T (float32), runs the scan itself over
+ * reversed time with B and C exchanged (float32: G_t B_t for dx and the
+ * adjoint at chunk boundaries), and forms dB, dC and the Delta gradient
+ * chunk by chunk: per group, M = sum over its heads of (dy x^T) o decay o
+ * Delta is built once on the matrix cores, dC = M B + dy H, dB = M^T C +
+ * x Ghat, and dL/d(Delta A) comes from sums inside each chunk only (no sum
+ * over the sequence cancels).  Every product is float32 on the matrix cores
+ * whatever the io type.  No atomics: results are deterministic.
  *
  *   inputs as ssd_chunk_scan; dy [Bt,T,H,P] io_dtype;
  *   dfinal_state [Bt,H,P,N] f32 or NULL (zero)
@@ -188,14 +191,11 @@ ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float*
  *   dinitial_state [Bt,H,P,N] or NULL (not returned)
  *   workspace: at least ssd_chunk_scan_backward_workspace_bytes(desc)
  *
- * Shapes: those of ssd_chunk_scan whose exchanged form (headdim N, dstate P,
- * one group per head) is also supported (N * L <= 32768; P >= 32 for
- * bfloat16); other valid shapes return SSD_ERR_UNSUPPORTED.  With bfloat16
- * io the internal operands (dy / Delta, replicated B and C) and the scans'
- * outputs are rounded to bfloat16 as in the forward scan.  Gradients may not
- * overlap any input, the workspace or each other.  batch == 0 writes zeros
- * to dA, dD and ddt_bias; seqlen == 0 also copies dfinal_state (or zeros) to
- * dinitial_state.
+ * Shapes: those of ssd_chunk_scan with chunk <= 256 and batch * seqlen *
+ * nheads <= INT32_MAX; other valid shapes return SSD_ERR_UNSUPPORTED (and a
+ * workspace size of 0).  Gradients may not overlap any input, the workspace
+ * or each other.  batch == 0 writes zeros to dA, dD and ddt_bias; seqlen == 0
+ * also copies dfinal_state (or zeros) to dinitial_state.
  */
 size_t ssd_chunk_scan_backward_workspace_bytes(const ssd_scan_desc* desc);
 ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* desc, const void* x, const float* dt,
