@@ -826,8 +826,20 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
     Gh = a.dfinal + (b * a.H + h) * PN;
   }
   float sc = 0.0f;
-  if (Gh)
-    for (int64_t e = l; e < PN; e += kBwdThreads) sc = __fmaf_rn(Gh[e], Hc[e], sc);
+  if (Gh) {
+    // float4 vectors, four in flight per thread (P N is a multiple of 256)
+    const float4* g4 = reinterpret_cast<const float4*>(Gh);
+    const float4* h4 = reinterpret_cast<const float4*>(Hc);
+    const int64_t n4 = PN / 4;
+#pragma unroll 4
+    for (int64_t e = l; e < n4; e += kBwdThreads) {
+      const float4 gv = g4[e], hv = h4[e];
+      sc = __fmaf_rn(gv.x, hv.x, sc);
+      sc = __fmaf_rn(gv.y, hv.y, sc);
+      sc = __fmaf_rn(gv.z, hv.z, sc);
+      sc = __fmaf_rn(gv.w, hv.w, sc);
+    }
+  }
   sc = block_sum(sc, s_w);
   const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
   sc *= gs * (float)exp(clast);
