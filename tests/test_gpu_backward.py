@@ -170,3 +170,99 @@ def test_backward_empty_inputs():
     got = ssd.ssd_chunk_scan_backward(x[:0], dt[:0], A, B[:0], B[:0], None, dy=x[:0], chunk=32)
     torch.cuda.synchronize()
     assert not got["dA"].any()
+
+
+def test_backward_long_batched_sampled():
+    """The 1.3B-shaped batched long prefill (8 x 16384, 64 heads, bfloat16,
+    chunk 256) in full on the GPU.  dx, ddt and the initial-state gradient of
+    a head depend on that head alone: for two sampled heads of row 0 they are
+    checked against the oracle run on those heads only.  Row 3 run alone on
+    the GPU gives the same dx, ddt, dB and dC as inside the batch."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = WORKLOADS["m1p3_long_bf16"]
+    announce("backward m1p3_long_bf16 sampled")
+    inp = make_inputs(w, with_initial_state=True)
+    g = torch.Generator().manual_seed(6600)
+    dy = torch.randn(inp["x"].shape, generator=g).to(inp["x"].dtype)
+    dfinal = torch.randn(inp["h0"].shape, generator=g)
+    d = to_dev(inp)
+    dyd, dfd = dy.to("cuda"), dfinal.to("cuda")
+
+    def gpu(sl):
+        return ssd.ssd_chunk_scan_backward(
+            d["x"][sl], d["dt"][sl], d["A"], d["B"][sl], d["C"][sl], d["D"], dy=dyd[sl],
+            dfinal_state=dfd[sl], chunk=w.chunk, dt_bias=d["dt_bias"], initial_state=d["h0"][sl])
+
+    got = gpu(slice(None))
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dB", "dC", "dinitial_state"):
+        assert torch.isfinite(got[k]).all(), k
+    heads = [0, 37]
+    ref = oracle.scan_backward(inp["x"][0:1, :, heads], inp["dt"][0:1, :, heads], inp["A"][heads],
+                               inp["B"][0:1], inp["C"][0:1], inp["D"][heads],
+                               inp["dt_bias"][heads], inp["h0"][0:1, heads].double().numpy(),
+                               dy=dy[0:1, :, heads].double().numpy(),
+                               dfinal=dfinal[0:1, heads].double().numpy(),
+                               dt_softplus=True, dt_min=w.dt_min, dt_max=w.dt_max)
+    errs = {"dx": slice_rel_err(got["dx"][0:1, :, heads], ref["dx"], 2, (1, 3)),
+            "ddt": slice_rel_err(got["ddt"][0:1, :, heads], ref["ddt"], 2, (1,)),
+            "dh0": slice_rel_err(got["dinitial_state"][0:1, heads], ref["dh0"], 1, (2, 3))}
+    print("sampled heads", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
+    one = gpu(slice(3, 4))
+    torch.cuda.synchronize()
+    for k in ("dx", "ddt", "dB", "dC"):
+        a_, b_ = one[k].double(), got[k][3:4].double()
+        rel = float((a_ - b_).abs().max() / b_.abs().max().clamp_min(1e-30))
+        assert rel <= 1e-5, (k, rel)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_of_a_split_sequence(io):
+    """A sequence cut at a token inside a chunk: the second part's backward
+    takes dfinal, its initial-state gradient is the first part's dfinal.  The
+    per-token gradients of the two parts equal those of the whole sequence,
+    and the per-head ones (dA, dD, ddt_bias) add up."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = make_tiny(2, 700, 4, 32, 64, 2, 128, io, seed=6700)
+    announce(f"backward split sequence {io}")
+    inp = make_inputs(w, with_initial_state=True)
+    g = torch.Generator().manual_seed(6701)
+    dy = torch.randn(inp["x"].shape, generator=g).to(inp["x"].dtype).to("cuda")
+    dfinal = torch.randn(inp["h0"].shape, generator=g).to("cuda")
+    d = to_dev(inp)
+    cut = 333
+
+    def part(sl, h0, dfin):
+        return ssd.ssd_chunk_scan_backward(
+            d["x"][:, sl].contiguous(), d["dt"][:, sl].contiguous(), d["A"],
+            d["B"][:, sl].contiguous(), d["C"][:, sl].contiguous(), d["D"],
+            dy=dy[:, sl].contiguous(), dfinal_state=dfin, chunk=w.chunk, dt_bias=d["dt_bias"],
+            initial_state=h0)
+
+    whole = part(slice(None), d["h0"], dfinal)
+    # the state entering the second part, from the float32 forward scan (the
+    # backward recomputes its forward in float32 from the same, exactly
+    # converted, inputs)
+    _, h_cut = ssd.ssd_chunk_scan(d["x"][:, :cut].float().contiguous(),
+                                  d["dt"][:, :cut].contiguous(), d["A"],
+                                  d["B"][:, :cut].float().contiguous(),
+                                  d["C"][:, :cut].float().contiguous(), d["D"], chunk=w.chunk,
+                                  dt_bias=d["dt_bias"], initial_state=d["h0"],
+                                  return_final_state=True)
+    second = part(slice(cut, None), h_cut, dfinal)
+    first = part(slice(0, cut), d["h0"], second["dinitial_state"])
+    torch.cuda.synchronize()
+
+    def rel(a_, b_):
+        return float((a_.double() - b_.double()).abs().max() / b_.double().abs().max())
+
+    bar = 1e-4
+    for k in ("dx", "ddt", "dB", "dC"):
+        cat = torch.cat([first[k], second[k]], 1)
+        assert rel(cat, whole[k]) <= bar, (k, rel(cat, whole[k]))
+    for k in ("dA", "dD", "ddt_bias"):
+        assert rel(first[k] + second[k], whole[k]) <= bar, k
+    assert rel(first["dinitial_state"], whole["dinitial_state"]) <= bar
