@@ -35,6 +35,7 @@ import math
 import os
 import platform
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -177,6 +178,16 @@ def bench_prefill(ssd, torch, w, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
+    # five more timed runs of the same K steps: spread of the step time
+    rep_ms = []
+    for _ in range(5):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        for i in range(steps):
+            run(i)
+        r1.record()
+        torch.cuda.synchronize()
+        rep_ms.append(r0.elapsed_time(r1) / steps)
     # per-kernel durations, HIP events on the stream the kernels run on
     nph = ssd.SSD_SCAN_PHASES
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(steps)]
@@ -187,7 +198,7 @@ def bench_prefill(ssd, torch, w, steps, warmup):
     phase_ms = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
                 for k, n in enumerate(names)}
     return {"ms": ms, "wall_ms": wall * 1e3 / steps, "phase_ms": phase_ms, "nsets": nsets,
-            "set_bytes": set_bytes, "tokens": Bt * T}
+            "set_bytes": set_bytes, "tokens": Bt * T, "rep_ms": rep_ms}
 
 
 def bench_decode(ssd, torch, batch, steps_n, warmup):
@@ -481,8 +492,15 @@ def cpu_baseline(w, target_s=10.0):
     per_rep = el / reps
     scale = pairs_full / k          # the full workload has this many times the (b, h) pairs
     full_s = per_rep * scale
+    # one thread, one (b, h) sequence: the oracle's serial rate, scaled the same way
+    one = {kk: (v[:1, :, :1] if kk in ("x", "dt") else v[:1] if kk in ("B", "C") else v[:1])
+           for kk, v in sl.items()}
+    t1 = time.perf_counter()
+    oracle.scan(one["x"], one["dt"], one["A"], one["B"], one["C"], one["D"], one["dt_bias"], None,
+                dt_min=w.dt_min, dt_max=w.dt_max, nthreads=1)
+    one_s = (time.perf_counter() - t1) * pairs_full
     return {"value": Bt * w.seqlen / full_s, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "value_1_thread": Bt * w.seqlen / one_s,
             "sample": (f"fp64 recurrence on {k} of {pairs_full} (batch, head) sequences of "
                        f"{w.seqlen} tokens, {reps} repetition(s) in {el:.1f} s, scaled by "
                        f"{scale:g} to the whole workload; host CPU: {cpu_model()}")}
@@ -558,6 +576,8 @@ def main():
                     "bytes_per_token": prefill_bytes_per_token(w, w.seqlen),
                     "hbm_gbs_algorithmic": prefill_bytes_per_token(w, w.seqlen) * tokens_s / 1e9,
                     "phase_ms": pf["phase_ms"], "wall_ms_per_step": pf["wall_ms"],
+                    "repeat_ms_per_step": {"runs": 5, "mean": statistics.mean(pf["rep_ms"]),
+                                           "std": statistics.stdev(pf["rep_ms"])},
                     "rotated_sets": pf["nsets"]},
     }
     if not args.no_decode:
