@@ -14,9 +14,9 @@
 // across the N/4 lanes that hold one row.  The state is touched exactly once
 // per step, so its loads and stores are non-temporal (no cache allocation for
 // a stream that will not be re-read before it is evicted); this alone raised
-// the measured rate at batch 64 from 53% to 65% of the HBM peak.  Large
-// batches use 512-thread workgroups with 4 vectors per lane, small ones
-// 256-thread workgroups with 8 (whichever measured faster for that size).
+// the measured rate at batch 64 from 53% to 65% of the HBM peak.  The
+// workgroup shape (threads x vectors per lane) is chosen per batch size from
+// measurements (launch_step).
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -33,13 +33,24 @@ __device__ __forceinline__ void st_stream(float4* p, float4 v) {
   __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 }
 
-// THREADS lanes per workgroup, BATCH float4 loads in flight per lane.
+// THREADS lanes per workgroup, BATCH float4 loads in flight per lane.  The
+// state loads of the first pass are issued before anything else (Delta, the
+// decay, B and C), so the slice is in flight while the rest is computed: at
+// batch 64 this took the step from 63.3 to 59 us, at batch 1 from 10.6 to ~5.
 template <typename T, int THREADS, int BATCH>
 __global__ __launch_bounds__(THREADS) void k_step(StepArgs a) {
   const int64_t bh = blockIdx.x;
-  const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
   const int P = a.P, N = a.N, NQ = N / 4;
   const int tid = threadIdx.x;
+  const int total = P * NQ;  // float4 elements of the slice, a multiple of 64
+  float4* st = reinterpret_cast<float4*>(a.state + bh * (int64_t)P * N);
+  float4 s[BATCH];
+#pragma unroll
+  for (int k = 0; k < BATCH; ++k) {
+    const int f = k * THREADS + tid;
+    if (f < total) s[k] = ld_stream(&st[f]);   // uniform per wavefront
+  }
+  const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const float d = delta_of(a.dt[bh] + bias, a.softplus, a.dt_min, a.dt_max);
   const float alpha = expf(d * a.A[h]);
@@ -48,7 +59,6 @@ __global__ __launch_bounds__(THREADS) void k_step(StepArgs a) {
   const T* Bg = reinterpret_cast<const T*>(a.B) + (b * a.G + g) * N;
   const T* Cg = reinterpret_cast<const T*>(a.C) + (b * a.G + g) * N;
   T* yg = reinterpret_cast<T*>(a.y) + bh * P;
-  float4* st = reinterpret_cast<float4*>(a.state + bh * (int64_t)P * N);
 
   // the n-quad of this lane is the same for every row it visits (NQ | THREADS)
   const int n4 = tid % NQ;
@@ -58,13 +68,13 @@ __global__ __launch_bounds__(THREADS) void k_step(StepArgs a) {
     bv[k] = to_f32(Bg[4 * n4 + k]);
     cv[k] = to_f32(Cg[4 * n4 + k]);
   }
-  const int total = P * NQ;  // float4 elements of the slice, a multiple of 64
   for (int base = 0; base < total; base += THREADS * BATCH) {
-    float4 s[BATCH];
+    if (base > 0) {
 #pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int f = base + k * THREADS + tid;
-      if (f < total) s[k] = ld_stream(&st[f]);
+      for (int k = 0; k < BATCH; ++k) {
+        const int f = base + k * THREADS + tid;
+        if (f < total) s[k] = ld_stream(&st[f]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
@@ -95,8 +105,13 @@ __global__ __launch_bounds__(kThreads) void k_copy_or_zero(float4* dst, const fl
 template <typename T>
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
   const int64_t slices = a.Bt * a.H;
-  if (slices >= 2048 && a.P * a.N >= 8192) {
+  // shapes measured at the 2.7B shape (P N = 8192): 512 x 4 at batch 64,
+  // 256 x 8 at batch 16, 1024 x 2 at batch 1 (80 slices: fewer, wider
+  // workgroups put more of the state in flight at once)
+  if (a.P * a.N >= 8192 && slices >= 2048) {
     hipLaunchKernelGGL((k_step<T, 512, 4>), dim3((unsigned)slices), dim3(512), 0, stream, a);
+  } else if (a.P * a.N >= 8192 && slices < 512) {
+    hipLaunchKernelGGL((k_step<T, 1024, 2>), dim3((unsigned)slices), dim3(1024), 0, stream, a);
   } else {
     hipLaunchKernelGGL((k_step<T, 256, 8>), dim3((unsigned)slices), dim3(256), 0, stream, a);
   }
