@@ -77,6 +77,9 @@ CASES = [
     (2, 130, 8, 16, 32, 2, 160, "bf16"),
     # 16 heads per group over 3 chunks: heads split over many workgroups
     (1, 384, 16, 32, 64, 1, 128, "f32"),
+    # a sequence shorter than one chunk, and a single token (R1 is then all pad but one)
+    (1, 50, 2, 32, 64, 1, 128, "f32"),
+    (2, 1, 3, 16, 32, 1, 64, "bf16"),
 ]
 
 
