@@ -401,8 +401,9 @@ def bench_backward(ssd, torch, w, reps=10):
             "flops_per_call": flops, "algorithmic_tflops": tflops,
             "mfma_fp32_frac": tflops / PEAK_TFLOPS["f32"],
             "workspace_bytes": ws.numel(),
-            "note": "gradients of every input; float32 matrix-core products for either io "
-                    "type; recomputes the forward chunk states"}
+            "note": "gradients of every input; recomputes the forward chunk states; the "
+                    "two scans run the io type's kernels, the gradient kernels float32 "
+                    "matrix-core products (mfma_fp32_frac prices all of it at the fp32 peak)"}
 
 
 def conv_bytes(Bt, T, D, K, es):

@@ -174,14 +174,16 @@ ssd_status ssd_chunk_scan(const ssd_scan_desc* desc, const void* x, const float*
  *
  * The adjoint state G_t = dL/dh_t obeys the same recurrence backwards in
  * time (G_t = dy_t (x) C_t + abar_{t+1} G_{t+1}).  The library recomputes the
- * forward chunk states and C B^T (float32), runs the scan itself over
- * reversed time with B and C exchanged (float32: G_t B_t for dx and the
- * adjoint at chunk boundaries), and forms dB, dC and the Delta gradient
- * chunk by chunk: per group, M = sum over its heads of (dy x^T) o decay o
- * Delta is built once on the matrix cores, dC = M B + dy H, dB = M^T C +
- * x Ghat, and dL/d(Delta A) comes from sums inside each chunk only (no sum
- * over the sequence cancels).  Every product is float32 on the matrix cores
- * whatever the io type.  No atomics: results are deterministic.
+ * forward chunk states and C B^T, runs the scan itself over reversed time
+ * with B and C exchanged (G_t B_t for dx, and the adjoint at chunk
+ * boundaries), both with the scan kernels of the io type (float32 states),
+ * and forms dB, dC and the Delta gradient chunk by chunk with float32
+ * matrix-core products: per group, M = sum over its heads of (dy x^T) o
+ * decay o Delta is built once, dC = M B + dy H, dB = M^T C + x Ghat, and
+ * dL/d(Delta A) comes from sums inside each chunk only (no sum over the
+ * sequence cancels).  With bfloat16 io the reversed scan's input dy / Delta
+ * and its output G B are rounded to bfloat16, as in the forward scan.  No
+ * atomics: results are deterministic.
  *
  *   inputs as ssd_chunk_scan; dy [Bt,T,H,P] io_dtype;
  *   dfinal_state [Bt,H,P,N] f32 or NULL (zero)

@@ -55,7 +55,9 @@ struct ScanSizes {
          ws_total = 0;
 };
 
-ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
+// force_phased: size (and run) the phased schedule even where the chain one
+// would be chosen (the gradients read the per-chunk states it leaves).
+ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s, bool force_phased = false) {
   if (!d) return SSD_ERR_INVALID_ARG;
   if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_DTYPE;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
@@ -84,8 +86,8 @@ ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s) {
       !mul_ok(d->chunk, d->chunk, &ll) || !mul_ok(bcg, ll, &cb_elems) ||
       !mul_ok(cb_elems, 4, &tmp))
     return SSD_ERR_UNSUPPORTED;
-  s->chain = ssd::scan_uses_chain(d->batch, d->nheads, d->headdim, d->dstate, d->chunk,
-                                  d->io_dtype == SSD_BF16);
+  s->chain = !force_phased && ssd::scan_uses_chain(d->batch, d->nheads, d->headdim, d->dstate,
+                                                   d->chunk, d->io_dtype == SSD_BF16);
   // the chain schedule keeps states on chip; the phased one needs S_c and alpha_c
   s->ws_state_bytes = s->chain ? 0 : round_up((size_t)ws_elems * 4, kAlign);
   s->ws_alpha_bytes = s->chain ? 0 : round_up((size_t)units * 4, kAlign);
@@ -106,13 +108,14 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
                      const float* dt_bias, const float* A, const void* B, const void* C,
                      const float* D, const float* initial_state, void* y, float* final_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream,
-                     hipEvent_t* events, int n_events, bool states_only = false) {
+                     hipEvent_t* events, int n_events, bool states_only = false,
+                     bool force_phased = false, bool keep_f32_states = false) {
   ScanSizes s;
-  ssd_status st = check_scan_desc(desc, &s);
+  ssd_status st = check_scan_desc(desc, &s, force_phased);
   if (st != SSD_OK) return st;
   // phases 0-2 alone (entering states and C B^T left in the workspace, no y):
-  // float32 phased schedule only
-  if (states_only && (desc->io_dtype != SSD_F32 || s.chain)) return SSD_ERR_UNSUPPORTED;
+  // phased schedule only
+  if (states_only && s.chain) return SSD_ERR_UNSUPPORTED;
   if (events) {
     if (n_events < SSD_SCAN_PHASES + 1) return SSD_ERR_INVALID_ARG;
     for (int k = 0; k <= SSD_SCAN_PHASES; ++k)
@@ -173,6 +176,7 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   a.dt_min = desc->dt_min; a.dt_max = desc->dt_max;
   a.chain = s.chain ? 1 : 0;
   a.states_only = states_only ? 1 : 0;
+  a.keep_f32_states = keep_f32_states ? 1 : 0;
   hipError_t e = desc->io_dtype == SSD_BF16
                      ? ssd::launch_scan_bf16(a, (int)desc->headdim, (int)desc->dstate, stream, events)
                      : ssd::launch_scan_f32(a, (int)desc->headdim, (int)desc->dstate, stream, events);
@@ -233,11 +237,11 @@ namespace {
 // ---------------------------------------------------------------------------
 enum BwdRegion {
   kScanWs, kScanWsR1, kWd, kCum, kDtr1, kR1x, kR1b, kR1c, kR1h0, kR1y, kR1final, kMix, kQrow,
-  kQcol, kUv, kDbcPart, kDdin, kDdp, kPart, kX32, kB32, kC32, kNumRegions
+  kQcol, kUv, kDbcPart, kDdin, kDdp, kPart, kNumRegions
 };
 
 struct BwdPlan {
-  ssd_scan_desc fw, r1;        // forward state scan and reversed scan R1, both float32
+  ssd_scan_desc fw, r1;        // forward state scan and reversed scan R1 (io type, phased)
   size_t scan_ws = 0;          // F0's workspace (entering states, decays, C B^T)
   size_t scan_ws_r1 = 0;       // R1's own (its entering states are read with F0's)
   size_t fwd_cb_off = 0;       // offset of C B^T in F0's workspace (after states and decays)
@@ -266,9 +270,9 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   // the kernels of the gradient stage one chunk per workgroup of 256 threads
   // and index (batch, token, head) rows in 32 bits
   if (d->chunk > 256 || s0.n_dt > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
-  // the forward states and R1 run in float32 whatever the io type
+  // both scans run the phased schedule of the io type and keep float32
+  // entering states in their workspaces
   pl->fw = *d;
-  pl->fw.io_dtype = SSD_F32;
   const int64_t Nc = (d->seqlen + d->chunk - 1) / d->chunk;
   pl->pad = Nc * d->chunk - d->seqlen;
   // R1 reads Delta' directly: no softplus, no bias, no clip
@@ -277,9 +281,8 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   pl->r1.dt_softplus = 0;
   pl->r1.dt_min = 0.0f;
   pl->r1.dt_max = FLT_MAX;
-  if ((st = check_scan_desc(&pl->fw, &sf)) != SSD_OK) return st;
-  if ((st = check_scan_desc(&pl->r1, &s1)) != SSD_OK) return st;
-  if (sf.chain || s1.chain) return SSD_ERR_UNSUPPORTED;   // float32 scans are phased
+  if ((st = check_scan_desc(&pl->fw, &sf, true)) != SSD_OK) return st;
+  if ((st = check_scan_desc(&pl->r1, &s1, true)) != SSD_OK) return st;
   pl->scan_ws = sf.ws_total;
   pl->scan_ws_r1 = s1.ws_total;
   pl->fwd_cb_off = sf.ws_state_bytes + sf.ws_alpha_bytes;
@@ -294,8 +297,8 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   head_split(hpg, bcg * nbt, 768, &pl->HS, &pl->hpw);
   head_split(hpg, bcg * 2 * pl->NS * pl->NB, 512, &pl->HSD, &pl->hpwd);
 
-  const bool bf = d->io_dtype == SSD_BF16;
-  const size_t nx = (size_t)s0.n_x, nbc = (size_t)s0.n_bc, nst = (size_t)s0.n_state;
+  const size_t es = io_size(d->io_dtype);
+  const size_t nst = (size_t)s0.n_state, nbc = (size_t)s0.n_bc;
   const size_t ndt = (size_t)s0.n_dt;
   const size_t nx1 = (size_t)s1.n_x, nbc1 = (size_t)s1.n_bc, ndt1 = (size_t)s1.n_dt;  // R1, padded
   const size_t LP = (size_t)pl->LP, NB = (size_t)pl->NB;
@@ -305,11 +308,11 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   sizes[kWd] = ndt * 4;
   sizes[kCum] = ndt * 8;
   sizes[kDtr1] = ndt1 * 4;
-  sizes[kR1x] = nx1 * 4;
-  sizes[kR1b] = nbc1 * 4;
-  sizes[kR1c] = nbc1 * 4;
+  sizes[kR1x] = nx1 * es;
+  sizes[kR1b] = nbc1 * es;
+  sizes[kR1c] = nbc1 * es;
   sizes[kR1h0] = nst * 4;
-  sizes[kR1y] = nx1 * 4;
+  sizes[kR1y] = nx1 * es;
   sizes[kR1final] = nst * 4;
   sizes[kMix] = (size_t)bcg * pl->HS * LP * LP * 4;
   sizes[kQrow] = (size_t)(Bt * Nc * H) * NB * NB * 128 * 4;
@@ -319,9 +322,6 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   sizes[kDdin] = ndt * 4;
   sizes[kDdp] = ndt * 4;
   sizes[kPart] = 3 * (size_t)(Bt * Nc * H) * 4;
-  sizes[kX32] = bf ? nx * 4 : 0;
-  sizes[kB32] = bf ? nbc * 4 : 0;
-  sizes[kC32] = bf ? nbc * 4 : 0;
   size_t at = 0;
   for (int k = 0; k < kNumRegions; ++k) {
     pl->off[k] = at;
@@ -543,11 +543,9 @@ ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* d, const void* x, const 
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
   a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state;
   const bool bf = d->io_dtype == SSD_BF16;
-  a.x32 = bf ? atf(kX32) : nullptr; a.b32 = bf ? atf(kB32) : nullptr;
-  a.c32 = bf ? atf(kC32) : nullptr;
   a.wd = atf(kWd); a.cum = reinterpret_cast<double*>(w + pl.off[kCum]); a.dtr1 = atf(kDtr1);
-  a.r1_x = atf(kR1x); a.r1_b = atf(kR1b); a.r1_c = atf(kR1c); a.r1_h0 = atf(kR1h0);
-  a.r1_y = atf(kR1y); a.r1_final = atf(kR1final);
+  a.r1_x = at(kR1x); a.r1_b = at(kR1b); a.r1_c = at(kR1c); a.r1_h0 = atf(kR1h0);
+  a.r1_y = at(kR1y); a.r1_final = atf(kR1final);
   a.fwd_state = atf(kScanWs);
   a.fwd_cb = reinterpret_cast<const float*>(w + pl.off[kScanWs] + pl.fwd_cb_off);
   a.r1_state = atf(kScanWsR1);
@@ -565,14 +563,16 @@ ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* d, const void* x, const 
   a.dt_min = d->dt_min; a.dt_max = d->dt_max;
 
   if (ssd::launch_backward_phase(a, bf, 0, stream) != hipSuccess) return SSD_ERR_HIP;
-  // forward states in float32: C B^T and the state entering each chunk
-  st = scan_impl(&pl.fw, bf ? a.x32 : x, dt, dt_bias, A, bf ? a.b32 : B, bf ? a.c32 : C, D,
-                 initial_state, nullptr, nullptr, at(kScanWs), pl.scan_ws, stream, nullptr, 0,
-                 true);
+  // forward states (phased schedule of the io type): C B^T and the float32
+  // state entering each chunk
+  st = scan_impl(&pl.fw, x, dt, dt_bias, A, B, C, D, initial_state, nullptr, nullptr,
+                 at(kScanWs), pl.scan_ws, stream, nullptr, 0, true, true, true);
   if (st != SSD_OK) return st;
-  // R1: sum_n G B over reversed time; its final state is dL/dh_{-1} / abar_0
-  st = ssd_chunk_scan(&pl.r1, a.r1_x, a.dtr1, nullptr, A, a.r1_b, a.r1_c, nullptr, a.r1_h0,
-                      at(kR1y), atf(kR1final), at(kScanWsR1), pl.scan_ws_r1, stream);
+  // R1: sum_n G B over reversed time; its entering states are the adjoint at
+  // the forward chunk boundaries and its final state dL/dh_{-1} / abar_0
+  st = scan_impl(&pl.r1, a.r1_x, a.dtr1, nullptr, A, a.r1_b, a.r1_c, nullptr, a.r1_h0,
+                 at(kR1y), atf(kR1final), at(kScanWsR1), pl.scan_ws_r1, stream, nullptr, 0,
+                 false, true, true);
   if (st != SSD_OK) return st;
   if (ssd::launch_backward_phase(a, bf, 1, stream) != hipSuccess) return SSD_ERR_HIP;
   return SSD_OK;

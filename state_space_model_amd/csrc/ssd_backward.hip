@@ -1,5 +1,5 @@
 // Gradients of the chunked scan for gfx950 (ssd_chunk_scan_backward): the
-// kernels around the two float32 scans the host runs.
+// kernels around the two scans the host runs.
 //
 // Source: "Compiler-First State Space Duality and Portable O(1)
 // Autoregressive Caching", Background (Eq. 2-3: the recurrence and its
@@ -25,8 +25,9 @@
 //   (sums inside the chunk only: no term cancels against another across the sequence)
 //   dd_t = A dL/da_t + x_t . (G_t B_t),  ddt_t = dd_t softplus'(z_t) where Delta is not clipped,
 //   dA = sum_t d_t dL/da_t,  dD = sum_t dy_t . x_t,  dh0 = abar_0 G_0.
-// The host runs the forward scan's state phases in float32 (H_c and C B^T
-// stay in its workspace) and R1, the scan itself over reversed time: reversed
+// The host runs the forward scan's state phases (H_c, kept in float32, and
+// C B^T stay in its workspace) and R1, the scan itself over reversed time, both
+// with the phased kernels of the io type: reversed
 // position T-1-t has the decay of step t+1 and the input dy_t / d_{t+1} (the
 // scan multiplies its input by its Delta), with B and C exchanged, so its
 // outputs are G_t B_t and its entering states the G at chunk boundaries; pad =
@@ -36,6 +37,8 @@
 // B[k][l%16] and D[4(l/16)+r][l%16]; the contraction index of four
 // consecutive instructions is k = 16 blk + 4 (l/16) + e, e = 0..3, so each
 // lane reads one float4 of a row-major operand per four instructions.
+#include <type_traits>
+
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -90,6 +93,18 @@ __device__ __forceinline__ void ldk(const T* p, bool ok, float (&v)[KK]) {
   } else {
     const float f = to_f32(p[0]);
     v[0] = ok ? f : 0.f;
+  }
+}
+
+// Four consecutive elements to memory in the io type (aligned to 4 elements).
+template <typename T>
+__device__ __forceinline__ void st4_io(T* p, float4 v) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = v;
+  } else {
+    bf16x4 w;
+    w[0] = (bf16)v.x; w[1] = (bf16)v.y; w[2] = (bf16)v.z; w[3] = (bf16)v.w;
+    *reinterpret_cast<bf16x4*>(p) = w;
   }
 }
 
@@ -165,8 +180,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_delta(BwdArgs a) {
 }
 
 // One thread per four head columns of a (b, t, h) row: R1's input
-// dy_t / Delta_{t+1} (0 for the last token) at R1 position pad + T-1-t, and
-// the float32 copy of x for the state scan (bfloat16 io).  `sh` = log2(P/4).
+// dy_t / Delta_{t+1} (0 for the last token) at R1 position pad + T-1-t, in the
+// io type (R1 runs the scan kernels of that type).  `sh` = log2(P/4).
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_x(BwdArgs a, int sh) {
   const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
@@ -184,14 +199,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_x(BwdArgs a, int sh) {
   const float4 v = ld4_io<T>(reinterpret_cast<const T*>(a.dy) + rp, true);
   const float4 r = has_next ? make_float4(v.x / dn, v.y / dn, v.z / dn, v.w / dn)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
-  *reinterpret_cast<float4*>(a.r1_x + ((b * T1 + tr1) * a.H + h) * P + 4 * pq) = r;
-  if (a.x32)
-    *reinterpret_cast<float4*>(a.x32 + rp) = ld4_io<T>(reinterpret_cast<const T*>(a.x) + rp, true);
+  st4_io<T>(reinterpret_cast<T*>(a.r1_x) + ((b * T1 + tr1) * a.H + h) * P + 4 * pq, r);
 }
 
 // One thread per four state columns of a (b, t, g) row: R1's B and C (C and
-// B, reversed), and the float32 copies of B and C (bfloat16 io).
-// `sh` = log2(N/4).
+// B, reversed), copied in the io type.  `sh` = log2(N/4).
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_bc(BwdArgs a, int sh) {
   const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
@@ -204,26 +216,25 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_bc(BwdArgs a, int sh) 
   const int N = a.N;
   const int64_t rn = (int64_t)row32 * N + 4 * nq;
   const int64_t rn1 = ((b * T1 + tr1) * a.G + g) * N + 4 * nq;
-  const float4 bv = ld4_io<T>(reinterpret_cast<const T*>(a.B) + rn, true);
-  const float4 cv = ld4_io<T>(reinterpret_cast<const T*>(a.C) + rn, true);
-  *reinterpret_cast<float4*>(a.r1_b + rn1) = cv;
-  *reinterpret_cast<float4*>(a.r1_c + rn1) = bv;
-  if (a.b32) {
-    *reinterpret_cast<float4*>(a.b32 + rn) = bv;
-    *reinterpret_cast<float4*>(a.c32 + rn) = cv;
-  }
+  using V = typename std::conditional<sizeof(T) == 4, float4, bf16x4>::type;
+  const V bv = *reinterpret_cast<const V*>(reinterpret_cast<const T*>(a.B) + rn);
+  const V cv = *reinterpret_cast<const V*>(reinterpret_cast<const T*>(a.C) + rn);
+  *reinterpret_cast<V*>(reinterpret_cast<T*>(a.r1_b) + rn1) = cv;
+  *reinterpret_cast<V*>(reinterpret_cast<T*>(a.r1_c) + rn1) = bv;
 }
 
 // The pad positions of R1 (reversed positions 0 .. pad-1) hold no token.
+template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_zero_pad(BwdArgs a, int64_t per_b) {
   const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
   if (e >= a.Bt * per_b) return;
   const int64_t b = e / per_b, r = e % per_b;
   const int64_t T1 = a.T + a.pad;
-  if (r < a.pad * a.H * a.P) a.r1_x[b * T1 * a.H * a.P + r] = 0.0f;
+  const T z = to_io<T>(0.0f);
+  if (r < a.pad * a.H * a.P) reinterpret_cast<T*>(a.r1_x)[b * T1 * a.H * a.P + r] = z;
   if (r < a.pad * a.G * a.N) {
-    a.r1_b[b * T1 * a.G * a.N + r] = 0.0f;
-    a.r1_c[b * T1 * a.G * a.N + r] = 0.0f;
+    reinterpret_cast<T*>(a.r1_b)[b * T1 * a.G * a.N + r] = z;
+    reinterpret_cast<T*>(a.r1_c)[b * T1 * a.G * a.N + r] = z;
   }
 }
 
@@ -757,7 +768,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a, int sh) {
   // threads past the last row read row 0 and store nothing
   const float4 xv = ld4_io<T>(reinterpret_cast<const T*>(a.x) + rp, true);
   const float4 dyv = ld4_io<T>(reinterpret_cast<const T*>(a.dy) + rp, true);
-  const float4 gb = ld4_io<float>(a.r1_y + rpr1, true);   // sum_n G[p,n] B_t[n]
+  const float4 gb = ld4_io<T>(reinterpret_cast<const T*>(a.r1_y) + rpr1, true);   // sum_n G[p,n] B_t[n]
   if (ok)
     *reinterpret_cast<float4*>(a.dx + rp) =
         make_float4(__fmaf_rn(Dh, dyv.x, d * gb.x), __fmaf_rn(Dh, dyv.y, d * gb.y),
@@ -936,7 +947,7 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
       if (a.pad > 0) {
         const int64_t hp = a.pad * a.H * a.P, gn = a.pad * a.G * a.N;
         const int64_t per_b = hp > gn ? hp : gn;
-        hipLaunchKernelGGL(k_bwd_zero_pad, dim3(blocks_of(a.Bt * per_b, kBwdThreads)),
+        hipLaunchKernelGGL(k_bwd_zero_pad<T>, dim3(blocks_of(a.Bt * per_b, kBwdThreads)),
                            dim3(kBwdThreads), 0, s, a, per_b);
       }
       hipLaunchKernelGGL(k_bwd_init_states<T>,

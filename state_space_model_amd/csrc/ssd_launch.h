@@ -28,6 +28,8 @@ struct ScanArgs {
   float dt_min, dt_max;
   int32_t chain;          // 1: chain schedule (bfloat16 only), 0: phased
   int32_t states_only;    // 1: phases 0-2 only (C B^T, chunk and entering states; no y)
+  int32_t keep_f32_states; // bf16 phased: the state pass also writes the float32 entering
+                           // states over ws_state (the gradients read them)
 };
 
 struct StepArgs {
@@ -72,21 +74,18 @@ struct BwdArgs {
   const float* h0;          // [Bt,H,P,N] or null
   const void* dy;           // [Bt,T,H,P] io
   const float* dfinal;      // [Bt,H,P,N] or null
-  // float32 copies of x, B, C for the float32 state scan (bfloat16 io only, else null)
-  float* x32;               // [Bt,T,H,P]
-  float* b32;               // [Bt,T,G,N]
-  float* c32;               // [Bt,T,G,N]
   // Delta, its chunk-local prefix, and the operands and results of the reversed scan R1
+  // (in the io type: R1 runs the scan kernels of that type)
   float* wd;                // [Bt,T,H] Delta
   double* cum;              // [Bt,T,H] sum of Delta A from the chunk start to the token (inclusive)
   float* dtr1;              // [Bt,T+pad,H] Delta' of R1: d_t at reversed position pad+T-t
-  float* r1_x;              // [Bt,T+pad,H,P] reversed dy_t / Delta_{t+1}
-  float* r1_b;              // [Bt,T+pad,G,N] reversed C
-  float* r1_c;              // [Bt,T+pad,G,N] reversed B
+  void* r1_x;               // [Bt,T+pad,H,P] io  reversed dy_t / Delta_{t+1}
+  void* r1_b;               // [Bt,T+pad,G,N] io  reversed C
+  void* r1_c;               // [Bt,T+pad,G,N] io  reversed B
   float* r1_h0;             // [Bt,H,P,N]     dfinal + dy_{T-1} (x) C_{T-1}
-  const float* r1_y;        // [Bt,T+pad,H,P] sum_n G B (reversed positions)
+  const void* r1_y;         // [Bt,T+pad,H,P] io  sum_n G B (reversed positions)
   const float* r1_final;    // [Bt,H,P,N]     dL/dh_{-1} / abar_0
-  // entering states and C B^T tiles the float32 scans leave in their workspaces
+  // entering states (float32) and C B^T tiles the two scans leave in their workspaces
   const float* fwd_state;   // [Bt,H,Nc,P,N] state entering forward chunk c (H_c)
   const float* fwd_cb;      // [Bt,Nc,G,L,L] C B^T of each forward chunk
   const float* r1_state;    // [Bt,H,Nc,P,N] state entering reversed chunk c' (G at (Nc-c')L)
@@ -155,8 +154,8 @@ bool conv_shape_supported(int64_t Bt, int64_t T, int64_t D);
 hipError_t launch_conv(const ConvArgs& a, bool io_bf16, bool step, hipStream_t stream);
 
 // Backward pass pieces: phase 0 prepares Delta, its chunk-local prefix and the
-// reversed operands and initial state of R1; phase 1 (after the float32
-// forward state scan and R1) forms every gradient.
+// reversed operands and initial state of R1; phase 1 (after the forward state
+// scan and R1) forms every gradient.
 hipError_t launch_backward_phase(const BwdArgs& a, bool io_bf16, int phase, hipStream_t stream);
 hipError_t launch_backward_zero_heads(float* dA, float* ddt_bias, float* dD, int64_t H,
                                       hipStream_t stream);

@@ -913,6 +913,7 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
   if ((e = rec(2)) != hipSuccess) return e;
   if ((e = launch_state_pass(a, P, N, stream, true)) != hipSuccess) return e;
   if ((e = rec(3)) != hipSuccess) return e;
+  if (a.states_only) return rec(4);   // entering states and C B^T only
   if (a.L <= 256) {
     hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 256>), dim3((unsigned)units), dim3(kThreads), 0,
                        stream, a);

@@ -13,8 +13,8 @@
 // Element-wise over the P x N state of every (batch, head), sequential over
 // chunks.  The workspace holds S_c on entry; the state entering chunk c,
 // h_{c-1}, is written over it in float32 or, for the bfloat16 output kernel
-// (which only uses it rounded to bfloat16), to a separate bf16 region; the
-// last state goes to final_state.  One lane owns one
+// (which only uses it rounded to bfloat16), to a separate bf16 region (and,
+// when asked, in float32 over it too); the last state goes to final_state.  One lane owns one
 // float4 of a state and keeps it in registers across all chunks; the chunk
 // states it reads are issued in batches of 16 so their latency overlaps.
 #include "ssd_prefill_common.h"
@@ -29,7 +29,7 @@ template <bool BF16_OUT>
 __global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const float* ws_alpha,
                                                          bf16* ws_hb, const float* h0,
                                                          float* final_state, int64_t BH,
-                                                         int64_t Nc, int PN) {
+                                                         int64_t Nc, int PN, int keep_f32) {
   const int PN4 = PN / 4;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= BH * PN4) return;
@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const 
           bf16x4 v;
           v[0] = (bf16)hc.x; v[1] = (bf16)hc.y; v[2] = (bf16)hc.z; v[3] = (bf16)hc.w;
           hb[(c0 + k) * PN4] = v;
+          if (keep_f32) st[(c0 + k) * PN4] = hc;   // this batch's S_c are already loaded
         } else {
           st[(c0 + k) * PN4] = hc;
         }
@@ -84,11 +85,11 @@ hipError_t launch_state_pass(const ScanArgs& a, int P, int N, hipStream_t stream
     hipLaunchKernelGGL(prefill::k_state_pass<true>, dim3((unsigned)blocks), dim3(prefill::kThreads),
                        0, stream, a.ws_state, (const float*)a.ws_alpha,
                        reinterpret_cast<bf16*>(a.ws_hb), a.h0, a.final_state, a.Bt * a.H, a.Nc,
-                       PN);
+                       PN, a.keep_f32_states);
   } else {
     hipLaunchKernelGGL(prefill::k_state_pass<false>, dim3((unsigned)blocks),
                        dim3(prefill::kThreads), 0, stream, a.ws_state, (const float*)a.ws_alpha,
-                       nullptr, a.h0, a.final_state, a.Bt * a.H, a.Nc, PN);
+                       nullptr, a.h0, a.final_state, a.Bt * a.H, a.Nc, PN, 0);
   }
   return hipGetLastError();
 }

@@ -262,7 +262,9 @@ def test_backward_of_a_split_sequence(io):
     def rel(a_, b_):
         return float((a_.double() - b_.double()).abs().max() / b_.double().abs().max())
 
-    bar = 1e-4
+    # bf16: each side rounds the reversed scan's operands and outputs to
+    # bfloat16 along its own chunk grid, so they agree to the bf16 bar only
+    bar = TOL[io]
     for k in ("dx", "ddt", "dB", "dC"):
         cat = torch.cat([first[k], second[k]], 1)
         assert rel(cat, whole[k]) <= bar, (k, rel(cat, whole[k]))
