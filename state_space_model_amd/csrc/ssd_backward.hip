@@ -354,25 +354,34 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
   // are loaded into registers while this head's are consumed.  Rows past the
   // chunk read its last row: finite values whose products the causal select
   // below discards.
-  constexpr int XS = P + 4;                       // padded LDS row
-  constexpr int RQ = P / 4;                       // float4 per row
-  constexpr int SL = 2 * 64 * RQ / kBwdThreads;   // float4 per thread per head
-  __shared__ __attribute__((aligned(16))) float s_op[2][2 * 64 * XS];
-  auto load_stage = [&](int64_t h, float4 (&st)[SL]) {
+  // bfloat16 rows (P a multiple of 32) go to the bf16 matrix cores as they
+  // are: products of two bf16 values are exact in float32, so S is the same
+  // up to the order of its sums.  Otherwise they are staged as float32.
+  constexpr bool kB = sizeof(T) == 2 && P % 32 == 0;
+  using ST = typename std::conditional<kB, bf16, float>::type;
+  using VT = typename std::conditional<kB, uint4, float4>::type;
+  constexpr int EPV = kB ? 8 : 4;                 // elements per 16-byte vector
+  constexpr int XS = P + EPV;                     // padded LDS row
+  constexpr int RQ = P / EPV;                     // vectors per row
+  constexpr int SL = 2 * 64 * RQ / kBwdThreads;   // vectors per thread per head
+  __shared__ __attribute__((aligned(16))) ST s_op[2][2 * 64 * XS];
+  auto load_stage = [&](int64_t h, VT (&st)[SL]) {
 #pragma unroll
     for (int k = 0; k < SL; ++k) {
       const int e = tid + k * kBwdThreads, which = e / (64 * RQ), rem = e % (64 * RQ);
       const int row = rem / RQ, p4 = rem % RQ;
       const int grow = min((which ? 64 * J : 64 * I) + row, Lc - 1);
-      st[k] = ld4_io<T>((which ? xg : dyg) + (int64_t)grow * xrs + h * P + 4 * p4, true);
+      const T* src = (which ? xg : dyg) + (int64_t)grow * xrs + h * P + EPV * p4;
+      if constexpr (kB) st[k] = *reinterpret_cast<const uint4*>(src);
+      else st[k] = ld4_io<T>(src, true);
     }
   };
-  auto store_stage = [&](int buf, const float4 (&st)[SL]) {
+  auto store_stage = [&](int buf, const VT (&st)[SL]) {
 #pragma unroll
     for (int k = 0; k < SL; ++k) {
       const int e = tid + k * kBwdThreads, which = e / (64 * RQ), rem = e % (64 * RQ);
       const int row = rem / RQ, p4 = rem % RQ;
-      *reinterpret_cast<float4*>(&s_op[buf][(which * 64 + row) * XS + 4 * p4]) = st[k];
+      *reinterpret_cast<VT*>(&s_op[buf][(which * 64 + row) * XS + EPV * p4]) = st[k];
     }
   };
   struct Dec {
@@ -388,25 +397,44 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
       o.dj[s] = wdg[(int64_t)min(jb[s], Lc - 1) * a.H + h];   // masked with the decay
     }
   };
-  auto process = [&](int64_t h, const float* so, const Dec& o) {
+  auto process = [&](int64_t h, const ST* so, const Dec& o) {
     f32x4 sv[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int v = 0; v < 2; ++v) sv[s][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kB) {
+      // v_mfma_f32_16x16x32_bf16: lane (q, r16) holds k-slots 32 kb + 8 q .. +7
 #pragma unroll
-    for (int pb = 0; pb < P / 16; ++pb) {
-      float4 dv[2], xv[2];
+      for (int kb = 0; kb < P / 32; ++kb) {
+        bf16x8 dv[2], xv[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        dv[s] = *reinterpret_cast<const float4*>(&so[(32 * wr + 16 * s + r16) * XS + 16 * pb + 4 * q]);
-        xv[s] = *reinterpret_cast<const float4*>(
-            &so[(64 + 32 * wc + 16 * s + r16) * XS + 16 * pb + 4 * q]);
+        for (int s = 0; s < 2; ++s) {
+          dv[s] = *reinterpret_cast<const bf16x8*>(&so[(32 * wr + 16 * s + r16) * XS + 32 * kb + 8 * q]);
+          xv[s] = *reinterpret_cast<const bf16x8*>(
+              &so[(64 + 32 * wc + 16 * s + r16) * XS + 32 * kb + 8 * q]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int v = 0; v < 2; ++v)
+            sv[s][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dv[s], xv[v], sv[s][v], 0, 0, 0);
       }
+    } else {
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int pb = 0; pb < P / 16; ++pb) {
+        float4 dv[2], xv[2];
 #pragma unroll
-        for (int v = 0; v < 2; ++v) sv[s][v] = mfma4(dv[s], xv[v], sv[s][v]);
+        for (int s = 0; s < 2; ++s) {
+          dv[s] = *reinterpret_cast<const float4*>(&so[(32 * wr + 16 * s + r16) * XS + 16 * pb + 4 * q]);
+          xv[s] = *reinterpret_cast<const float4*>(
+              &so[(64 + 32 * wc + 16 * s + r16) * XS + 16 * pb + 4 * q]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int v = 0; v < 2; ++v) sv[s][v] = mfma4(dv[s], xv[v], sv[s][v]);
+      }
     }
     float rowp[2][4], colp[2] = {0.f, 0.f};
 #pragma unroll
@@ -449,7 +477,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
     }
   };
   {
-    float4 st[SL];
+    VT st[SL];
     Dec cur, nxt;
     load_stage(hb, st);
     load_dec(hb, cur);
