@@ -271,3 +271,22 @@ def test_backward_of_a_split_sequence(io):
     for k in ("dA", "dD", "ddt_bias"):
         assert rel(first[k] + second[k], whole[k]) <= bar, k
     assert rel(first["dinitial_state"], whole["dinitial_state"]) <= bar
+
+
+@pytest.mark.parametrize("case", [(1, 2048, 64, 8, "f32"), (4, 1024, 64, 8, "bf16")],
+                         ids=lambda c: "_".join(map(str, c)))
+def test_backward_groups_at_scale(case):
+    """G > 1 at layer scale (8 B/C groups of 8 heads, P = 64, N = 128,
+    L = 256) against the oracle in full: dB and dC sum over a group's heads,
+    whose products with B and C are taken once per group.  The bf16 case has
+    256 (batch, head) chains, where the forward scan would take the chain
+    schedule; the gradients run the phased one."""
+    need_gpu()
+    Bt, T, H, G, io = case
+    w = make_tiny(Bt, T, H, 64, 128, G, 256, io, seed=6800 + T + Bt)
+    announce(f"backward groups at scale {case}")
+    got, ref = run_case(w, 6810 + Bt)
+    errs = grad_errors(got, ref)
+    print(case, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= TOL[io]}
+    assert not bad, bad
