@@ -290,3 +290,28 @@ def test_backward_groups_at_scale(case):
     print(case, {k: f"{v:.2e}" for k, v in errs.items()})
     bad = {k: v for k, v in errs.items() if not v <= TOL[io]}
     assert not bad, bad
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_backward_every_optional_input_absent(io):
+    """dt_bias, D, the initial state and dfinal all absent (NULL through the
+    C ABI): gradients against the oracle with the same inputs absent (zero
+    bias, no skip term, zero initial state, zero dfinal)."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = make_tiny(2, 300, 4, 32, 64, 2, 128, io, seed=6900)
+    announce(f"backward optional inputs absent {io}")
+    inp = make_inputs(w)
+    g = torch.Generator().manual_seed(6901)
+    dy = torch.randn(inp["x"].shape, generator=g).to(inp["x"].dtype)
+    d = to_dev(inp)
+    got = ssd.ssd_chunk_scan_backward(d["x"], d["dt"], d["A"], d["B"], d["C"], None,
+                                      dy=dy.to("cuda"), chunk=w.chunk)
+    torch.cuda.synchronize()
+    ref = oracle.scan_backward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None,
+                               None, dy=dy.double().numpy(), dt_softplus=True,
+                               dt_min=w.dt_min, dt_max=w.dt_max)
+    errs = {k: v for k, v in grad_errors(got, ref).items() if k not in ("dD", "ddt_bias")}
+    print(io, {k: f"{v:.2e}" for k, v in errs.items()})
+    bad = {k: v for k, v in errs.items() if not v <= TOL[io]}
+    assert not bad, bad
