@@ -60,8 +60,8 @@ TRAFFIC = {
     ("chunk_out/f32", "m130_f32"): (41.16e6 + 30.57e6, "1ca538f3919d2260"),
     ("decode", "m2p7_decode_b64"): (169.13e6 + 168.44e6, "52c5cda5fcfeee0e"),
     # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
-    ("conv1d", "conv_m2p7_bf16"): (49.19e6 + 44.07e6, "9c6f061da92854fb"),
-    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "9c6f061da92854fb"),
+    ("conv1d", "conv_m2p7_bf16"): (49.18e6 + 44.07e6, "f00255d06cc64912"),
+    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "f00255d06cc64912"),
 }
 COPY_CALIBRATION_BYTES = 1 << 30
 

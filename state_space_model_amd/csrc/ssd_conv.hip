@@ -78,6 +78,22 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[VEC]) {
   }
 }
 
+// The same for y, which nothing re-reads: non-temporal stores (no cache
+// allocation for the stream).
+template <typename T, int VEC>
+__device__ __forceinline__ void store_vec_stream(T* p, const float (&v)[VEC]) {
+  if constexpr (VEC == 1) {
+    __builtin_nontemporal_store(to_io<T>(v[0]), p);
+  } else if constexpr (sizeof(T) == 4) {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+  } else {
+    bf16x4 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) h[e] = (bf16)v[e];  // round to nearest even
+    __builtin_nontemporal_store(__builtin_bit_cast(uint64_t, h), reinterpret_cast<uint64_t*>(p));
+  }
+}
+
 // silu(z) = z * logistic(z), logistic(z) = 1 / (1 + 2^(-z log2 e)) on the
 // hardware base-2 exponential and reciprocal (about 1 ulp each; the
 // accurate library exp and IEEE division cost some 30 instructions per
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(kConvThreads) void k_conv(ConvArgs a, int32_t NG, i
       unpack<T, VEC>(rx[t], xw[K - 1]);
       float out[VEC];
       conv_point<K, VEC>(w, bs, xw, a.silu, out);
-      store_vec<T, VEC>(yb + (t0 + t) * D, out);
+      store_vec_stream<T, VEC>(yb + (t0 + t) * D, out);
 #pragma unroll
       for (int jj = 0; jj < K - 1; ++jj)
 #pragma unroll
@@ -225,7 +241,7 @@ __global__ __launch_bounds__(kConvThreads) void k_conv_step(ConvArgs a, int32_t 
   load_weights<K, VEC>(a, c0, w, bs);
   float out[VEC];
   conv_point<K, VEC>(w, bs, xp, a.silu, out);
-  store_vec<T, VEC>(reinterpret_cast<T*>(a.y) + b * D + c0, out);
+  store_vec_stream<T, VEC>(reinterpret_cast<T*>(a.y) + b * D + c0, out);
   // shift: the oldest input drops out, x_t enters as the newest
 #pragma unroll
   for (int v = 0; v < VEC; ++v)
