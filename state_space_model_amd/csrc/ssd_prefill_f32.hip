@@ -255,10 +255,13 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_f32(ScanArgs a,
 // rather than y puts four consecutive head columns of one token in each lane:
 // the skip term and the store are float4 accesses.
 //
-// Order: the x loads are issued first and land while the inter-chunk term
-// (which needs only h_{c-1} and C) runs on the matrix cores; its decay
-// exp(cum_i) is applied to the accumulators afterwards, once the prefix sum
-// is known.  Then x is staged, and the intra-chunk term runs.
+// Order: the inter-chunk term needs only h_{c-1} and C, the staging (prefix
+// sum, x into LDS, decay tables) only dt and x, so they run in either order
+// (below); the inter-chunk decay exp(cum_i) is applied to the accumulators
+// once both are done, and then the intra-chunk term runs.  A wavefront's
+// loads complete in issue order, so a workgroup that starts with the
+// inter-chunk term issues its x loads only after it: issued first, they
+// would hold back the h and C loads behind them.
 //
 // Decay factors.  For a token in 64-token block R > 0 and a key j in an
 // earlier block, exp(cum_i - cum_j) = exp(cum_i - cum_r) * exp(cum_r - cum_j)
@@ -303,18 +306,20 @@ void k_chunk_out_f32(ScanArgs a) {
     vk[k] = Ik[k] < nrt;
   }
 
-  // dt of the chunk and x of this workgroup's PW columns for every chunk row:
-  // loads issued now, consumed by the staging
+  // x of this workgroup's PW columns for every chunk row, loaded into
+  // registers ahead of the staging that writes it to LDS
   constexpr int XQ = PW / 4;
   constexpr int XLB = (LMAX * XQ + kThreads - 1) / kThreads;
   const int nx = nrt * 16 * XQ;
   float4 xv_stage[XLB];
+  auto load_x = [&]() {
 #pragma unroll
-  for (int i = 0; i < XLB; ++i) {
-    const int e = i * kThreads + tid, j = e / XQ, m = e % XQ;
-    xv_stage[i] = ld4_masked(&xg[((b * a.T + t0 + min(j, Lc - 1)) * a.H + h) * P + p0 + 4 * m],
-                             e < nx && j < Lc);
-  }
+    for (int i = 0; i < XLB; ++i) {
+      const int e = i * kThreads + tid, j = e / XQ, m = e % XQ;
+      xv_stage[i] = ld4_masked(&xg[((b * a.T + t0 + min(j, Lc - 1)) * a.H + h) * P + p0 + 4 * m],
+                               e < nx && j < Lc);
+    }
+  };
 
   const float2 dtv = chunk_dt_load(a, b, c, h);
 
@@ -391,10 +396,12 @@ void k_chunk_out_f32(ScanArgs a) {
   // (blockIdx % 8 picks the XCD, the rest the unit), so the round's parity
   // is what differs between the workgroups of one unit.
   if ((blockIdx.x >> 8) & 1) {
+    load_x();
     stage();
     inter();
   } else {
     inter();
+    load_x();
     stage();
   }
 
