@@ -57,7 +57,7 @@ KERNEL_SOURCES = {
 # HBM bytes per launch from the counter runs: (kernel key, workload) -> (bytes, digest)
 TRAFFIC = {
     # counter runs and calibration: profiles/chunk_out_f32_m130_f32_decode_m2p7_b64_hbm_bytes.txt
-    ("chunk_out/f32", "m130_f32"): (37.76e6 + 30.41e6, "d10491345d7c8482"),
+    ("chunk_out/f32", "m130_f32"): (38.19e6 + 30.45e6, "56909f5168ee5332"),
     ("decode", "m2p7_decode_b64"): (169.13e6 + 168.44e6, "52c5cda5fcfeee0e"),
     # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
     ("conv1d", "conv_m2p7_bf16"): (49.18e6 + 44.07e6, "f00255d06cc64912"),

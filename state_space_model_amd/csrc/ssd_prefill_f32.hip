@@ -150,11 +150,14 @@ __device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int ntiles, i
       if (e < KB * BQ) st4(&sb[l * BS + 4 * m], br[i]);
     }
   };
-  // two token blocks are always in flight ahead of the one being consumed
+  // Two token blocks are always in flight ahead of the one being consumed.
+  // The loads are unconditional (rows past the chunk's end are clamped and
+  // zeroed), so every path has the same loads in flight and each wait covers
+  // exactly the block about to be staged.
   const float2 dtv = chunk_dt_load(a, b, c, h);
   float4 xA[XL], bA[BL], xB[XL], bB[BL];
   load_block(0, xA, bA);
-  if (KB < Lc) load_block(KB, xB, bB);
+  load_block(KB, xB, bB);
 
   {
     const DeltaScan ds = chunk_scan_stage1(a, c, h, dtv, s_wsum);
@@ -203,12 +206,12 @@ __device__ __forceinline__ void chunk_state_f32(const ScanArgs& a, int ntiles, i
   for (int kb0 = 0; kb0 < Lc; kb0 += 2 * KB) {
     store_block(kb0, xA, bA, s_x0, s_b0);
     __syncthreads();
-    if (kb0 + 2 * KB < Lc) load_block(kb0 + 2 * KB, xA, bA);
+    load_block(kb0 + 2 * KB, xA, bA);
     compute(s_x0, s_b0);
     if (kb0 + KB >= Lc) break;
     store_block(kb0 + KB, xB, bB, s_x1, s_b1);
     __syncthreads();
-    if (kb0 + 3 * KB < Lc) load_block(kb0 + 3 * KB, xB, bB);
+    load_block(kb0 + 3 * KB, xB, bB);
     compute(s_x1, s_b1);
   }
   if (active) {
@@ -357,16 +360,15 @@ void k_chunk_out_f32(ScanArgs a) {
         }
       }
     };
-    float4 hA[TP], cA[RT], hB[TP], cB[RT];
-    load_nb(0, hA, cA);
-#pragma unroll 1
-    for (int nb = 0; nb < N / 16; nb += 2) {
-      const bool two = nb + 1 < N / 16;     // N / 16 is 1 for N = 16
-      if (two) load_nb(nb + 1, hB, cB);
-      mma_nb(hA, cA);
-      if (!two) break;
-      if (nb + 2 < N / 16) load_nb(nb + 2, hA, cA);
-      mma_nb(hB, cB);
+    // Unrolled, so that the same loads are in flight on every path: the
+    // compiler then waits for exactly the n-block being consumed (after a
+    // conditional load it waits for every load).
+    float4 hs[2][TP], cs[2][RT];
+    load_nb(0, hs[0], cs[0]);
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) {
+      if (nb + 1 < N / 16) load_nb(nb + 1, hs[(nb + 1) & 1], cs[(nb + 1) & 1]);
+      mma_nb(hs[nb & 1], cs[nb & 1]);
     }
   };
 
@@ -424,7 +426,7 @@ void k_chunk_out_f32(ScanArgs a) {
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
     if (!vk[k]) continue;                      // uniform
-    const int I = Ik[k], R = I >> 2;
+    const int I = Ik[k], R = k;   // row_tile_of deals tile k of a wavefront from block k
     const int ri = 16 * I + r16;
     const float cum_i = cumk[k];
     const float* sr = S + (int64_t)ri * a.L + 4 * q;
@@ -494,15 +496,17 @@ void k_chunk_out_f32(ScanArgs a) {
         }
       }
     };
-    // score tiles double-buffered in two fixed register sets
-    float4 sa[4], sb[4];
-    load_s(0, sa);
-    for (int jb = 0; jb <= R; jb += 2) {
-      if (jb + 1 <= R) load_s(jb + 1, sb);
-      block(jb, sa);
-      if (jb + 1 > R) break;
-      if (jb + 2 <= R) load_s(jb + 2, sa);
-      block(jb + 1, sb);
+    // Score tiles double-buffered in two register sets.  R is a compile-time
+    // constant here, so the loop unrolls and every wait is for exactly the
+    // block being consumed; the scheduling barrier keeps the next block's
+    // loads ahead of this block's work instead of next to their use.
+    float4 sbuf[2][4];
+    load_s(0, sbuf[0]);
+#pragma unroll
+    for (int jb = 0; jb <= R; ++jb) {
+      if (jb + 1 <= R) load_s(jb + 1, sbuf[(jb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      block(jb, sbuf[jb & 1]);
     }
   }
 
