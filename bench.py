@@ -58,7 +58,7 @@ KERNEL_SOURCES = {
 TRAFFIC = {
     # counter runs and calibration: profiles/chunk_out_f32_m130_f32_decode_m2p7_b64_hbm_bytes.txt
     ("chunk_out/f32", "m130_f32"): (38.19e6 + 30.45e6, "56909f5168ee5332"),
-    ("decode", "m2p7_decode_b64"): (169.13e6 + 168.44e6, "52c5cda5fcfeee0e"),
+    ("decode", "m2p7_decode_b64"): (169.13e6 + 168.43e6, "d164f32a0d3b83f2"),
     # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
     ("conv1d", "conv_m2p7_bf16"): (49.18e6 + 44.07e6, "f00255d06cc64912"),
     ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "f00255d06cc64912"),

@@ -33,55 +33,84 @@ __device__ __forceinline__ void st_stream(float4* p, float4 v) {
   __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 }
 
-// THREADS lanes per workgroup, BATCH float4 loads in flight per lane.  The
-// state loads of the first pass are issued before anything else (Delta, the
-// decay, B and C), so the slice is in flight while the rest is computed: at
-// batch 64 this took the step from 63.3 to 59 us, at batch 1 from 10.6 to ~5.
-template <typename T, int THREADS, int BATCH>
+// THREADS lanes per workgroup, BATCH float4 loads in flight per lane.
+//
+// EXACT = true: the token's x, B and C and the state vectors of the first
+// pass are all issued before anything is computed, and every load is issued
+// on every path (indexes clamped), so the wait before each state vector
+// covers exactly that vector.  EXACT = false: the state loads go first and
+// each vector's x is loaded next to its use; the wait for that x also waits
+// for the previous vector's store (loads and stores share one counter), which
+// spaces out the stores.  Measured at the 2.7B shape: exact waits took batch
+// 64 from 57.8 to 56.1 us and batch 1 from 4.74 to 4.28 us; at batch 16 the
+// spaced stores are faster (15.4 against 17.1 us).
+template <typename T, int THREADS, int BATCH, bool EXACT>
 __global__ __launch_bounds__(THREADS) void k_step(StepArgs a) {
   const int64_t bh = blockIdx.x;
   const int P = a.P, N = a.N, NQ = N / 4;
+  const int nq_shift = __builtin_ctz(NQ);   // N / 4 is a power of two
   const int tid = threadIdx.x;
   const int total = P * NQ;  // float4 elements of the slice, a multiple of 64
   float4* st = reinterpret_cast<float4*>(a.state + bh * (int64_t)P * N);
-  float4 s[BATCH];
-#pragma unroll
-  for (int k = 0; k < BATCH; ++k) {
-    const int f = k * THREADS + tid;
-    if (f < total) s[k] = ld_stream(&st[f]);   // uniform per wavefront
-  }
   const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
-  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  const float d = delta_of(a.dt[bh] + bias, a.softplus, a.dt_min, a.dt_max);
-  const float alpha = expf(d * a.A[h]);
-  const float Dh = a.D ? a.D[h] : 0.0f;
   const T* xg = reinterpret_cast<const T*>(a.x) + bh * P;
   const T* Bg = reinterpret_cast<const T*>(a.B) + (b * a.G + g) * N;
   const T* Cg = reinterpret_cast<const T*>(a.C) + (b * a.G + g) * N;
   T* yg = reinterpret_cast<T*>(a.y) + bh * P;
-
   // the n-quad of this lane is the same for every row it visits (NQ | THREADS)
   const int n4 = tid % NQ;
-  float bv[4], cv[4];
+
+  float4 s[BATCH];
+  T xraw[BATCH], braw[4], craw[4];
+  auto load_pass = [&](int base) {
+    if constexpr (EXACT) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    bv[k] = to_f32(Bg[4 * n4 + k]);
-    cv[k] = to_f32(Cg[4 * n4 + k]);
-  }
-  for (int base = 0; base < total; base += THREADS * BATCH) {
-    if (base > 0) {
+      for (int k = 0; k < BATCH; ++k) xraw[k] = xg[min(base + k * THREADS + tid, total - 1) >> nq_shift];
+#pragma unroll
+      for (int k = 0; k < BATCH; ++k) s[k] = ld_stream(&st[min(base + k * THREADS + tid, total - 1)]);
+    } else {
 #pragma unroll
       for (int k = 0; k < BATCH; ++k) {
         const int f = base + k * THREADS + tid;
-        if (f < total) s[k] = ld_stream(&st[f]);
+        if (f < total) s[k] = ld_stream(&st[f]);   // uniform per wavefront
       }
     }
+    // keep the loads ahead of the conversions that consume them
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (EXACT) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      braw[k] = Bg[4 * n4 + k];
+      craw[k] = Cg[4 * n4 + k];
+    }
+  }
+  load_pass(0);
+  if constexpr (!EXACT) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      braw[k] = Bg[4 * n4 + k];
+      craw[k] = Cg[4 * n4 + k];
+    }
+  }
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float d = delta_of(a.dt[bh] + bias, a.softplus, a.dt_min, a.dt_max);
+  const float alpha = expf(d * a.A[h]);
+  const float Dh = a.D ? a.D[h] : 0.0f;
+  float bv[4], cv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    bv[k] = to_f32(braw[k]);
+    cv[k] = to_f32(craw[k]);
+  }
+  for (int base = 0; base < total; base += THREADS * BATCH) {
+    if (base > 0) load_pass(base);
 #pragma unroll
     for (int k = 0; k < BATCH; ++k) {
       const int f = base + k * THREADS + tid;
       if (f < total) {  // uniform per wavefront: total is a multiple of 64
-        const int p = f / NQ;
-        const float xp = to_f32(xg[p]);
+        const int p = f >> nq_shift;
+        const float xp = to_f32(EXACT ? xraw[k] : xg[p]);
         const float dx = d * xp;
         float4 v = s[k];
         v.x = alpha * v.x + dx * bv[0];
@@ -109,11 +138,11 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
   // 256 x 8 at batch 16, 1024 x 2 at batch 1 (80 slices: fewer, wider
   // workgroups put more of the state in flight at once)
   if (a.P * a.N >= 8192 && slices >= 2048) {
-    hipLaunchKernelGGL((k_step<T, 512, 4>), dim3((unsigned)slices), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((k_step<T, 512, 4, true>), dim3((unsigned)slices), dim3(512), 0, stream, a);
   } else if (a.P * a.N >= 8192 && slices < 512) {
-    hipLaunchKernelGGL((k_step<T, 1024, 2>), dim3((unsigned)slices), dim3(1024), 0, stream, a);
+    hipLaunchKernelGGL((k_step<T, 1024, 2, true>), dim3((unsigned)slices), dim3(1024), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((k_step<T, 256, 8>), dim3((unsigned)slices), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((k_step<T, 256, 8, false>), dim3((unsigned)slices), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
