@@ -60,8 +60,8 @@ TRAFFIC = {
     ("chunk_out/f32", "m130_f32"): (38.19e6 + 30.45e6, "56909f5168ee5332"),
     ("decode", "m2p7_decode_b64"): (169.13e6 + 168.43e6, "d164f32a0d3b83f2"),
     # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
-    ("conv1d", "conv_m2p7_bf16"): (49.18e6 + 44.07e6, "f00255d06cc64912"),
-    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "f00255d06cc64912"),
+    ("conv1d", "conv_m2p7_bf16"): (49.20e6 + 44.07e6, "fbbf46e4543e456b"),
+    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "fbbf46e4543e456b"),
 }
 COPY_CALIBRATION_BYTES = 1 << 30
 
