@@ -339,7 +339,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int i = io[s][r], j = jb[v];
         const float cv = cb[(int64_t)min(i, Lc - 1) * L + min(j, Lc - 1)];
-        cbv[s][v][r] = (i < Lc && j < i) ? cv : 0.0f;
+        // one select (not a short-circuit branch) keeps the 16 loads together
+        cbv[s][v][r] = ((i < Lc) & (j < i)) ? cv : 0.0f;
       }
 
   f32x4 mv[2][2];
