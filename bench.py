@@ -554,8 +554,9 @@ def main():
                     help="only run the known-size copy used to calibrate the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(batch and heads shard with no communication; see the design notes).",
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(batch rows and heads are independent, so a split over GPUs would need "
+              "no communication in the forward scan).",
               file=sys.stderr)
         sys.exit(2)
 
