@@ -6,8 +6,11 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 One step is one ssd_chunk_scan over the workload's whole batch (the prefill
 path: Delta preparation, per-chunk prefix sum, decay matrix, C B^T, the
 intra-chunk product, chunk states, the inter-chunk recurrence and the
-state-to-output term).  The cached-decode path (ssd_step) is timed in the same
-run and reported in the "decode" object.  Inputs are seeded synthetic
+state-to-output term).  The headline workload is the largest one-GPU prefill,
+the 1.3B-shaped batched long prefill (8 x 16384 tokens, 64 heads, bf16 x/B/C,
+chunk 256).  The 130M- and 2.7B-shaped layer prefills are timed in the same
+run ("prefill_configs"), and so is the cached-decode path (ssd_step) at
+batch 1, 16 and 64 ("decode").  Inputs are seeded synthetic
 activations resident in device memory before timing starts; K steps are
 timed between two device synchronisations.  Input/output sets are rotated so
 that their total exceeds the 256 MB Infinity Cache.
@@ -45,12 +48,15 @@ METRIC = ("SSD prefill tokens/s (% MFMA peak); cached decode tokens/s (% HBM GB/
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
-DEFAULT_WORKLOAD = "m130_f32"
+DEFAULT_WORKLOAD = "m1p3_long_bf16"
+SUB_WORKLOADS = ("m130_f32", "m2p7_bf16")
+DECODE_BATCHES = (1, 16, 64)
 CSRC = os.path.join(ROOT, "state_space_model_amd", "csrc")
 # sources a kernel's code comes from (the digest that keys TRAFFIC)
 KERNEL_SOURCES = {
     "chunk_out/f32": ["ssd_prefill_f32.hip", "ssd_prefill_common.h", "ssd_device.h"],
     "chunk_out/bf16": ["ssd_prefill_bf16.hip", "ssd_prefill_common.h", "ssd_device.h"],
+    "chain/bf16": ["ssd_prefill_bf16.hip", "ssd_prefill_common.h", "ssd_device.h"],
     "decode": ["ssd_step.hip", "ssd_device.h"],
     "conv1d": ["ssd_conv.hip", "ssd_device.h"],
 }
@@ -71,15 +77,33 @@ def prefill_flops_per_token(w):
     return H * ((L + 1) * P + 4 * N * P + 2 * P * N / L) + G * (L + 1) * N
 
 
-def phase_flops_per_token(w):
-    """Algorithmic FLOP/token of each kernel of the scan."""
+def phase_flops_per_token(w, chain):
+    """Algorithmic FLOP/token of each kernel of the scan, by schedule.
+    phased: C B^T rides in the chunk-state launch; chain: a C B^T / B^T
+    pre-pass, then one kernel doing the chunk states, the inter-chunk
+    recurrence and the outputs (a5-a8)."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    if chain:
+        return {"cb_bt_prepass": G * (L + 1) * N,
+                "chain": H * ((L + 1) * P + 4 * N * P + 2 * P * N / L)}
     return {
-        "cb": G * (L + 1) * N,                                          # C B^T, causal half
-        "chunk_state": H * 2 * N * P,                                   # chunk summary states
+        "chunk_state": H * 2 * N * P + G * (L + 1) * N,                 # chunk states + C B^T
         "state_pass": H * 2 * P * N / L,                                # inter-chunk recurrence
         "chunk_out": H * ((L + 1) * P + 2 * N * P),                     # decay, products
     }
+
+
+# kernel (phase) names of each schedule, and the event interval that times
+# each: the timed call records an event before each of its 4 phases and one
+# after the last; an empty phase's two events add only event overhead, so
+# empty phases are not reported.
+PHASES = {
+    False: {"chunk_state": (1, 2), "state_pass": (2, 3), "chunk_out": (3, 4)},
+    True: {"cb_bt_prepass": (0, 1), "chain": (3, 4)},
+}
+KERNEL_NAMES = {"chunk_state": "k_cb_and_chunk_state", "state_pass": "k_state_pass",
+                "chunk_out": "k_chunk_out", "cb_bt_prepass": "k_cb_and_bt_bf16",
+                "chain": "k_chain_bf16"}
 
 
 def prefill_bytes_per_token(w, T):
@@ -190,15 +214,53 @@ def bench_prefill(ssd, torch, w, steps, warmup):
         rep_ms.append(r0.elapsed_time(r1) / steps)
     # per-kernel durations, HIP events on the stream the kernels run on
     nph = ssd.SSD_SCAN_PHASES
+    chain = ssd.ssd_chunk_scan_schedule(x0, B0, w.chunk) == ssd.SSD_SCHEDULE_CHAIN
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(steps)]
     for i in range(steps):
         run(i, evs[i])
     torch.cuda.synchronize()
-    names = ["cb", "chunk_state", "state_pass", "chunk_out"]
-    phase_ms = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(steps)) / steps
-                for k, n in enumerate(names)}
+    phase_ms = {n: sum(evs[i][a].elapsed_time(evs[i][b]) for i in range(steps)) / steps
+                for n, (a, b) in PHASES[chain].items()}
     return {"ms": ms, "wall_ms": wall * 1e3 / steps, "phase_ms": phase_ms, "nsets": nsets,
-            "set_bytes": set_bytes, "tokens": Bt * T, "rep_ms": rep_ms}
+            "set_bytes": set_bytes, "tokens": Bt * T, "rep_ms": rep_ms, "chain": chain}
+
+
+def prefill_report(w, pf, headline=False):
+    """The prefill numbers of one workload: whole call against the MFMA peak
+    of its dtype, and the dominant kernel's roofline (its own algorithmic
+    FLOPs over its event-timed launch duration)."""
+    tokens_s = pf["tokens"] / (pf["ms"] * 1e-3)
+    fpt = prefill_flops_per_token(w)
+    per = phase_flops_per_token(w, pf["chain"])
+    peak = PEAK_TFLOPS[w.io_dtype]
+    dom = max(pf["phase_ms"], key=pf["phase_ms"].get)
+    dom_flops = per[dom] * pf["tokens"]
+    dom_ms = pf["phase_ms"][dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    key = f"{dom}/{w.io_dtype}"
+    whole_tflops = fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12
+    bpt = prefill_bytes_per_token(w, w.seqlen)
+    roof = {"bound": "mfma", "kernel": KERNEL_NAMES[dom], "achieved": achieved, "peak": peak,
+            "unit": "TFLOP/s", "frac": achieved / peak,
+            "traffic": traffic_for(key, w.name) if key in KERNEL_SOURCES else None,
+            "flops_per_launch": dom_flops, "avg_launch_ms": dom_ms}
+    rep = {"workload": w.name, "schedule": "chain" if pf["chain"] else "phased",
+           "ms_per_step": pf["ms"], "tokens_per_s": tokens_s,
+           "algorithmic_tflops": whole_tflops, "mfma_peak_frac": whole_tflops / peak,
+           "flops_per_token": fpt, "bytes_per_token": bpt,
+           "hbm_gbs_algorithmic": bpt * tokens_s / 1e9,
+           "hbm_peak_frac_algorithmic": bpt * tokens_s / 1e9 / PEAK_HBM_GBS,
+           "phase_ms": pf["phase_ms"],
+           "phase_tflops": {n: per[n] * pf["tokens"] / (ms * 1e-3) / 1e12
+                            for n, ms in pf["phase_ms"].items()},
+           "wall_ms_per_step": pf["wall_ms"],
+           "repeat_ms_per_step": {"runs": 5, "mean": statistics.mean(pf["rep_ms"]),
+                                  "std": statistics.stdev(pf["rep_ms"]),
+                                  "min": min(pf["rep_ms"]), "max": max(pf["rep_ms"])},
+           "rotated_sets": pf["nsets"]}
+    if not headline:
+        rep["roofline"] = roof
+    return rep, roof
 
 
 def bench_decode(ssd, torch, batch, steps_n, warmup):
@@ -255,6 +317,42 @@ def bench_decode(ssd, torch, batch, steps_n, warmup):
                          "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                          "traffic": traffic_for("decode", f"m2p7_decode_b{batch}")},
             "bytes_per_token": bpt}
+
+
+def launch_floor_us(ssd, torch, n=1024):
+    """Time per node of a HIP graph of n launches of the library's smallest
+    kernel (the float4 copy an empty-sequence scan makes of a 1 KiB state):
+    the launch/latency floor a one-row decode step sits on."""
+    H, P, N = 1, 16, 16
+    h0 = torch.randn(1, H, P, N, device="cuda")
+    fin = torch.empty_like(h0)
+    x = torch.empty(1, 0, H, P, device="cuda")
+    dt = torch.empty(1, 0, H, device="cuda")
+    B = torch.empty(1, 0, 1, N, device="cuda")
+    A = -torch.ones(H, device="cuda")
+
+    def body():
+        for _ in range(n):
+            ssd.ssd_chunk_scan(x, dt, A, B, B, None, chunk=64, initial_state=h0, final_state=fin)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (3 * n)
 
 
 def bench_cached_vs_recompute(ssd, torch, context=4096, reps=20):
@@ -541,7 +639,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--decode-batch", type=int, default=64)
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="one decode batch size (default: 1, 16 and 64)")
+    ap.add_argument("--no-sub-configs", action="store_true",
+                    help="skip the 130M- and 2.7B-shaped prefill lines")
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--chunk", type=int, default=0, help="override the workload's chunk size")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -579,49 +680,42 @@ def main():
     print(f"[bench] prefill {w.name} L={w.chunk} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
     pf = bench_prefill(ssd, torch, w, args.steps, args.warmup)
-    tokens_s = pf["tokens"] / (pf["ms"] * 1e-3)
-    fpt = prefill_flops_per_token(w)
-    per = phase_flops_per_token(w)
-    dom = max(pf["phase_ms"], key=pf["phase_ms"].get)
-    dom_flops = per[dom] * pf["tokens"]
-    dom_ms = pf["phase_ms"][dom]
-    peak = PEAK_TFLOPS[w.io_dtype]
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    head, roof = prefill_report(w, pf, headline=True)
     out = {
-        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1,
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": pf["ms"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.io_dtype, "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
                    "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
                    "chunk": w.chunk, "io_dtype": w.io_dtype, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic_for(f"{dom}/{w.io_dtype}", w.name)
-                     if f"{dom}/{w.io_dtype}" in KERNEL_SOURCES else None,
-                     "flops_per_launch": dom_flops, "avg_launch_ms": dom_ms},
-        "prefill": {"algorithmic_tflops": fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12,
-                    "mfma_peak_frac": fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12 / peak,
-                    "flops_per_token": fpt,
-                    "bytes_per_token": prefill_bytes_per_token(w, w.seqlen),
-                    "hbm_gbs_algorithmic": prefill_bytes_per_token(w, w.seqlen) * tokens_s / 1e9,
-                    "phase_ms": pf["phase_ms"], "wall_ms_per_step": pf["wall_ms"],
-                    "repeat_ms_per_step": {"runs": 5, "mean": statistics.mean(pf["rep_ms"]),
-                                           "std": statistics.stdev(pf["rep_ms"])},
-                    "rotated_sets": pf["nsets"]},
+        "roofline": roof,
+        "prefill": head,
     }
+    if not args.no_sub_configs and args.workload == DEFAULT_WORKLOAD and not args.chunk:
+        out["prefill_configs"] = {}
+        for name in SUB_WORKLOADS:
+            ws = WORKLOADS[name]
+            print(f"[bench] prefill {name} L={ws.chunk}", file=sys.stderr, flush=True)
+            out["prefill_configs"][name] = prefill_report(
+                ws, bench_prefill(ssd, torch, ws, args.steps, args.warmup))[0]
     if not args.no_decode:
-        print(f"[bench] decode b={args.decode_batch} steps={args.decode_steps}", file=sys.stderr,
-              flush=True)
-        out["decode"] = bench_decode(ssd, torch, args.decode_batch, args.decode_steps,
-                                     args.warmup)
+        out["decode"] = {}
+        batches = DECODE_BATCHES if args.decode_batch == 0 else (args.decode_batch,)
+        for b in batches:
+            print(f"[bench] decode b={b} steps={args.decode_steps}", file=sys.stderr, flush=True)
+            out["decode"][f"b{b}"] = bench_decode(ssd, torch, b, args.decode_steps, args.warmup)
+        if 1 in batches:
+            out["decode"]["b1"]["launch_floor_us"] = launch_floor_us(ssd, torch)
         print("[bench] cached decode vs recompute at 4096", file=sys.stderr, flush=True)
         out["cached_vs_recompute"] = bench_cached_vs_recompute(ssd, torch)
         print("[bench] conv1d prefill and step", file=sys.stderr, flush=True)
         out["conv1d"] = bench_conv(ssd, torch, args.warmup)
         if not args.no_backward:
-            print("[bench] backward", file=sys.stderr, flush=True)
-            out["backward"] = bench_backward(ssd, torch, w)
+            out["backward"] = {}
+            for name in SUB_WORKLOADS:
+                print(f"[bench] backward {name}", file=sys.stderr, flush=True)
+                out["backward"][name] = bench_backward(ssd, torch, WORKLOADS[name])
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w)

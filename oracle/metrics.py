@@ -49,3 +49,22 @@ def state_err(got, ref) -> float:
 def step_y_err(got, ref) -> float:
     """y_t layout [Bt, H, P]."""
     return slice_rel_err(got, ref, 1, (2,))
+
+
+def token_rel_err(got, ref, floor: float = 1e-3) -> float:
+    """max over (b, t, h) of ||got-ref||_inf / ||ref||_inf taken over one
+    token's P outputs, the denominator floored at `floor` times its (b, h)
+    slice's ||ref||_inf (tokens whose output is near zero would otherwise
+    divide by almost nothing).  Layout [Bt, T, H, P].  Reported beside the
+    slice metric: it shows a local error that a slice's largest value could
+    hide."""
+    g, r = _as64(got), _as64(ref)
+    if g.shape != r.shape:
+        raise ValueError(f"shape mismatch {g.shape} vs {r.shape}")
+    if g.size == 0:
+        return 0.0
+    num = np.abs(g - r).max(axis=3)
+    den = np.abs(r).max(axis=3)
+    slice_den = np.abs(r).max(axis=(1, 3), keepdims=True)[..., 0]
+    den = np.maximum(den, floor * np.where(slice_den > 0, slice_den, 1.0))
+    return float((num / den).max())

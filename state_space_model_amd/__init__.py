@@ -128,8 +128,35 @@ def _check(t: Optional[torch.Tensor], name: str, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _shape(t: Optional[torch.Tensor], name: str, shape) -> None:
+    """Raise ValueError unless t is None or has exactly `shape`.  The C ABI
+    receives bare pointers and cannot see a buffer's extent, so every tensor's
+    shape is checked here, before any launch."""
+    if t is not None and tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(v) for v in shape)}, "
+                         f"got {tuple(t.shape)}")
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _scan_shapes(x, dt, A, B, C, D=None, dt_bias=None, initial_state=None) -> None:
+    """Shapes of a scan's inputs against (Bt, T, H, P) of x and (G, N) of B."""
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [Bt,T,H,P] and B, C [Bt,T,G,N]")
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _shape(B, "B", (Bt, T, G, N))
+    _shape(C, "C", (Bt, T, G, N))
+    _shape(dt, "dt", (Bt, T, H))
+    for t, n in ((A, "A"), (D, "D"), (dt_bias, "dt_bias")):
+        _shape(t, n, (H,))
+    _shape(initial_state, "initial_state", (Bt, H, P, N))
 
 
 def scan_desc(x: torch.Tensor, B: torch.Tensor, chunk: int, dt_softplus: bool,
@@ -174,16 +201,17 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     `phase_events`: optional SSD_SCAN_PHASES+1 torch.cuda.Event objects
     (created with enable_timing=True) recorded around the scan's kernels.
     """
-    if x.dim() != 4 or B.dim() != 4 or C.shape != B.shape:
-        raise ValueError("x must be [Bt,T,H,P] and B, C [Bt,T,G,N]")
+    _scan_shapes(x, dt, A, B, C, D, dt_bias, initial_state)
+    Bt, T, H, P = x.shape
+    N = B.shape[3]
+    _shape(y, "y", (Bt, T, H, P))
+    _shape(final_state, "final_state", (Bt, H, P, N))
     for t, n, dt_ in ((x, "x", None), (B, "B", x.dtype), (C, "C", x.dtype), (dt, "dt", torch.float32),
                       (A, "A", torch.float32), (D, "D", torch.float32),
                       (dt_bias, "dt_bias", torch.float32),
                       (initial_state, "initial_state", torch.float32)):
         _check(t, n, dt_)
     desc = scan_desc(x, B, chunk, dt_softplus, dt_limit)
-    Bt, T, H, P = x.shape
-    N = B.shape[3]
     dev = x.device
     if y is None:
         y = torch.empty_like(x)
@@ -195,7 +223,7 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace")
-    wbytes = workspace.numel() * workspace.element_size()
+    wbytes = _nbytes(workspace)
     args = (ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
             _ptr(D), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
             ctypes.c_size_t(wbytes), _stream(dev))
@@ -228,8 +256,17 @@ def ssd_step(state: torch.Tensor, x_t: torch.Tensor, dt_t: torch.Tensor, A: torc
     """One decode step on the current stream; `state` [Bt,H,P,N] float32 is
     updated in place.  x_t [Bt,H,P], B_t/C_t [Bt,G,N] (float32 or bfloat16),
     dt_t [Bt,H] float32.  Returns y_t [Bt,H,P] in x_t's dtype."""
-    if state.dim() != 4 or x_t.dim() != 3 or B_t.dim() != 3 or C_t.shape != B_t.shape:
+    if state.dim() != 4 or B_t.dim() != 3:
         raise ValueError("state [Bt,H,P,N], x_t [Bt,H,P], B_t/C_t [Bt,G,N]")
+    Bt, H, P, N = state.shape
+    G = B_t.shape[1]
+    _shape(x_t, "x_t", (Bt, H, P))
+    _shape(dt_t, "dt_t", (Bt, H))
+    _shape(B_t, "B_t", (Bt, G, N))
+    _shape(C_t, "C_t", (Bt, G, N))
+    for t, n in ((A, "A"), (D, "D"), (dt_bias, "dt_bias")):
+        _shape(t, n, (H,))
+    _shape(y_t, "y_t", (Bt, H, P))
     for t, n, dt_ in ((state, "state", torch.float32), (x_t, "x_t", None),
                       (B_t, "B_t", x_t.dtype), (C_t, "C_t", x_t.dtype),
                       (dt_t, "dt_t", torch.float32), (A, "A", torch.float32),
@@ -252,6 +289,12 @@ def ssd_chunk_scan_backward_workspace_bytes(x: torch.Tensor, B: torch.Tensor,
     return int(lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(d)))
 
 
+# shapes of the gradients ssd_chunk_scan_backward returns, in terms of (Bt, T, H, P, G, N)
+_GRAD_SHAPES = {"dx": ("Bt", "T", "H", "P"), "ddt": ("Bt", "T", "H"), "dA": ("H",),
+                "dB": ("Bt", "T", "G", "N"), "dC": ("Bt", "T", "G", "N"), "dD": ("H",),
+                "ddt_bias": ("H",), "dinitial_state": ("Bt", "H", "P", "N")}
+
+
 def ssd_chunk_scan_backward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                             C: torch.Tensor, D: Optional[torch.Tensor] = None, *, dy: torch.Tensor,
                             dfinal_state: Optional[torch.Tensor] = None, chunk: int = 256,
@@ -265,17 +308,26 @@ def ssd_chunk_scan_backward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, 
     dfinal_state [Bt,H,P,N] float32 or None.  Returns a dict of float32
     tensors dx, ddt, dA, dB, dC, dD, ddt_bias, dinitial_state (the last three
     always computed here)."""
+    _scan_shapes(x, dt, A, B, C, D, dt_bias, initial_state)
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _shape(dy, "dy", (Bt, T, H, P))
+    _shape(dfinal_state, "dfinal_state", (Bt, H, P, N))
+    g = grads or {}
+    unknown = set(g) - set(_GRAD_SHAPES)
+    if unknown:
+        raise ValueError(f"unknown gradient names {sorted(unknown)}")
+    dims = dict(Bt=Bt, T=T, H=H, P=P, G=G, N=N)
+    for k, v in g.items():
+        _shape(v, k, tuple(dims[a] for a in _GRAD_SHAPES[k]))
     for t, n, dt_ in ((x, "x", None), (dt, "dt", torch.float32), (A, "A", torch.float32),
                       (B, "B", x.dtype), (C, "C", x.dtype), (D, "D", torch.float32),
                       (dt_bias, "dt_bias", torch.float32), (initial_state, "initial_state", torch.float32),
                       (dy, "dy", x.dtype), (dfinal_state, "dfinal_state", torch.float32)):
         _check(t, n, dt_)
     desc = scan_desc(x, B, chunk, dt_softplus, dt_limit)
-    Bt, T, H, P = x.shape
-    G, N = B.shape[2], B.shape[3]
     dev = x.device
     f32 = torch.float32
-    g = grads or {}
     out = {
         "dx": g.get("dx", torch.empty(Bt, T, H, P, device=dev, dtype=f32)),
         "ddt": g.get("ddt", torch.empty(Bt, T, H, device=dev, dtype=f32)),
@@ -291,11 +343,12 @@ def ssd_chunk_scan_backward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, 
     need = int(lib.ssd_chunk_scan_backward_workspace_bytes(ctypes.byref(desc)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace")
     st = lib.ssd_chunk_scan_backward(
         ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
         _ptr(initial_state), _ptr(dy), _ptr(dfinal_state), _ptr(out["dx"]), _ptr(out["ddt"]),
         _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["ddt_bias"]),
-        _ptr(out["dinitial_state"]), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+        _ptr(out["dinitial_state"]), _ptr(workspace), ctypes.c_size_t(_nbytes(workspace)),
         _stream(dev))
     if st != SSD_OK:
         raise SSDError(st, "ssd_chunk_scan_backward")
@@ -318,6 +371,10 @@ def ssd_conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tenso
         raise ValueError("x [Bt,T,D], weight [D,k]")
     Bt, T, Dc = x.shape
     K = weight.shape[1]
+    _shape(bias, "bias", (Dc,))
+    _shape(state, "state", (Bt, Dc, K - 1))
+    _shape(y, "y", (Bt, T, Dc))
+    _shape(state_out, "state_out", (Bt, Dc, K - 1))
     for t, n, dt_ in ((x, "x", None), (weight, "weight", torch.float32),
                       (bias, "bias", torch.float32), (state, "state", x.dtype)):
         _check(t, n, dt_)
@@ -344,6 +401,10 @@ def ssd_conv1d_step(state: torch.Tensor, x_t: torch.Tensor, weight: torch.Tensor
         raise ValueError("state [Bt,D,k-1], x_t [Bt,D], weight [D,k]")
     Bt, Dc = x_t.shape
     K = weight.shape[1]
+    _shape(weight, "weight", (Dc, K))
+    _shape(state, "state", (Bt, Dc, K - 1))
+    _shape(bias, "bias", (Dc,))
+    _shape(y_t, "y_t", (Bt, Dc))
     for t, n, dt_ in ((state, "state", x_t.dtype), (x_t, "x_t", None),
                       (weight, "weight", torch.float32), (bias, "bias", torch.float32)):
         _check(t, n, dt_)

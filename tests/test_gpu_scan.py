@@ -17,6 +17,7 @@ import torch
 import oracle
 from gpu_util import (TOL, announce, need_gpu, oracle_scan, slice_bh, state_err, to_dev,
                       workload_inputs, y_err)
+from oracle.metrics import token_rel_err
 from ssd_inputs import WORKLOADS, make_inputs, make_tiny
 
 pytestmark = pytest.mark.gpu
@@ -46,29 +47,41 @@ def test_scan_workload_full(name):
     assert ey <= TOL[w.io_dtype] and ef <= TOL[w.io_dtype]
 
 
-SAMPLE_BH = [(0, 0), (3, 17), (5, 40), (7, 63)]
-
-
-@pytest.mark.parametrize("chunk", [128, 256, 512])
-def test_scan_long_batched_sampled(chunk):
-    """1.3B-shaped batched long prefill (8 x 16384, H=64) at chunk 128/256/512:
-    the full problem runs on the GPU in the benchmark's launch configuration;
-    the oracle recomputes sampled (b, h) sequences end to end."""
+def test_scan_long_batched_full():
+    """1.3B-shaped batched long prefill (8 x 16384, H=64, bf16) at chunk
+    128, 256 and 512, each run whole on the GPU in the benchmark's launch
+    configuration, and every one of the 512 (b, h) sequences compared with
+    the oracle (one batch row at a time, to bound host memory; the oracle
+    does not depend on the chunk, so each row's reference serves all three)."""
     need_gpu()
+    import state_space_model_amd as ssd
     w = WORKLOADS["m1p3_long_bf16"]
     inp = workload_inputs("m1p3_long_bf16")
-    announce(f"scan m1p3_long_bf16 chunk={chunk}")
-    y, fin = run_gpu(inp, w, chunk=chunk)
-    worst = 0.0
-    for b, h in SAMPLE_BH:
-        s = slice_bh(inp, b, h, w.ngroups, w.nheads)
-        y_ref, f_ref = oracle_scan(s, w)
-        ey = y_err(y[b:b + 1, :, h:h + 1], y_ref)
-        ef = state_err(fin[b:b + 1, h:h + 1], f_ref)
-        worst = max(worst, ey, ef)
-    print(f"chunk {chunk}: worst sampled err {worst:.3e}")
-    assert worst <= TOL["bf16"]
-    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    d = to_dev(inp)
+    outs = {}
+    for chunk in (128, 256, 512):
+        announce(f"scan m1p3_long_bf16 chunk={chunk} schedule "
+                 f"{ssd.ssd_chunk_scan_schedule(d['x'], d['B'], chunk)}")
+        outs[chunk] = ssd.ssd_chunk_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                                         chunk=chunk, dt_bias=d["dt_bias"],
+                                         dt_limit=(w.dt_min, w.dt_max))
+    torch.cuda.synchronize()
+    del d
+    worst = {L: [0.0, 0.0, 0.0] for L in outs}
+    for b in range(w.batch):
+        row = {k: (v[b:b + 1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+        y_ref, f_ref = oracle_scan(row, w)
+        for L, (y, fin) in outs.items():
+            yb = y[b:b + 1].cpu()
+            e = (y_err(yb, y_ref), state_err(fin[b:b + 1].cpu(), f_ref),
+                 token_rel_err(yb, y_ref))
+            worst[L] = [max(a_, b_) for a_, b_ in zip(worst[L], e)]
+        print(f"row {b}: " + "  ".join(f"L{L} y {v[0]:.2e} fin {v[1]:.2e}"
+                                       for L, v in worst.items()), flush=True)
+    for L, (ey, ef, et) in worst.items():
+        print(f"chunk {L}: y err {ey:.3e}  final-state err {ef:.3e}  "
+              f"(per-token normalised {et:.3e}, information)")
+        assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (L, ey, ef)
 
 
 def test_scan_chunk_size_invariance_on_gpu():
@@ -223,6 +236,84 @@ def test_scan_chunked_prefill_chain(io):
     assert ey <= TOL[io] and ef <= TOL[io]
     assert y_err(y_chain, y_one.double().cpu().numpy()) <= TOL[io]
     assert state_err(state, f_one.double().cpu().numpy()) <= TOL[io]
+
+
+# Delta at its clip limits ([SSD] Implementation: softplus then clip).  At
+# dt_max with A = -16 every token decays by e^-8, so the decay across a chunk
+# underflows float32 (the masked and factored exponentials must flush to 0,
+# never overflow); at dt_min with A = -1 the memory is near-identity over
+# 16384 tokens (large states, tiny per-token decay).
+CLIP_CASES = [
+    # (Bt, T, H, io, bound): bf16 with 256 chains runs the chain schedule
+    (2, 4096, 8, "f32", "max"),
+    (2, 4096, 8, "bf16", "max"),
+    (4, 2048, 64, "bf16", "max"),
+    (1, 16384, 8, "f32", "min"),
+    (1, 16384, 8, "bf16", "min"),
+    (4, 16384, 64, "bf16", "min"),
+]
+
+
+@pytest.mark.parametrize("case", CLIP_CASES, ids=lambda c: "_".join(map(str, c)))
+def test_scan_delta_at_clip_bounds(case):
+    need_gpu()
+    import state_space_model_amd as ssd
+    Bt, T, H, io, bound = case
+    w = make_tiny(Bt, T, H, 64, 128, 1, 256, io, seed=4300 + CLIP_CASES.index(case))
+    inp = make_inputs(w, with_initial_state=(bound == "max"))
+    if bound == "max":
+        inp["dt_bias"] = torch.full((H,), 5.0)    # softplus ~ 5 -> clipped to 0.5
+        inp["A"] = torch.full((H,), -16.0)
+    else:
+        inp["dt_bias"] = torch.full((H,), -20.0)  # softplus ~ 2e-9 -> clipped to 1e-4
+        inp["A"] = torch.full((H,), -1.0)
+    d = to_dev(inp)
+    announce(f"scan delta at dt_{bound} {case} schedule "
+             f"{ssd.ssd_chunk_scan_schedule(d['x'], d['B'], 256)}")
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    ey, ef = y_err(y, y_ref), state_err(fin, f_ref)
+    print(f"dt_{bound} {case}: y err {ey:.3e}  final-state err {ef:.3e}  "
+          f"per-token {token_rel_err(y, y_ref):.3e}")
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    assert ey <= TOL[io] and ef <= TOL[io]
+
+
+# Chunk sizes that are multiples of 32 but not of 64 (the kernels work in
+# 64-token key blocks, so the last block of each chunk is partial), on both
+# bf16 schedules and in float32, with several full chunks and a ragged one.
+ODD_CHUNK = [
+    # (Bt, T, H, P, N, G, L, io)
+    (1, 500, 4, 64, 128, 1, 96, "bf16"),
+    (2, 700, 4, 32, 64, 2, 160, "bf16"),
+    (1, 1500, 2, 64, 128, 1, 480, "bf16"),
+    (1, 333, 4, 128, 32, 1, 224, "bf16"),
+    (4, 700, 64, 64, 128, 1, 96, "bf16"),     # chain
+    (2, 1000, 128, 32, 64, 2, 160, "bf16"),   # chain
+    (1, 900, 256, 64, 128, 4, 224, "bf16"),   # chain
+    (2, 500, 4, 64, 128, 1, 96, "f32"),
+    (1, 700, 4, 64, 128, 2, 160, "f32"),
+    (1, 1500, 2, 64, 64, 1, 480, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", ODD_CHUNK, ids=lambda c: "x".join(map(str, c)))
+def test_scan_chunk_not_multiple_of_64(case):
+    need_gpu()
+    import state_space_model_amd as ssd
+    Bt, T, H, P, N, G, L, io = case
+    w = make_tiny(Bt, T, H, P, N, G, L, io, seed=4400 + ODD_CHUNK.index(case))
+    inp = make_inputs(w, with_initial_state=True)
+    d = to_dev(inp)
+    sched = ssd.ssd_chunk_scan_schedule(d["x"], d["B"], L)
+    assert sched == (ssd.SSD_SCHEDULE_CHAIN if io == "bf16" and Bt * H >= 256 and L <= 256
+                     else ssd.SSD_SCHEDULE_PHASED)
+    announce(f"scan chunk {L} {case} schedule {sched}")
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    ey, ef = y_err(y, y_ref), state_err(fin, f_ref)
+    print(f"{case}: y err {ey:.3e}  final-state err {ef:.3e}")
+    assert ey <= TOL[io] and ef <= TOL[io]
 
 
 def test_scan_options_off():

@@ -60,9 +60,10 @@ def test_step_tiny_shapes(case):
 @pytest.mark.parametrize("batch", [1, 16, 64])
 def test_decode_after_prefill_matches_longer_prefill(batch):
     """2.7B-shaped cached decode: prefill 4096 tokens with ssd_chunk_scan, then
-    1024 ssd_step calls.  Sampled (b, h) sequences are recomputed by the
-    oracle over all 5120 tokens; at full size the decoded state must equal a
-    GPU prefill over all 5120 tokens within the bf16 bar."""
+    1024 ssd_step calls.  Every (b, h) sequence is recomputed by the oracle
+    over all 5120 tokens (one batch row at a time); the decoded outputs and
+    the state after the last step are compared with it.  The decoded state
+    must also equal a GPU prefill over all 5120 tokens within the bf16 bar."""
     need_gpu()
     import state_space_model_amd as ssd
     w = WORKLOADS["m2p7_decode"].with_(batch=batch)
@@ -77,17 +78,22 @@ def test_decode_after_prefill_matches_longer_prefill(batch):
     for t in range(T0, T0 + DECODE_STEPS):
         ys.append(gpu_step(ssd, d, state, t))
     torch.cuda.synchronize()
-    y_dec = torch.stack(ys, dim=1)                         # [b, 1024, H, P]
+    y_dec = torch.stack(ys, dim=1).cpu()                   # [b, 1024, H, P]
     y_full, f_full = ssd.ssd_chunk_scan(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
                                         chunk=w.chunk, dt_bias=d["dt_bias"])
     torch.cuda.synchronize()
+    state = state.cpu()
     assert state_err(state, f_full.double().cpu()) <= TOL["bf16"]
     assert y_err(y_dec, y_full[:, T0:].double().cpu()) <= TOL["bf16"]
-    for b, h in [(0, 0), (batch - 1, 79), (batch // 2, 33)]:
-        s = slice_bh(inp, b, h, w.ngroups, w.nheads)
-        y_ref, f_ref = oracle_scan(s, w)
-        assert state_err(state[b:b + 1, h:h + 1], f_ref) <= TOL["bf16"]
-        assert y_err(y_dec[b:b + 1, :, h:h + 1], y_ref[:, T0:]) <= TOL["bf16"]
+    worst_y = worst_s = 0.0
+    for b in range(batch):
+        row = {k: (v[b:b + 1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+        y_ref, f_ref = oracle_scan(row, w)
+        worst_s = max(worst_s, state_err(state[b:b + 1], f_ref))
+        worst_y = max(worst_y, y_err(y_dec[b:b + 1], y_ref[:, T0:]))
+    print(f"decode b={batch}: all {batch * w.nheads} sequences against the oracle: "
+          f"y_t err {worst_y:.3e}  state err {worst_s:.3e}")
+    assert worst_y <= TOL["bf16"] and worst_s <= TOL["bf16"]
 
 
 def test_step_zero_batch_is_noop():
