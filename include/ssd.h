@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum {
   SSD_OK = 0,
@@ -110,8 +110,9 @@ typedef struct {
 
 /*
  * Workspace bytes ssd_chunk_scan needs for `desc` (0 if desc is invalid).
- * Both schedules (see ssd_chunk_scan_schedule) hold the float32 L x L matrix
- * C B^T of every (batch, chunk, group): 4*Bt*ceil(T/L)*G*L*L bytes.  The
+ * Both schedules (see ssd_chunk_scan_schedule) hold the L x L matrix C B^T
+ * of every (batch, chunk, group), in the io dtype: s*Bt*ceil(T/L)*G*L*L
+ * bytes with s = 4 (float32) or 2 (bfloat16).  The
  * phased schedule adds one float32 P x N state and one float32 decay per
  * (batch, head, chunk): 4*Bt*ceil(T/L)*H*(P*N+1) bytes, and with bfloat16 io
  * a bfloat16 copy of the entering states: 2*Bt*ceil(T/L)*H*P*N bytes; the
@@ -227,6 +228,41 @@ ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const 
                                 void* y, float* final_state, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream,
                                 hipEvent_t* phase_events, int n_events);
+
+/*
+ * ssd_chunk_scan with a variant of its output path, for the two ablations of
+ * "Compiler-First State Space Duality and Portable O(1) Autoregressive
+ * Caching", Implementation choices:
+ *
+ *   SSD_VARIANT_BF16_DECAY   every decay factor of the output path (the
+ *                            exponentials of segment sums of A*Delta that
+ *                            weight C B^T, and those of the inter-chunk term)
+ *                            rounded to bfloat16 before use, instead of kept
+ *                            in float32 ("precision management": the decay
+ *                            held in bfloat16 costs accuracy)
+ *   SSD_VARIANT_LOADED_MASK  the causal mask of the diagonal tiles read from a
+ *                            stored lower-triangular bit table in device
+ *                            memory instead of formed by an index comparison
+ *                            in registers ("static masking": where the mask
+ *                            lives changes the speed, not the bits); bfloat16
+ *                            io only; the output is bitwise that of
+ *                            ssd_chunk_scan
+ *   SSD_VARIANT_DEFAULT      ssd_chunk_scan itself
+ *
+ * Arguments, layouts, ownership and errors as ssd_chunk_scan.  Supported for
+ * P = 64, N = 128 and chunk <= 256 (the 130M, 2.7B and 1.3B head shapes);
+ * other shapes return SSD_ERR_UNSUPPORTED, an unknown variant
+ * SSD_ERR_INVALID_ARG.  The chunk states and the recurrence are those of
+ * ssd_chunk_scan in every variant.
+ */
+#define SSD_VARIANT_DEFAULT 0
+#define SSD_VARIANT_BF16_DECAY 1
+#define SSD_VARIANT_LOADED_MASK 2
+ssd_status ssd_chunk_scan_ablation(const ssd_scan_desc* desc, int32_t variant, const void* x,
+                                   const float* dt, const float* dt_bias, const float* A,
+                                   const void* B, const void* C, const float* D,
+                                   const float* initial_state, void* y, float* final_state,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One decode step of the recurrence, the state updated in place.

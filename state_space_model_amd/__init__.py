@@ -32,8 +32,12 @@ SSD_SCHEDULE_CHAIN = 1
 STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
                 4: "SSD_ERR_ALIGNMENT", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE",
                 7: "SSD_ERR_HIP"}
+SSD_VARIANT_DEFAULT = 0
+SSD_VARIANT_BF16_DECAY = 1
+SSD_VARIANT_LOADED_MASK = 2
 EXPORTED = ("ssd_chunk_scan", "ssd_chunk_scan_timed", "ssd_chunk_scan_workspace_bytes",
-            "ssd_chunk_scan_schedule", "ssd_step", "ssd_conv1d", "ssd_conv1d_step",
+            "ssd_chunk_scan_schedule", "ssd_chunk_scan_ablation",
+            "ssd_step", "ssd_conv1d", "ssd_conv1d_step",
             "ssd_chunk_scan_backward", "ssd_chunk_scan_backward_workspace_bytes",
             "ssd_status_string", "ssd_abi_version")
 
@@ -81,6 +85,8 @@ def _load() -> ctypes.CDLL:
     L.ssd_chunk_scan_timed.restype = i32
     L.ssd_chunk_scan_timed.argtypes = ([ctypes.POINTER(ScanDesc)] + [vp] * 11 + [sz, vp]
                                        + [ctypes.POINTER(vp), ctypes.c_int])
+    L.ssd_chunk_scan_ablation.restype = i32
+    L.ssd_chunk_scan_ablation.argtypes = ([ctypes.POINTER(ScanDesc), i32] + [vp] * 11 + [sz, vp])
     L.ssd_chunk_scan_workspace_bytes.restype = sz
     L.ssd_chunk_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     L.ssd_chunk_scan_schedule.restype = i32
@@ -190,7 +196,8 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
                    return_final_state: bool = True,
                    y: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None,
-                   phase_events: Optional[Sequence[torch.cuda.Event]] = None
+                   phase_events: Optional[Sequence[torch.cuda.Event]] = None,
+                   variant: int = SSD_VARIANT_DEFAULT
                    ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunked SSD scan (prefill) on the current stream.
 
@@ -200,6 +207,8 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     Output and workspace tensors may be passed in to avoid allocation.
     `phase_events`: optional SSD_SCAN_PHASES+1 torch.cuda.Event objects
     (created with enable_timing=True) recorded around the scan's kernels.
+    `variant`: SSD_VARIANT_BF16_DECAY or SSD_VARIANT_LOADED_MASK runs the
+    ablation variant of the output path (ssd_chunk_scan_ablation).
     """
     _scan_shapes(x, dt, A, B, C, D, dt_bias, initial_state)
     Bt, T, H, P = x.shape
@@ -227,7 +236,11 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     args = (ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A), _ptr(B), _ptr(C),
             _ptr(D), _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace),
             ctypes.c_size_t(wbytes), _stream(dev))
-    if phase_events is None:
+    if variant != SSD_VARIANT_DEFAULT:
+        if phase_events is not None:
+            raise ValueError("phase_events time the default variant only")
+        st = lib.ssd_chunk_scan_ablation(args[0], int(variant), *args[1:])
+    elif phase_events is None:
         st = lib.ssd_chunk_scan(*args)
     else:
         for e in phase_events:  # torch creates the HIP event at its first record

@@ -50,6 +50,7 @@ inline bool limits_ok(float lo, float hi) { return !isnan(lo) && !isnan(hi) && l
 struct ScanSizes {
   int64_t Nc = 0;
   bool chain = false;
+  bool cb_bf16 = false;
   int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0;  // element counts
   size_t ws_state_bytes = 0, ws_alpha_bytes = 0, ws_cb_bytes = 0, ws_bt_bytes = 0, ws_hb_bytes = 0,
          ws_total = 0;
@@ -57,7 +58,10 @@ struct ScanSizes {
 
 // force_phased: size (and run) the phased schedule even where the chain one
 // would be chosen (the gradients read the per-chunk states it leaves).
-ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s, bool force_phased = false) {
+// cb_f32: keep C B^T in float32 with bfloat16 io as well (the gradients read
+// it); otherwise the bfloat16 scan holds it in bfloat16.
+ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s, bool force_phased = false,
+                           bool cb_f32 = false) {
   if (!d) return SSD_ERR_INVALID_ARG;
   if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_DTYPE;
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
@@ -95,7 +99,8 @@ ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s, bool force_phas
   if (!mul_ok(bcg, d->dstate, &bt_elems) || !mul_ok(bt_elems, d->chunk, &bt_elems) ||
       !mul_ok(bt_elems, 2, &tmp))
     return SSD_ERR_UNSUPPORTED;
-  s->ws_cb_bytes = round_up((size_t)cb_elems * 4, kAlign);
+  s->cb_bf16 = d->io_dtype == SSD_BF16 && !cb_f32;
+  s->ws_cb_bytes = round_up((size_t)cb_elems * (s->cb_bf16 ? 2 : 4), kAlign);
   s->ws_bt_bytes = s->chain ? round_up((size_t)bt_elems * 2, kAlign) : 0;
   // the bfloat16 phased schedule hands the entering states to its output kernel in bf16
   s->ws_hb_bytes = (!s->chain && d->io_dtype == SSD_BF16) ? round_up((size_t)ws_elems * 2, kAlign) : 0;
@@ -109,10 +114,21 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
                      const float* D, const float* initial_state, void* y, float* final_state,
                      void* workspace, size_t workspace_bytes, hipStream_t stream,
                      hipEvent_t* events, int n_events, bool states_only = false,
-                     bool force_phased = false, bool keep_f32_states = false) {
+                     bool force_phased = false, bool keep_f32_states = false,
+                     int32_t variant = SSD_VARIANT_DEFAULT) {
   ScanSizes s;
-  ssd_status st = check_scan_desc(desc, &s, force_phased);
+  // a states-only run serves the gradients, which read C B^T in float32
+  ssd_status st = check_scan_desc(desc, &s, force_phased, states_only);
   if (st != SSD_OK) return st;
+  if (variant != SSD_VARIANT_DEFAULT) {
+    if (variant != SSD_VARIANT_BF16_DECAY && variant != SSD_VARIANT_LOADED_MASK)
+      return SSD_ERR_INVALID_ARG;
+    // compiled for the 130M / 2.7B / 1.3B head shape at chunks up to 256; the
+    // loaded-mask variant exists in the bfloat16 output path only
+    if (!ssd::ablation_shape(desc->headdim, desc->dstate) || desc->chunk > 256 ||
+        (variant == SSD_VARIANT_LOADED_MASK && desc->io_dtype != SSD_BF16))
+      return SSD_ERR_UNSUPPORTED;
+  }
   // phases 0-2 alone (entering states and C B^T left in the workspace, no y):
   // phased schedule only
   if (states_only && s.chain) return SSD_ERR_UNSUPPORTED;
@@ -177,6 +193,8 @@ ssd_status scan_impl(const ssd_scan_desc* desc, const void* x, const float* dt,
   a.chain = s.chain ? 1 : 0;
   a.states_only = states_only ? 1 : 0;
   a.keep_f32_states = keep_f32_states ? 1 : 0;
+  a.variant = variant;
+  a.cb_bf16 = s.cb_bf16 ? 1 : 0;
   hipError_t e = desc->io_dtype == SSD_BF16
                      ? ssd::launch_scan_bf16(a, (int)desc->headdim, (int)desc->dstate, stream, events)
                      : ssd::launch_scan_f32(a, (int)desc->headdim, (int)desc->dstate, stream, events);
@@ -281,7 +299,7 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   pl->r1.dt_softplus = 0;
   pl->r1.dt_min = 0.0f;
   pl->r1.dt_max = FLT_MAX;
-  if ((st = check_scan_desc(&pl->fw, &sf, true)) != SSD_OK) return st;
+  if ((st = check_scan_desc(&pl->fw, &sf, true, true)) != SSD_OK) return st;
   if ((st = check_scan_desc(&pl->r1, &s1, true)) != SSD_OK) return st;
   pl->scan_ws = sf.ws_total;
   pl->scan_ws_r1 = s1.ws_total;
@@ -365,6 +383,15 @@ ssd_status ssd_chunk_scan_timed(const ssd_scan_desc* desc, const void* x, const 
                                 hipEvent_t* phase_events, int n_events) {
   return scan_impl(desc, x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, workspace,
                    workspace_bytes, stream, phase_events, n_events);
+}
+
+ssd_status ssd_chunk_scan_ablation(const ssd_scan_desc* desc, int32_t variant, const void* x,
+                                   const float* dt, const float* dt_bias, const float* A,
+                                   const void* B, const void* C, const float* D,
+                                   const float* initial_state, void* y, float* final_state,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return scan_impl(desc, x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, workspace,
+                   workspace_bytes, stream, nullptr, 0, false, false, false, variant);
 }
 
 ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x_t, const float* dt_t,

@@ -20,7 +20,8 @@ struct ScanArgs {
   float* final_state;     // [Bt,H,P,N] or null
   float* ws_state;        // [Bt,H,Nc,P,N]: chunk summary states, then entering states
   float* ws_alpha;        // [Bt,H,Nc]: exp(total decay of the chunk)
-  float* ws_cb;           // [Bt,Nc,G,L,L]: C B^T of each chunk (causal 16x16 tiles)
+  float* ws_cb;           // [Bt,Nc,G,L,L]: C B^T of each chunk (causal 16x16 tiles); bf16
+                          // elements when cb_bf16
   void* ws_bt;            // [Bt,Nc,G,N,L] bf16: B of each chunk, transposed (token-contiguous)
   void* ws_hb;            // [Bt,H,Nc,P,N] bf16: entering states, rounded (bf16 phased schedule)
   int64_t Bt, T, H, G, L, Nc;
@@ -30,6 +31,9 @@ struct ScanArgs {
   int32_t states_only;    // 1: phases 0-2 only (C B^T, chunk and entering states; no y)
   int32_t keep_f32_states; // bf16 phased: the state pass also writes the float32 entering
                            // states over ws_state (the gradients read them)
+  int32_t cb_bf16 = 0;     // ws_cb holds bfloat16 (the bfloat16 forward scan) instead of float32
+  int32_t variant = 0;     // bf16 output path: 0 float32 decay and in-register mask; 1 decay
+                           // factors rounded to bf16; 2 mask loaded from a stored table
 };
 
 struct StepArgs {
@@ -121,6 +125,10 @@ struct BwdArgs {
 
 // Compiled shape variants.
 bool scan_shape_supported(int64_t P, int64_t N, int64_t L, bool bf16);
+
+// Head/state sizes with compiled ablation variants of the bfloat16 output path
+// (ssd_chunk_scan_ablation), at chunks up to 256.
+constexpr bool ablation_shape(int64_t P, int64_t N) { return P == 64 && N == 128; }
 
 // Head/state sizes with a compiled chain kernel (bfloat16 io, L <= 256).
 constexpr bool chain_variant(int64_t P, int64_t N) {

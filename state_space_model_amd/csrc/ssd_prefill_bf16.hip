@@ -107,8 +107,13 @@ __device__ __forceinline__ bf16x8 scale8(bf16x8 v, float4 w0, float4 w1) {
 }
 
 // ---------------------------------------------------------------------------
-// S = C B^T (float32) for the causal 16x16 tiles of every (b, c, g).
-// One wavefront computes tile t of (b, c, g) = bcg: (I, J), J <= I.
+// S = C B^T for the causal 16x16 tiles of every (b, c, g), float32
+// accumulation.  The forward scan keeps S in bfloat16 (a.cb_bf16): it is only
+// ever a matrix-core operand after its decay factor is applied, and half the
+// bytes halve the rows each column tile streams; the gradients' recompute of
+// the forward states keeps float32 (their own products read it).
+// One wavefront computes tile t of (b, c, g) = bcg: (I, J), J <= I, as
+// S^T = B_J C_I^T, so that a lane holds 4 consecutive keys of one query row.
 // ---------------------------------------------------------------------------
 template <int N>
 __device__ __forceinline__ void cb_tile_bf16(const ScanArgs& a, int64_t bcg, int t) {
@@ -133,10 +138,17 @@ __device__ __forceinline__ void cb_tile_bf16(const ScanArgs& a, int64_t bcg, int
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < N / 32; ++nb) acc = mma(cf[nb], bf[nb], acc);
-  float* S = a.ws_cb + bcg * a.L * a.L;
+  for (int nb = 0; nb < N / 32; ++nb) acc = mma(bf[nb], cf[nb], acc);
+  // lane holds S[16I + r16][16J + 4q + r], r = 0..3
+  const int64_t at = bcg * a.L * a.L + (int64_t)(16 * I + r16) * a.L + 16 * J + 4 * q;
+  if (a.cb_bf16) {
+    bf16x4 v;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) S[(int64_t)(16 * I + 4 * q + r) * a.L + 16 * J + r16] = acc[r];
+    for (int r = 0; r < 4; ++r) v[r] = (bf16)acc[r];
+    st4b(reinterpret_cast<bf16*>(a.ws_cb) + at, v);
+  } else {
+    st4(a.ws_cb + at, make_float4(acc[0], acc[1], acc[2], acc[3]));
+  }
 }
 
 // Number of causal 16x16 tiles of one chunk and the C B^T blocks of a grid
@@ -164,14 +176,17 @@ __device__ __forceinline__ void cb_block_bf16(const ScanArgs& a, int ntiles, int
 // Shared per-chunk pieces.
 // ---------------------------------------------------------------------------
 
-// x of one chunk, in 8 x 8 blocks (8 token rows x 8 head columns): block id
-// -> token block id / (P/8), column block id % (P/8).  Rows past the chunk's
+// x of one chunk, in blocks of 8 token rows x CW head columns (CW = 8, or 4
+// when the workgroup has threads enough for the smaller blocks): block id ->
+// token block id / (P/CW), column block id % (P/CW).  Rows past the chunk's
 // end are zeros.  NXB blocks per thread cover LMAX rows.
-template <int P, int LMAX>
+template <int P, int LMAX, int NTH = kThreads>
 struct XStage {
-  static constexpr int NBLK8 = (LMAX / 8) * (P / 8);
-  static constexpr int NXB = (NBLK8 + kThreads - 1) / kThreads;
-  bf16x8 v[NXB][8];
+  static constexpr int CW = (LMAX / 8) * (P / 8) >= NTH ? 8 : 4;
+  static constexpr int NBLK = (LMAX / 8) * (P / CW);
+  static constexpr int NXB = (NBLK + NTH - 1) / NTH;
+  typedef __bf16 vrow __attribute__((ext_vector_type(CW)));
+  vrow v[NXB][8];
 
   __device__ __forceinline__ void load(const ScanArgs& a, int64_t b, int64_t c, int64_t h) {
     const int tid = threadIdx.x;
@@ -181,12 +196,20 @@ struct XStage {
     const int64_t xs = a.H * P;
 #pragma unroll
     for (int i = 0; i < NXB; ++i) {
-      const int id = min(tid + i * kThreads, NBLK8 - 1);
-      const int lb = id / (P / 8), cb = id % (P / 8);
+      const int id = min(tid + i * NTH, NBLK - 1);
+      const int lb = id / (P / CW), cb = id % (P / CW);
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int l = 8 * lb + r;
-        v[i][r] = ld8_masked(xg + min(l, Lc - 1) * xs + 8 * cb, l < Lc);
+        const bf16* src = xg + min(l, Lc - 1) * xs + CW * cb;
+        if constexpr (CW == 8) {
+          v[i][r] = ld8_masked(src, l < Lc);
+        } else {
+          uint2 u = *reinterpret_cast<const uint2*>(src);
+          u.x = l < Lc ? u.x : 0u;
+          u.y = l < Lc ? u.y : 0u;
+          v[i][r] = __builtin_bit_cast(vrow, u);
+        }
       }
     }
   }
@@ -195,71 +218,138 @@ struct XStage {
     constexpr int XTS = LMAX + 8;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int i = 0; i < NXB; ++i)
-#pragma unroll
-      for (int r = 0; r < 8; ++r) pin(v[i][r]);
-#pragma unroll
     for (int i = 0; i < NXB; ++i) {
-      const int id = tid + i * kThreads;
-      if (id < NBLK8) {
-        const int lb = id / (P / 8), cb = id % (P / 8);
-        bf16x8 tr[8];
-        transpose8(v[i], tr);
+      const int id = tid + i * NTH;
+      if (id < NBLK) {
+        const int lb = id / (P / CW), cb = id % (P / CW);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) st8(s_xt + (8 * cb + cc) * XTS + 8 * lb, tr[cc]);
+        for (int cc = 0; cc < CW; ++cc) {
+          bf16x8 col;
+#pragma unroll
+          for (int r = 0; r < 8; ++r) col[r] = v[i][r][cc];
+          st8(s_xt + (CW * cb + cc) * XTS + 8 * lb, col);
+        }
       }
     }
   }
 };
 
-// Factored-decay table: for a query block R >= 1 (queries 64R..) and a key
-// j of an earlier block, decay(i, j) Delta_j = u_i * s_w[(R-1)*LMAX + j] with
-// u_i = exp(cum_i - cum_r), r = 64R (both factors <= 1 since cum falls).
-template <int LMAX>
-__device__ __forceinline__ void factored_table(int Lc, const float* s_d, const float* s_cum,
-                                               float* s_w) {
-  constexpr int NBLK = LMAX / 64;
-  for (int e = threadIdx.x; e < (NBLK - 1) * LMAX; e += kThreads) {
-    const int R = e / LMAX + 1, j = e % LMAX;
-    const int r = min(64 * R, Lc - 1);
-    s_w[e] = (j < r) ? __fmul_rn(fast_exp(__fsub_rn(s_cum[r], s_cum[j])), s_d[j]) : 0.0f;
+// Variants of the output path, chosen at compile time:
+//   kDecayF32    decay factors in float32 (the library's path)
+//   kDecayBf16   every decay factor of the output path rounded to bfloat16
+//                before use (the decay-precision ablation)
+//   kMaskLoaded  the causal mask of the diagonal tiles read from a stored
+//                lower-triangular bit table instead of formed from an index
+//                comparison (the mask-placement ablation; same bits)
+enum : int { kDecayF32 = 0, kDecayBf16 = 1, kMaskLoaded = 2 };
+
+template <int VAR>
+__device__ __forceinline__ float decay_factor(float e) {
+  if constexpr (VAR == kDecayBf16) return (float)(bf16)e;
+  return e;
+}
+
+// Lower-triangular mask of a kMaxL x kMaxL chunk as bits: bit b of word
+// [i][wd] is set iff key 32 wd + b <= query i.  Read by the loaded-mask
+// variant only.
+struct TrilBits {
+  uint32_t w[kMaxL * (kMaxL / 32)];
+};
+constexpr TrilBits make_tril_bits() {
+  TrilBits t{};
+  for (int i = 0; i < kMaxL; ++i)
+    for (int wd = 0; wd < kMaxL / 32; ++wd) {
+      const int k = i - 32 * wd;
+      t.w[i * (kMaxL / 32) + wd] = k < 0 ? 0u : (k >= 31 ? 0xffffffffu : ((2u << k) - 1u));
+    }
+  return t;
+}
+__device__ const TrilBits kTrilBits = make_tril_bits();
+
+// Per-column-tile decay tables.  Column tile I >= 1 (queries 16I .. 16I+15)
+// takes token r = 16I as its reference: for a key j < r,
+//   decay(i, j) Delta_j = exp(cum_i - cum_r) * W_I[j],   W_I[j] = exp(cum_r - cum_j) Delta_j,
+// both factors <= 1 since cum falls.  Row I holds its 16I entries at 8 I (I-1);
+// only the rows of the chunk's tiles are written.
+constexpr int tile_table_size(int LMAX) { return 8 * (LMAX / 16) * (LMAX / 16 - 1); }
+
+template <int VAR, int NTH>
+__device__ __forceinline__ void tile_decay_table(int Lc, const float* s_d, const float* s_cum,
+                                                 float* s_w) {
+  const int nrt = (Lc + 15) / 16;
+  const int n = 8 * nrt * (nrt - 1);
+  for (int e = threadIdx.x; e < n; e += NTH) {
+    int I = (int)(0.5f + sqrtf(0.25f + 0.125f * (float)e));   // row: 8 I (I-1) <= e
+    if (8 * I * (I - 1) > e) --I;
+    else if (8 * I * (I + 1) <= e) ++I;
+    const int j = e - 8 * I * (I - 1);
+    s_w[e] = __fmul_rn(decay_factor<VAR>(fast_exp(__fsub_rn(s_cum[16 * I], s_cum[j]))), s_d[j]);
   }
 }
 
 // State weights w_l = Delta_l exp(cum_last - cum_l) of the chunk summary state.
-template <int LMAX>
+template <int LMAX, int NTH = kThreads>
 __device__ __forceinline__ void state_weights(int Lc, const float* s_d, const float* s_cum,
                                               float* s_ws) {
   const float cum_last = s_cum[Lc - 1];
-  for (int l = threadIdx.x; l < LMAX; l += kThreads)
+  for (int l = threadIdx.x; l < LMAX; l += NTH)
     s_ws[l] = (l < Lc) ? __fmul_rn(s_d[l], fast_exp(__fsub_rn(cum_last, s_cum[l]))) : 0.0f;
 }
 
-// Outputs of one chunk, y^T tiles [p][i]: wavefront w owns the 16-token
-// column tiles row_tile_of(w, k), k < LMAX/64, and all P/16 head tiles,
-// processed KP column tiles per pass.
+__device__ __forceinline__ f32x4 mma16(bf16x4 a, bf16x4 b, f32x4 c) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Column tile k of wavefront w of NW: the tiles are dealt in a snake order
+// (0 1 .. NW-1 NW-1 .. 1 0), which balances the triangular work.
+template <int NW>
+__device__ __forceinline__ int col_tile_of(int wave, int k) {
+  return NW * k + ((k & 1) ? NW - 1 - wave : wave);
+}
+
+// Outputs of one chunk, y^T tiles [p][i]: wavefront w of NW owns the one or
+// two 16-query column tiles col_tile_of<NW>(w, k) and all P/16 head tiles.
+// For column tile I (reference token r = 16I, query i = 16I + lane%16):
+//   acc  = exp(cum_r) * sum_n bf16(h_{c-1})[p][n] C[i][n]          inter-chunk term
+//   acc += sum_{j < r} x^T[p][j] bf16(S[i][j] W_I[j])               earlier key tiles
+//   acc *= exp(cum_i - cum_r)
+//   acc += sum_{r <= j <= i} x^T[p][j] bf16(S[i][j] exp(cum_i - cum_j) Delta_j)
+//   y[i][p] = bf16(acc + D x[i][p])
+// so an earlier key costs one multiply (the exponentials are in the table)
+// and only the 16 x 16 diagonal tile takes exponentials and the causal
+// select (made before the exponential's result is used).  Earlier keys go 32
+// at a time through v_mfma_f32_16x16x32_bf16 (lane: 8 consecutive keys 8q ..);
+// a 16-key remainder and the diagonal tile through v_mfma_f32_16x16x16_bf16
+// (lane: keys 4q ..).
 //   s_h   bf16(h_{c-1})[p][n] (row stride N + 8): the inter-chunk operand
 //   s_xt  bf16 x^T[p][j]     (row stride LMAX + 8), zero past the chunk
-//   s_d, s_cum, s_w: Delta, cum and the factored-decay table of the chunk
-// S (C B^T) and C come from global memory (L2: shared by all heads of a
-// group).  A pass's C fragments and the first S block of each of its column
-// tiles are loaded ahead (prefetch()), so that their latency hides behind
-// other work: the next pass's behind this pass's intra-chunk term, the first
-// pass's behind whatever the kernel does between prefetch() and run().
-// Every accumulator sees the same instruction sequence whatever KP is.
-template <int P, int N, int LMAX, int KP>
+//   s_d, s_cum, s_w: Delta, cum and the per-tile decay tables of the chunk
+// S (C B^T, bfloat16) and C come from global memory (L2: shared by all heads
+// of a group).  Every S row a wavefront needs is requested at once by
+// prefetch() (one round trip instead of one per key step), together with the
+// first tile's C: tile 0's 32-key steps fill sf from the front, tile 1's from
+// the back (their counts add up to NS), so every register index is static.
+// C_AHEAD: the second tile's C is loaded behind the first tile's intra term
+// (else at the second tile's start, 16 registers fewer).
+template <int P, int N, int LMAX, int NW, int VAR = kDecayF32, bool C_AHEAD = true>
 struct ChunkOut {
   static constexpr int TP = P / 16;
-  static constexpr int RT = LMAX / 64;
-  static constexpr int NPASS = RT / KP;
+  static constexpr int NT = LMAX / 16;   // 16-query column tiles of a chunk
+  static constexpr int CT = NT / NW;     // column tiles per wavefront
+  static_assert(NT % NW == 0 && (CT == 1 || CT == 2), "one or two column tiles per wavefront");
+  // 32-key steps before the wavefront's tiles: tile w has w/2, and with a
+  // second tile 2NW-1-w the two add up to NW-1
+  static constexpr int NS = CT == 2 ? NW - 1 : (NW - 1) / 2;
   static constexpr int XTS = LMAX + 8, HS = N + 8;
-  static_assert(RT % KP == 0, "passes must cover the column tiles");
 
   const ScanArgs& a;
   int64_t b, c, h, g;
   int Lc;
-  bf16x8 cf[N / 32][KP];   // C[i][32 nb + 8q ..] of the pass's column tiles
-  float4 s0[KP][4];        // first 64-key block of S for each column tile
+  bf16x8 cf[N / 32];              // C[i][32 nb + 8q ..] of the tile about to run
+  bf16x8 sf[NS > 0 ? NS : 1];     // S[i][32 ks + 8q ..] of the 32-key steps
+  bf16x4 sod[CT], sdg[CT];        // S of the 16-key step before the diagonal, and of the diagonal
 
   __device__ __forceinline__ ChunkOut(const ScanArgs& a_, int64_t b_, int64_t c_, int64_t h_,
                                       int64_t g_, int Lc_)
@@ -278,40 +368,50 @@ struct ChunkOut {
   }
   __device__ __forceinline__ int nrt() const { return (Lc + 15) / 16; }
 
-  // S[ri][16t + 4q ..] of 64-key block jb, tile t (tiles past the diagonal
-  // tile are never written: the diagonal one is read instead)
-  __device__ __forceinline__ void load_s(int I, int jb, float4 (&st)[4]) const {
+  // C fragments of column tile I (rows past the chunk read its last row, with
+  // no zeroing select: they feed only output columns that are never stored)
+  __device__ __forceinline__ void load_c(int I) {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
-    const float* sr = a.ws_cb + ((b * a.Nc + c) * a.G + g) * a.L * a.L +
-                      (int64_t)(16 * I + r16) * a.L + 4 * q;
+    const bf16* Cg = reinterpret_cast<const bf16*>(a.C) + ((b * a.T + c * a.L) * a.G + g) * N + 8 * q;
+    const int i = min(16 * I + r16, Lc - 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) st[t] = ld4(sr + 64 * jb + 16 * min(t, I - 4 * jb));
+    for (int nb = 0; nb < N / 32; ++nb) cf[nb] = ld8(Cg + i * a.G * N + nb * 32);
   }
 
-  // C fragments and first S blocks of a pass.  The C rows are loaded with no
-  // zeroing select (rows past the chunk read its last row: they only feed
-  // output columns that are never stored): with the select the compiler
-  // waited for these loads right after issuing them, which left nothing in
-  // flight behind the intra-chunk term (chain schedule 1.92 -> 1.85 ms at
-  // 8 x 16384).
-  __device__ __forceinline__ void prefetch(int pass) {
+  // The first tile's C and every S row the wavefront's tiles need.  Each load
+  // is issued on every path (exact waits): a tile past the chunk, or a step a
+  // tile does not have, reads the first keys of the chunk's last tile.
+  __device__ __forceinline__ void prefetch() {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
     const int wave = wave_id(), n_rt = nrt();
-    const bf16* Cg = reinterpret_cast<const bf16*>(a.C) + ((b * a.T + c * a.L) * a.G + g) * N + 8 * q;
-    const int64_t crs = a.G * N;
+    load_c(min(col_tile_of<NW>(wave, 0), n_rt - 1));
+    const bf16* S = reinterpret_cast<const bf16*>(a.ws_cb) + ((b * a.Nc + c) * a.G + g) * a.L * a.L;
+    const bf16* row[CT];
+    int nf[CT];
 #pragma unroll
-    for (int k = 0; k < KP; ++k) {
-      const int I = row_tile_of(wave, pass * KP + k);
+    for (int k = 0; k < CT; ++k) {
+      const int I = col_tile_of<NW>(wave, k);
       const bool v = I < n_rt;
-      const int i = 16 * I + r16;
+      const int Ic = v ? I : n_rt - 1;
+      row[k] = S + (int64_t)(16 * Ic + r16) * a.L;
+      nf[k] = v ? I >> 1 : 0;
+      sod[k] = ld4b(row[k] + 16 * (Ic - (Ic & 1)) + 4 * q);
+      sdg[k] = ld4b(row[k] + 16 * Ic + 4 * q);
+    }
 #pragma unroll
-      for (int nb = 0; nb < N / 32; ++nb)
-        cf[nb][k] = ld8(Cg + min(i, Lc - 1) * crs + nb * 32);
-      load_s(v ? I : n_rt - 1, 0, s0[k]);   // unconditional: exact waits
+    for (int j = 0; j < NS; ++j) {
+      const bf16* src;
+      if constexpr (CT == 2) {
+        const int ks1 = NS - 1 - j;
+        src = j < nf[0] ? row[0] + 32 * j : (ks1 < nf[1] ? row[1] + 32 * ks1 : row[1]);
+      } else {
+        src = j < nf[0] ? row[0] + 32 * j : row[0];
+      }
+      sf[j] = ld8(src + 8 * q);
     }
   }
 
-  // All passes; pass 0 must have been prefetched.
+  // Both tiles; prefetch() must have been called.
   __device__ __forceinline__ void run(const float* s_d, const float* s_cum, const float* s_w,
                                       const bf16* s_xt, const bf16* s_h) {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
@@ -320,164 +420,120 @@ struct ChunkOut {
     const float Dh = a.D ? a.D[h] : 0.0f;
     bf16* yg = reinterpret_cast<bf16*>(a.y);
 
-#pragma unroll 1
-    for (int pass = 0; pass < NPASS; ++pass) {
-      int Ik[KP];
-      bool vk[KP];
 #pragma unroll
-      for (int k = 0; k < KP; ++k) {
-        Ik[k] = row_tile_of(wave, pass * KP + k);
-        vk[k] = Ik[k] < n_rt;
-      }
-      // later passes hold later (snake-ordered) tiles only when this one does
-      if (!vk[0]) break;
-      const bool more = pass + 1 < NPASS && row_tile_of(wave, (pass + 1) * KP) < n_rt;
-      f32x4 acc[KP][TP];
+    for (int k = 0; k < CT; ++k) {
+      const int I = col_tile_of<NW>(wave, k);
+      if (I >= n_rt) break;                 // later tiles lie further on
+      if (!C_AHEAD && k > 0) load_c(I);
+      f32x4 acc[TP];
 #pragma unroll
-      for (int k = 0; k < KP; ++k)
-#pragma unroll
-        for (int pt = 0; pt < TP; ++pt) acc[k][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int pt = 0; pt < TP; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-      // ---- inter-chunk term: acc[k] = exp(cum_i) * sum_n h_{c-1}[p][n] C[i][n] ----
+      // ---- inter-chunk term, then the decay from the chunk start to the
+      // tile's reference token ----
 #pragma unroll
       for (int nb = 0; nb < N / 32; ++nb) {
         bf16x8 hf[TP];
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) hf[pt] = ld8(s_h + (16 * pt + r16) * HS + 32 * nb + 8 * q);
 #pragma unroll
-        for (int k = 0; k < KP; ++k) {
-          if (!vk[k]) continue;
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) acc[k][pt] = mma(hf[pt], cf[nb][k], acc[k][pt]);
-        }
+        for (int pt = 0; pt < TP; ++pt) acc[pt] = mma(hf[pt], cf[nb], acc[pt]);
       }
-      // decay from the chunk start: column i = 16 I + r16 of every accumulator
-#pragma unroll
-      for (int k = 0; k < KP; ++k) {
-        if (!vk[k]) continue;
-        const int i = 16 * Ik[k] + r16;
-        const float sc = i < Lc ? fast_exp(s_cum[i]) : 0.0f;
+      // the C fragments are dead now: the next tile's fly behind this one's intra term
+      if (C_AHEAD && k + 1 < CT) load_c(min(col_tile_of<NW>(wave, k + 1), n_rt - 1));
+      {
+        const float er = decay_factor<VAR>(fast_exp(s_cum[16 * I]));
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[k][pt][r] = __fmul_rn(acc[k][pt][r], sc);
+          for (int r = 0; r < 4; ++r) acc[pt][r] = __fmul_rn(acc[pt][r], er);
       }
 
-      // ---- intra-chunk term: column tile by column tile, 64 keys (two 32-key slots) at a time ----
+      // ---- earlier key tiles: 32-key steps, then the odd 16-key one ----
+      const int ri = 16 * I + r16;
+      const float* wI = s_w + 8 * I * (I - 1);
+      const int nfull = I >> 1;
 #pragma unroll
-      for (int k = 0; k < KP; ++k) {
-        if (!vk[k]) continue;
-        const int I = Ik[k], R = I >> 2;
-        const int ri = 16 * I + r16;
-        const float cum_i = s_cum[min(ri, Lc - 1)];
-        const float u_i = R > 0 ? fast_exp(__fsub_rn(cum_i, s_cum[64 * R])) : 0.0f;
-        auto block = [&](int jb, const float4 (&st)[4]) {
-          // k-slots of a 32-key half (key tiles 2s, 2s+1): slot e < 4 -> key
-          // 16(2s) + 4q + e, slot e >= 4 -> key 16(2s+1) + 4q + e - 4
-          const bf16* xq = s_xt + (int64_t)r16 * XTS + 64 * jb + 4 * q;
-          if (jb < R) {
-            const float* wrow = &s_w[(R - 1) * LMAX + 64 * jb + 4 * q];
+      for (int ks = 0; ks < NS; ++ks) {
+        if (ks < nfull) {
+          const bf16x8 st = sf[k == 0 ? ks : NS - 1 - ks];
+          const int k0 = 32 * ks + 8 * q;
+          const float4 w0 = ld4(wI + k0), w1 = ld4(wI + k0 + 4);
+          bf16x8 m;
+          m[0] = (bf16)__fmul_rn((float)st[0], w0.x);
+          m[1] = (bf16)__fmul_rn((float)st[1], w0.y);
+          m[2] = (bf16)__fmul_rn((float)st[2], w0.z);
+          m[3] = (bf16)__fmul_rn((float)st[3], w0.w);
+          m[4] = (bf16)__fmul_rn((float)st[4], w1.x);
+          m[5] = (bf16)__fmul_rn((float)st[5], w1.y);
+          m[6] = (bf16)__fmul_rn((float)st[6], w1.z);
+          m[7] = (bf16)__fmul_rn((float)st[7], w1.w);
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-              const float4 w0 = ld4(wrow + 32 * sh), w1 = ld4(wrow + 32 * sh + 16);
-              const float4 t0v = st[2 * sh], t1v = st[2 * sh + 1];
-              bf16x8 m;
-              m[0] = (bf16)__fmul_rn(__fmul_rn(t0v.x, u_i), w0.x);
-              m[1] = (bf16)__fmul_rn(__fmul_rn(t0v.y, u_i), w0.y);
-              m[2] = (bf16)__fmul_rn(__fmul_rn(t0v.z, u_i), w0.z);
-              m[3] = (bf16)__fmul_rn(__fmul_rn(t0v.w, u_i), w0.w);
-              m[4] = (bf16)__fmul_rn(__fmul_rn(t1v.x, u_i), w1.x);
-              m[5] = (bf16)__fmul_rn(__fmul_rn(t1v.y, u_i), w1.y);
-              m[6] = (bf16)__fmul_rn(__fmul_rn(t1v.z, u_i), w1.z);
-              m[7] = (bf16)__fmul_rn(__fmul_rn(t1v.w, u_i), w1.w);
+          for (int pt = 0; pt < TP; ++pt)
+            acc[pt] = mma(ld8(s_xt + (16 * pt + r16) * XTS + k0), m, acc[pt]);
+        }
+      }
+      if (I & 1) {   // the key tile just before the diagonal one
+        const int k0 = 16 * (I - 1) + 4 * q;
+        const float4 w = ld4(wI + k0);
+        const bf16x4 st = sod[k];
+        bf16x4 m;
+        m[0] = (bf16)__fmul_rn((float)st[0], w.x);
+        m[1] = (bf16)__fmul_rn((float)st[1], w.y);
+        m[2] = (bf16)__fmul_rn((float)st[2], w.z);
+        m[3] = (bf16)__fmul_rn((float)st[3], w.w);
 #pragma unroll
-              for (int pt = 0; pt < TP; ++pt) {
-                const bf16* xr = xq + pt * 16 * XTS + 32 * sh;
-                acc[k][pt] = mma(cat(ld4b(xr), ld4b(xr + 16)), m, acc[k][pt]);
-              }
-            }
-          } else {
-            const int nt = I - 4 * R + 1;          // key tiles up to the diagonal (uniform)
+        for (int pt = 0; pt < TP; ++pt)
+          acc[pt] = mma16(ld4b(s_xt + (16 * pt + r16) * XTS + k0), m, acc[pt]);
+      }
+      // decay from the reference token to the query
+      const float cum_i = s_cum[ri];
+      {
+        const float u = decay_factor<VAR>(fast_exp(__fsub_rn(cum_i, s_cum[16 * I])));
 #pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-              if (2 * sh < nt) {
-                const int j0 = 64 * jb + 32 * sh + 4 * q;   // keys j0..j0+3 and j0+16..j0+19
-                const float4 c0 = ld4(&s_cum[j0]), c1 = ld4(&s_cum[j0 + 16]);
-                const float4 d0 = ld4(&s_d[j0]), d1 = ld4(&s_d[j0 + 16]);
-                const float4 t0v = st[2 * sh], t1v = st[2 * sh + 1];
-                const bool hi = 2 * sh + 1 < nt;
-                auto dec = [&](bool on, float sv, float cj, float dj) {
-                  return on ? __fmul_rn(__fmul_rn(sv, fast_exp(__fsub_rn(cum_i, cj))), dj) : 0.0f;
-                };
-                bf16x8 m;
-                m[0] = (bf16)dec(j0 + 0 <= ri, t0v.x, c0.x, d0.x);
-                m[1] = (bf16)dec(j0 + 1 <= ri, t0v.y, c0.y, d0.y);
-                m[2] = (bf16)dec(j0 + 2 <= ri, t0v.z, c0.z, d0.z);
-                m[3] = (bf16)dec(j0 + 3 <= ri, t0v.w, c0.w, d0.w);
-                m[4] = (bf16)dec(hi && j0 + 16 <= ri, t1v.x, c1.x, d1.x);
-                m[5] = (bf16)dec(hi && j0 + 17 <= ri, t1v.y, c1.y, d1.y);
-                m[6] = (bf16)dec(hi && j0 + 18 <= ri, t1v.z, c1.z, d1.z);
-                m[7] = (bf16)dec(hi && j0 + 19 <= ri, t1v.w, c1.w, d1.w);
-                // the upper key tile may lie past the staged rows of a ragged
-                // chunk's x^T: never read it then
-                bf16x4 z4;
+        for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) z4[e] = (bf16)0.0f;
+          for (int r = 0; r < 4; ++r) acc[pt][r] = __fmul_rn(acc[pt][r], u);
+      }
+      // ---- diagonal tile: keys j0 .. j0+3, causal select before the result is used ----
+      {
+        const int j0 = 16 * I + 4 * q;
+        const float4 cj = ld4(s_cum + j0), dj = ld4(s_d + j0);
+        const bf16x4 st = sdg[k];
+        bool mk[4];
+        if constexpr (VAR == kMaskLoaded) {
+          const uint32_t bits = kTrilBits.w[ri * (kMaxL / 32) + (j0 >> 5)] >> (j0 & 31);
 #pragma unroll
-                for (int pt = 0; pt < TP; ++pt) {
-                  const bf16* xr = xq + pt * 16 * XTS + 32 * sh;
-                  acc[k][pt] = mma(cat(ld4b(xr), hi ? ld4b(xr + 16) : z4), m, acc[k][pt]);
-                }
-              }
-            }
-          }
+          for (int e = 0; e < 4; ++e) mk[e] = (bits >> e) & 1u;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mk[e] = j0 + e <= ri;
+        }
+        auto dec = [&](bool on, float sv, float cjv, float djv) {
+          return on ? (bf16)__fmul_rn(__fmul_rn(sv, decay_factor<VAR>(fast_exp(__fsub_rn(cum_i, cjv)))), djv)
+                    : (bf16)0.0f;
         };
-        float4 sa[4], sb[4];
+        bf16x4 m;
+        m[0] = dec(mk[0], (float)st[0], cj.x, dj.x);
+        m[1] = dec(mk[1], (float)st[1], cj.y, dj.y);
+        m[2] = dec(mk[2], (float)st[2], cj.z, dj.z);
+        m[3] = dec(mk[3], (float)st[3], cj.w, dj.w);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) sa[t] = s0[k][t];
-        // the C fragments are dead now: the next pass's are loaded behind this intra term
-        if (k == 0 && more) {
-          const bf16* Cg = reinterpret_cast<const bf16*>(a.C) + ((b * a.T + t0) * a.G + g) * N + 8 * q;
-          const int64_t crs = a.G * N;
-#pragma unroll
-          for (int kk = 0; kk < KP; ++kk) {
-            const int In = row_tile_of(wave, (pass + 1) * KP + kk);
-            const int i = 16 * In + r16;
-#pragma unroll
-            for (int nb = 0; nb < N / 32; ++nb)
-              cf[nb][kk] = ld8(Cg + min(i, Lc - 1) * crs + nb * 32);   // see prefetch
-          }
-        }
-        for (int jb = 0; jb <= R; jb += 2) {
-          if (jb + 1 <= R) load_s(I, jb + 1, sb);
-          block(jb, sa);
-          if (jb + 1 > R) break;
-          if (jb + 2 <= R) load_s(I, jb + 2, sa);
-          block(jb + 1, sb);
-        }
-        // this column tile's first S block is consumed: load the next pass's
-        if (more) {
-          const int In = row_tile_of(wave, (pass + 1) * KP + k);
-          if (In < n_rt) load_s(In, 0, s0[k]);
-        }
+        for (int pt = 0; pt < TP; ++pt)
+          acc[pt] = mma16(ld4b(s_xt + (16 * pt + r16) * XTS + j0), m, acc[pt]);
       }
 
       // ---- skip term and store: lane holds y[i][p..p+3], p = 16 pt + 4q ----
+      if (ri < Lc) {
+        const int64_t rowy = ((b * a.T + t0 + ri) * a.H + h) * P;
 #pragma unroll
-      for (int k = 0; k < KP; ++k) {
-        if (!vk[k]) continue;
-        const int i = 16 * Ik[k] + r16;
-        if (i < Lc) {
-          bf16* row = yg + ((b * a.T + t0 + i) * a.H + h) * P;
+        for (int pt = 0; pt < TP; ++pt) {
+          const int p0 = 16 * pt + 4 * q;
+          bf16x4 o;
 #pragma unroll
-          for (int pt = 0; pt < TP; ++pt) {
-            const int p0 = 16 * pt + 4 * q;
-            bf16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              o[r] = (bf16)__fmaf_rn(Dh, (float)s_xt[(p0 + r) * XTS + i], acc[k][pt][r]);
-            st4b(row + p0, o);
-          }
+          for (int r = 0; r < 4; ++r)
+            o[r] = (bf16)__fmaf_rn(Dh, (float)s_xt[(p0 + r) * XTS + ri], acc[pt][r]);
+          st4b(yg + rowy + p0, o);
         }
       }
     }
@@ -662,17 +718,37 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_bf16(ScanArgs a
 // entering state h_{c-1} (rounded to bf16 by the state pass) is copied to
 // LDS, x is staged transposed, then the shared ChunkOut runs.
 // ---------------------------------------------------------------------------
-constexpr int kOutPass = 2;     // column tiles per output pass, phased schedule
-constexpr int kChainPass = 1;   // and chain schedule (which holds more besides)
+// The output kernels run LMAX/32 wavefronts per workgroup (two 16-query
+// column tiles each; the chain kernel 8): two workgroups share a compute unit
+// (LDS), so each SIMD keeps four wavefronts to cover the latency of the rows
+// they read from L2.  Delta and its prefix sum are formed by the first 256
+// threads with the same arithmetic as every other kernel of the scan
+// (bit-identical values).
+constexpr int kOutThreads = 512;   // the chain kernel, and the phased one at chunks <= 256
+constexpr int kOutWaves = kOutThreads / 64;
 
-template <int P, int N, int LMAX>
-__global__ __launch_bounds__(kThreads) void k_chunk_out_bf16(ScanArgs a) {
-  constexpr int NBLK = LMAX / 64;
+// Delta and the chunk-local prefix sum for a workgroup of more than kThreads
+// threads: the first kThreads compute (as chunk_delta_cumsum), all wait.
+__device__ __forceinline__ void chunk_delta_cumsum_wide(const ScanArgs& a, int64_t b, int64_t c,
+                                                        int64_t h, float* s_d, float* s_cum,
+                                                        float* s_wsum) {
+  const bool on = threadIdx.x < kThreads;
+  DeltaScan ds{};
+  if (on) ds = chunk_scan_stage1(a, c, h, chunk_dt_load(a, b, c, h), s_wsum);
+  __syncthreads();
+  if (on) chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
+  __syncthreads();
+}
+
+template <int P, int N, int LMAX, int VAR>
+__global__ __launch_bounds__(2 * LMAX) __attribute__((amdgpu_waves_per_eu(LMAX <= 256 ? 4 : 2)))
+void k_chunk_out_bf16(ScanArgs a) {
   constexpr int XTS = LMAX + 8, HS = N + 8;
+  constexpr int NTH = 2 * LMAX, NW = NTH / 64;
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
   __shared__ float s_wsum[4];
-  __shared__ __attribute__((aligned(16))) float s_w[(NBLK - 1) * LMAX + 4];
+  __shared__ __attribute__((aligned(16))) float s_w[tile_table_size(LMAX) + 4];
   __shared__ __attribute__((aligned(16))) bf16 s_xt[P * XTS];
   __shared__ __attribute__((aligned(16))) bf16 s_h[P * HS];
 
@@ -683,23 +759,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk_out_bf16(ScanArgs a) {
   const int Lc = chunk_len(a, c);
 
   // every global load of the staging is issued before the first barrier
-  XStage<P, LMAX> xs;
+  XStage<P, LMAX, NTH> xs;
   xs.load(a, b, c, h);
   constexpr int HV = P * N / 8;                 // 8-element groups of the state
-  constexpr int NHV = (HV + kThreads - 1) / kThreads;
+  constexpr int NHV = (HV + NTH - 1) / NTH;
   const bf16* hp = reinterpret_cast<const bf16*>(a.ws_hb) +
                    ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
   bf16x8 hv[NHV];
 #pragma unroll
-  for (int i = 0; i < NHV; ++i) hv[i] = ld8(hp + min(tid + i * kThreads, HV - 1) * 8);
-  ChunkOut<P, N, LMAX, kOutPass> out(a, b, c, h, g, Lc);
-  out.prefetch(0);
-  chunk_delta_cumsum(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
-  factored_table<LMAX>(Lc, s_d, s_cum, s_w);
+  for (int i = 0; i < NHV; ++i) hv[i] = ld8(hp + min(tid + i * NTH, HV - 1) * 8);
+  ChunkOut<P, N, LMAX, NW, VAR> out(a, b, c, h, g, Lc);
+  out.prefetch();
+  chunk_delta_cumsum_wide(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
+  tile_decay_table<VAR, NTH>(Lc, s_d, s_cum, s_w);
   xs.store(s_xt);
 #pragma unroll
   for (int i = 0; i < NHV; ++i) {
-    const int e = tid + i * kThreads;
+    const int e = tid + i * NTH;
     if (e < HV) st8(s_h + ((e * 8) / N) * HS + (e * 8) % N, hv[i]);
   }
   __syncthreads();
@@ -743,10 +819,11 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int nti
   for (int cc = 0; cc < 8; ++cc) st8(dst + cc * a.L, tr[cc]);
 }
 
-// Chain kernel: one workgroup per (b, h), chunks in order.  Wavefront w keeps
-// the float32 state tiles [n][p] of n-tiles NTW*w .. NTW*w + NTW-1 (all p) in
-// matrix-core accumulators for the whole sequence; LDS holds only bf16(h) as
-// the inter-chunk operand.  Per chunk c:
+// Chain kernel: one workgroup of 8 wavefronts per (b, h), chunks in order.
+// The float32 state [n][p] lives in matrix-core accumulators for the whole
+// sequence: wavefront w keeps n-tile w % (N/16) and P/16 / (8 / (N/16))
+// p-tiles of it; LDS holds only bf16(h) as the inter-chunk operand.  Per
+// chunk c:
 //   stage:   Delta/cum, x^T and bf16(h_{c-1}) into LDS, decay tables
 //   outputs: ChunkOut (inter-chunk term from the LDS copy)
 //   state:   S_c = sum_ks (B^T w)_bf16 x into a fresh accumulator, then
@@ -756,81 +833,79 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int nti
 // then the next chunk's x and dt (consumed after the next barrier); the next
 // chunk's first output-pass operands right after that barrier, so they fly
 // during the staging.
-template <int P, int N, int LMAX>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+template <int P, int N, int LMAX, int VAR>
+__global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void k_chain_bf16(ScanArgs a) {
-  constexpr int TP = P / 16, TN = N / 16, NTW = TN / 4;
-  constexpr int NBLK = LMAX / 64, NKS = LMAX / 32;
+  constexpr int NTH = kOutThreads, NW = kOutWaves;
+  constexpr int TP = P / 16, TN = N / 16;
+  constexpr int WPN = NW / TN;          // wavefronts per n-tile
+  constexpr int TPW = TP / WPN;         // p-tiles per wavefront
+  constexpr int NKS = LMAX / 32;
   constexpr int XTS = LMAX + 8, HS = N + 8;
-  static_assert(TN % 4 == 0, "N must give every wavefront whole n-tiles");
-  using Out = ChunkOut<P, N, LMAX, kChainPass>;
+  static_assert(TN <= NW && NW % TN == 0 && TP % WPN == 0, "whole state tiles per wavefront");
+  using Out = ChunkOut<P, N, LMAX, NW, VAR, false>;
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
   __shared__ __attribute__((aligned(16))) float s_ws[LMAX];
   __shared__ float s_wsum[4];
-  __shared__ __attribute__((aligned(16))) float s_w[(NBLK - 1) * LMAX + 4];
+  __shared__ __attribute__((aligned(16))) float s_w[tile_table_size(LMAX) + 4];
   __shared__ __attribute__((aligned(16))) bf16 s_xt[P * XTS];
   __shared__ __attribute__((aligned(16))) bf16 s_h[P * HS];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool scan_thread = threadIdx.x < kThreads;   // Delta and its prefix sum
+  const int nt = wave % TN, pt0 = (wave / TN) * TPW;
   const int64_t u = xcd_remap(blockIdx.x, gridDim.x);   // heads of a batch row share an XCD
   const int64_t h = u % a.H, b = u / a.H;
   const int64_t g = h / (a.H / a.G);
   const int64_t sbase = (b * a.H + h) * (int64_t)(P * N);
 
   Out out(a, b, 0, h, g, chunk_len(a, 0));
-  XStage<P, LMAX> xs;
+  XStage<P, LMAX, NTH> xs;
   xs.load(a, b, 0, h);
-  float2 dtv = chunk_dt_load(a, b, 0, h);
-  out.prefetch(0);
+  float2 dtv = scan_thread ? chunk_dt_load(a, b, 0, h) : make_float2(0.f, 0.f);
 
-  // state tiles: acc_h[in][pt] holds h[p = 16 pt + r16][n = 16 (NTW w + in) + 4q + r]
-  f32x4 acc_h[NTW][TP];
+  // state tiles: acc_h[ip] holds h[p = 16 (pt0 + ip) + r16][n = 16 nt + 4q + r]
+  f32x4 acc_h[TPW];
   {
     const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
 #pragma unroll
-    for (int in = 0; in < NTW; ++in)
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        if (a.h0) {
-          const float4 v =
-              ld4(a.h0 + sbase + (16 * pt + r16) * N + 16 * (NTW * wave + in) + 4 * q);
-          acc_h[in][pt] = f32x4{v.x, v.y, v.z, v.w};
-        } else {
-          acc_h[in][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int ip = 0; ip < TPW; ++ip) {
+      if (a.h0) {
+        const float4 v = ld4(a.h0 + sbase + (16 * (pt0 + ip) + r16) * N + 16 * nt + 4 * q);
+        acc_h[ip] = f32x4{v.x, v.y, v.z, v.w};
+      } else {
+        acc_h[ip] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    }
   }
 
   for (int64_t c = 0; c < a.Nc; ++c) {
     const int Lc = chunk_len(a, c);
     // ---- stage chunk c ----
-    const DeltaScan ds = chunk_scan_stage1(a, c, h, dtv, s_wsum);
+    DeltaScan ds{};
+    if (scan_thread) ds = chunk_scan_stage1(a, c, h, dtv, s_wsum);
     __syncthreads();   // every wavefront is done with chunk c-1's LDS; s_wsum published
-    if (c > 0) {
-      // first output pass of this chunk: younger than x, which the staging
-      // below waits for anyway, and in flight during the staging
-      out.c = c;
-      out.Lc = Lc;
-      out.prefetch(0);
-    }
-    chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
+    if (scan_thread) chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
     xs.store(s_xt);
     {
       const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
 #pragma unroll
-      for (int in = 0; in < NTW; ++in)
+      for (int ip = 0; ip < TPW; ++ip) {
+        bf16x4 v;
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          bf16x4 v;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = (bf16)acc_h[in][pt][r];
-          st4b(s_h + (16 * pt + r16) * HS + 16 * (NTW * wave + in) + 4 * q, v);
-        }
+        for (int r = 0; r < 4; ++r) v[r] = (bf16)acc_h[ip][r];
+        st4b(s_h + (16 * (pt0 + ip) + r16) * HS + 16 * nt + 4 * q, v);
+      }
     }
     __syncthreads();
-    factored_table<LMAX>(Lc, s_d, s_cum, s_w);
-    state_weights<LMAX>(Lc, s_d, s_cum, s_ws);
+    // this chunk's C and S rows, in flight during the tables (issued once the
+    // staging registers are free)
+    out.c = c;
+    out.Lc = Lc;
+    out.prefetch();
+    tile_decay_table<VAR, NTH>(Lc, s_d, s_cum, s_w);
+    state_weights<LMAX, NTH>(Lc, s_d, s_cum, s_ws);
     const float alpha = fast_exp(s_cum[Lc - 1]);
     __syncthreads();
 
@@ -838,72 +913,53 @@ void k_chain_bf16(ScanArgs a) {
     out.run(s_d, s_cum, s_w, s_xt, s_h);
 
     // ---- chunk summary state S_c, then h_c = fma(alpha, h_{c-1}, S_c) ----
-    // steps st = (ks, in): one x^T fragment per (ks, pt) serves every n-tile
-    // of the wavefront.  B^T fragments stream through a ring of RING register
-    // sets, RING steps ahead; the next chunk's x and dt are issued once the
-    // last fragment load is out.
+    // 32-token steps: the wavefront's B^T fragment (n-tile nt), scaled by the
+    // state weights, against its p-tiles' x^T fragments.  All the chunk's
+    // fragments are requested at once (steps past the chunk re-read its
+    // last), then the next chunk's x and dt.
     {
       const int nks = (Lc + 31) / 32;
       const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
       const bf16* btc = reinterpret_cast<const bf16*>(a.ws_bt) +
-                        ((b * a.Nc + c) * a.G + g) * (int64_t)(N * a.L) + 8 * q;
-      constexpr int NSTEP = NKS * NTW, RING = 4;
-      bf16x8 ring[RING];
-      auto issue = [&](int st) {
-        const int ks = st / NTW, in = st % NTW;
-        if (ks < nks)
-          ring[st % RING] = ld8(btc + (int64_t)(16 * (NTW * wave + in) + r16) * a.L + 32 * ks);
-      };
-      f32x4 t[NTW][TP];
+                        ((b * a.Nc + c) * a.G + g) * (int64_t)(N * a.L) +
+                        (int64_t)(16 * nt + r16) * a.L + 8 * q;
+      bf16x8 bt[NKS];
 #pragma unroll
-      for (int in = 0; in < NTW; ++in)
+      for (int ks = 0; ks < NKS; ++ks) bt[ks] = ld8(btc + 32 * min(ks, nks - 1));
+      {
+        // the last chunk re-reads itself: the same loads on every path
+        const int64_t cn = c + 1 < a.Nc ? c + 1 : c;
+        xs.load(a, b, cn, h);
+        if (scan_thread) dtv = chunk_dt_load(a, b, cn, h);
+      }
+      f32x4 t[TPW];
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) t[in][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ip = 0; ip < TPW; ++ip) t[ip] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < RING && st < NSTEP; ++st) issue(st);
-      bf16x8 xf[TP];
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) {
-        const int ks = st / NTW, in = st % NTW;
-        const bf16x8 frag = ring[st % RING];
-        if (st + RING < NSTEP) issue(st + RING);
-        if (st + RING == NSTEP - 1 || (st == 0 && NSTEP <= RING)) {
-          if (c + 1 < a.Nc) {
-            xs.load(a, b, c + 1, h);
-            dtv = chunk_dt_load(a, b, c + 1, h);
-          }
-        }
+      for (int ks = 0; ks < NKS; ++ks) {
         if (ks < nks) {
           const int l0 = 32 * ks + 8 * q;
-          if (in == 0) {
+          const bf16x8 bw = scale8(bt[ks], ld4(&s_ws[l0]), ld4(&s_ws[l0 + 4]));
 #pragma unroll
-            for (int pt = 0; pt < TP; ++pt) xf[pt] = ld8(s_xt + (16 * pt + r16) * XTS + l0);
-          }
-          const bf16x8 bw = scale8(frag, ld4(&s_ws[l0]), ld4(&s_ws[l0 + 4]));
-#pragma unroll
-          for (int pt = 0; pt < TP; ++pt) t[in][pt] = mma(bw, xf[pt], t[in][pt]);
+          for (int ip = 0; ip < TPW; ++ip)
+            t[ip] = mma(bw, ld8(s_xt + (16 * (pt0 + ip) + r16) * XTS + l0), t[ip]);
         }
       }
 #pragma unroll
-      for (int in = 0; in < NTW; ++in)
+      for (int ip = 0; ip < TPW; ++ip)
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc_h[in][pt][r] = __fmaf_rn(alpha, acc_h[in][pt][r], t[in][pt][r]);
+        for (int r = 0; r < 4; ++r) acc_h[ip][r] = __fmaf_rn(alpha, acc_h[ip][r], t[ip][r]);
     }
   }
 
   if (a.final_state) {
     const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
 #pragma unroll
-    for (int in = 0; in < NTW; ++in)
-#pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        const f32x4 v = acc_h[in][pt];
-        st4(a.final_state + sbase + (16 * pt + r16) * N + 16 * (NTW * wave + in) + 4 * q,
-            make_float4(v[0], v[1], v[2], v[3]));
-      }
+    for (int ip = 0; ip < TPW; ++ip) {
+      const f32x4 v = acc_h[ip];
+      st4(a.final_state + sbase + (16 * (pt0 + ip) + r16) * N + 16 * nt + 4 * q,
+          make_float4(v[0], v[1], v[2], v[3]));
+    }
   }
 }
 
@@ -924,13 +980,26 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
   if ((e = launch_state_pass(a, P, N, stream, true)) != hipSuccess) return e;
   if ((e = rec(3)) != hipSuccess) return e;
   if (a.states_only) return rec(4);   // entering states and C B^T only
-  if (a.L <= 256) {
-    hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 256>), dim3((unsigned)units), dim3(kThreads), 0,
-                       stream, a);
+  if (a.variant != kDecayF32) {
+    // ablation variants: the 2.7B / 1.3B head shape at chunks up to 256 only
+    if constexpr (ablation_shape(P, N)) {
+      if (a.L > 256) return hipErrorInvalidValue;
+      if (a.variant == kDecayBf16)
+        hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 256, kDecayBf16>), dim3((unsigned)units),
+                           dim3(512), 0, stream, a);
+      else
+        hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 256, kMaskLoaded>), dim3((unsigned)units),
+                           dim3(512), 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (a.L <= 256) {
+    hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 256, kDecayF32>), dim3((unsigned)units),
+                       dim3(512), 0, stream, a);
   } else {
     if constexpr (P <= 64) {
-      hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 512>), dim3((unsigned)units), dim3(kThreads), 0,
-                         stream, a);
+      hipLaunchKernelGGL((k_chunk_out_bf16<P, N, 512, kDecayF32>), dim3((unsigned)units),
+                         dim3(1024), 0, stream, a);
     } else {
       return hipErrorInvalidValue;
     }
@@ -954,10 +1023,24 @@ hipError_t launch_chain(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
     if ((e = rec(2)) != hipSuccess) return e;
     if ((e = rec(3)) != hipSuccess) return e;
     const unsigned chains = (unsigned)(a.Bt * a.H);
-    if (a.L <= 128) {
-      hipLaunchKernelGGL((k_chain_bf16<P, N, 128>), dim3(chains), dim3(kThreads), 0, stream, a);
+    if (a.variant != kDecayF32) {
+      if constexpr (ablation_shape(P, N)) {
+        if (a.L > 256) return hipErrorInvalidValue;
+        if (a.variant == kDecayBf16)
+          hipLaunchKernelGGL((k_chain_bf16<P, N, 256, kDecayBf16>), dim3(chains),
+                             dim3(kOutThreads), 0, stream, a);
+        else
+          hipLaunchKernelGGL((k_chain_bf16<P, N, 256, kMaskLoaded>), dim3(chains),
+                             dim3(kOutThreads), 0, stream, a);
+      } else {
+        return hipErrorInvalidValue;
+      }
+    } else if (a.L <= 128) {
+      hipLaunchKernelGGL((k_chain_bf16<P, N, 128, kDecayF32>), dim3(chains), dim3(kOutThreads),
+                         0, stream, a);
     } else {
-      hipLaunchKernelGGL((k_chain_bf16<P, N, 256>), dim3(chains), dim3(kThreads), 0, stream, a);
+      hipLaunchKernelGGL((k_chain_bf16<P, N, 256, kDecayF32>), dim3(chains), dim3(kOutThreads),
+                         0, stream, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return rec(4);

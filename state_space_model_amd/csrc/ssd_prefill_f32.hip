@@ -274,7 +274,15 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_chunk_state_f32(ScanArgs a,
 // and column tile.  Inside the token's own block the decay is exponentiated
 // element by element, with the causal mask selected first.
 // ---------------------------------------------------------------------------
-template <int P, int N, int PW, int LMAX>
+// VAR 1 (the decay-precision ablation, ssd_chunk_scan_ablation): every decay
+// factor of the output path is rounded to bfloat16 before use.
+template <int VAR>
+__device__ __forceinline__ float decay_f32(float e) {
+  if constexpr (VAR == 1) return (float)(__bf16)e;
+  return e;
+}
+
+template <int P, int N, int PW, int LMAX, int VAR>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void k_chunk_out_f32(ScanArgs a) {
   constexpr int PSPLIT = P / PW, TP = PW / 16;
@@ -386,7 +394,7 @@ void k_chunk_out_f32(ScanArgs a) {
     for (int e = tid; e < (NBLK - 1) * LMAX; e += kThreads) {
       const int R = e / LMAX + 1, j = e % LMAX;
       const int r = min(64 * R, Lc - 1);
-      s_w[e] = (j < r) ? fast_exp(s_cum[r] - s_cum[j]) * s_d[j] : 0.0f;
+      s_w[e] = (j < r) ? decay_f32<VAR>(fast_exp(s_cum[r] - s_cum[j])) * s_d[j] : 0.0f;
     }
     __syncthreads();
   };
@@ -413,7 +421,7 @@ void k_chunk_out_f32(ScanArgs a) {
   for (int k = 0; k < RT; ++k) {
     const int ri = 16 * Ik[k] + r16;
     cumk[k] = s_cum[min(ri, Lc - 1)];
-    const float sc = (vk[k] && ri < Lc) ? fast_exp(cumk[k]) : 0.0f;
+    const float sc = (vk[k] && ri < Lc) ? decay_f32<VAR>(fast_exp(cumk[k])) : 0.0f;
 #pragma unroll
     for (int pt = 0; pt < TP; ++pt)
 #pragma unroll
@@ -434,7 +442,7 @@ void k_chunk_out_f32(ScanArgs a) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) st[t] = ld4(sr + 64 * jb + 16 * min(t, I - 4 * jb));
     };
-    const float u_i = R > 0 ? fast_exp(cum_i - s_cum[64 * R]) : 0.0f;
+    const float u_i = R > 0 ? decay_f32<VAR>(fast_exp(cum_i - s_cum[64 * R])) : 0.0f;
     auto block = [&](int jb, const float4 (&st)[4]) {
       float xv[4][4][TP];   // [key tile][kk][pt]
       if (jb < R) {
@@ -481,10 +489,10 @@ void k_chunk_out_f32(ScanArgs a) {
         for (int t = 0; t < 4; ++t) {
           if (t < nt) {
             const int j0 = 64 * jb + 16 * t + 4 * q;
-            const float m0 = (j0 + 0 <= ri) ? st[t].x * fast_exp(cum_i - cj[t].x) * dj[t].x : 0.0f;
-            const float m1 = (j0 + 1 <= ri) ? st[t].y * fast_exp(cum_i - cj[t].y) * dj[t].y : 0.0f;
-            const float m2 = (j0 + 2 <= ri) ? st[t].z * fast_exp(cum_i - cj[t].z) * dj[t].z : 0.0f;
-            const float m3 = (j0 + 3 <= ri) ? st[t].w * fast_exp(cum_i - cj[t].w) * dj[t].w : 0.0f;
+            const float m0 = (j0 + 0 <= ri) ? st[t].x * decay_f32<VAR>(fast_exp(cum_i - cj[t].x)) * dj[t].x : 0.0f;
+            const float m1 = (j0 + 1 <= ri) ? st[t].y * decay_f32<VAR>(fast_exp(cum_i - cj[t].y)) * dj[t].y : 0.0f;
+            const float m2 = (j0 + 2 <= ri) ? st[t].z * decay_f32<VAR>(fast_exp(cum_i - cj[t].z)) * dj[t].z : 0.0f;
+            const float m3 = (j0 + 3 <= ri) ? st[t].w * decay_f32<VAR>(fast_exp(cum_i - cj[t].w)) * dj[t].w : 0.0f;
 #pragma unroll
             for (int pt = 0; pt < TP; ++pt) {
               acc[k][pt] = mma(xv[t][0][pt], m0, acc[k][pt]);
@@ -556,12 +564,22 @@ hipError_t launch_pn(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
   if (a.states_only) return rec(4);
   constexpr int PW = P < 32 ? P : 32;
   const int64_t units3 = a.Bt * a.Nc * a.H * (P / PW);
-  if (a.L <= 256)
-    hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 256>), dim3((unsigned)units3), dim3(kThreads),
+  if (a.variant != 0) {
+    // the decay-precision ablation: the 130M / 2.7B head shape at chunks up to 256 only
+    if constexpr (ablation_shape(P, N)) {
+      if (a.variant != 1 || a.L > 256) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 256, 1>), dim3((unsigned)units3),
+                         dim3(kThreads), 0, stream, a);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (a.L <= 256) {
+    hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 256, 0>), dim3((unsigned)units3), dim3(kThreads),
                        0, stream, a);
-  else
-    hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 512>), dim3((unsigned)units3), dim3(kThreads),
+  } else {
+    hipLaunchKernelGGL((k_chunk_out_f32<P, N, PW, 512, 0>), dim3((unsigned)units3), dim3(kThreads),
                        0, stream, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return rec(4);
 }

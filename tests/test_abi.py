@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert ssd.abi_version() == 4
+    assert ssd.abi_version() == 5
     for code in range(8):
         s = lib.ssd_status_string(code).decode()
         assert s.startswith(ssd.STATUS_NAMES[code])
@@ -112,7 +112,7 @@ def test_schedule_and_workspace(kw, chain):
     assert sched == (ssd.SSD_SCHEDULE_CHAIN if chain else ssd.SSD_SCHEDULE_PHASED)
     Bt, H, P, N, L, G = d.batch, d.nheads, d.headdim, d.dstate, d.chunk, d.ngroups
     nc = (d.seqlen + L - 1) // L
-    cb = _r256(4 * Bt * nc * G * L * L)
+    cb = _r256((2 if d.io_dtype == 1 else 4) * Bt * nc * G * L * L)   # bf16 scan: C B^T in bf16
     if chain:
         want = cb + _r256(2 * Bt * nc * G * N * L)
     else:
@@ -323,3 +323,30 @@ def test_binding_refuses_cpu_tensors():
     B = torch.zeros(1, 64, 1, 16)
     with pytest.raises(ValueError, match="device tensor"):
         ssd.ssd_chunk_scan(x, torch.zeros(1, 64, 4), torch.zeros(4), B, B, chunk=64)
+
+
+def ablation_status(d, variant, **kw):
+    a = fake_args(d, **kw)
+    return lib.ssd_chunk_scan_ablation(a[0], variant, *a[1:])
+
+
+@pytest.mark.parametrize("kw,variant,code", [
+    (dict(io_dtype=1, headdim=64, dstate=128, chunk=256), 7, INVALID),      # unknown variant
+    (dict(io_dtype=1, headdim=64, dstate=128, chunk=256), -1, INVALID),
+    (dict(io_dtype=1, headdim=32, dstate=128, chunk=256), 1, UNSUP),        # not the 64 x 128 head
+    (dict(io_dtype=1, headdim=64, dstate=64, chunk=256), 2, UNSUP),
+    (dict(io_dtype=1, headdim=64, dstate=128, chunk=512), 1, UNSUP),        # chunk > 256
+    (dict(io_dtype=0, headdim=64, dstate=128, chunk=256), 2, UNSUP),        # loaded mask: bf16 only
+    (dict(io_dtype=1, headdim=24, dstate=128, chunk=256), 1, UNSUP),        # the descriptor's own error
+])
+def test_ablation_rejects_before_launch(kw, variant, code):
+    assert ablation_status(desc(**kw), variant) == code
+
+
+def test_ablation_shares_the_scan_validation():
+    d = desc(io_dtype=1, headdim=64, dstate=128, chunk=256)
+    assert ablation_status(d, 1, x=0) == INVALID                  # NULL x
+    assert ablation_status(d, 2, x=BASE + 8) == ALIGN             # misaligned x
+    assert ablation_status(d, 1, ws_bytes=16) == WS               # workspace too small
+    # batch 0 writes nothing and is valid for every variant
+    assert ablation_status(desc(io_dtype=1, headdim=64, dstate=128, chunk=256, batch=0), 2) == OK
