@@ -48,7 +48,8 @@
  *  - The caller owns every buffer, including the workspace.  The library never
  *    allocates, frees or synchronises; calls are asynchronous on `stream`
  *    (0 = the null stream) and results are valid once the stream has reached
- *    them.  The library keeps no mutable global state.
+ *    them.  The library keeps no mutable global state other than the
+ *    per-device address of ssd_chunk_scan_noalloc's static scratch.
  *  - Errors: arguments are validated before anything is launched; on any error
  *    other than SSD_ERR_HIP nothing has been written.  SSD_ERR_HIP means a
  *    launch failed (hipGetLastError); outputs are then undefined.  No C++
@@ -263,6 +264,34 @@ ssd_status ssd_chunk_scan_ablation(const ssd_scan_desc* desc, int32_t variant, c
                                    const void* B, const void* C, const float* D,
                                    const float* initial_state, void* y, float* final_state,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssd_chunk_scan without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It calls no allocating routine: its
+ * workspace is a static device array of SSD_NOALLOC_MAX_WORKSPACE bytes
+ * that the library holds on every GPU it runs on, until the process ends.
+ *
+ * Arguments, layouts, results and errors as ssd_chunk_scan, less the
+ * workspace.  A problem whose ssd_chunk_scan_workspace_bytes exceeds
+ * SSD_NOALLOC_MAX_WORKSPACE returns SSD_ERR_WORKSPACE before anything is
+ * launched (96 MiB holds the 130M- and 2.7B-shaped 4096-token layers and
+ * the 8 x 16384-token batch of 64 heads; larger problems must use
+ * ssd_chunk_scan with a workspace of their own).  `stream`
+ * must belong to the current device (0: the current device's null stream),
+ * else SSD_ERR_INVALID_ARG.  The first call on a device looks up the array's
+ * address on that device (SSD_ERR_HIP if that fails).
+ *
+ * Every call on one GPU uses that GPU's one array, and nothing in it needs
+ * to start at zero: calls on one GPU that may overlap in time (on different
+ * streams, or from several host threads without ordering) race on it and
+ * give undefined results; calls ordered on one stream are safe.
+ */
+#define SSD_NOALLOC_MAX_WORKSPACE (96u << 20)
+ssd_status ssd_chunk_scan_noalloc(const ssd_scan_desc* desc, const void* x, const float* dt,
+                                  const float* dt_bias, const float* A, const void* B,
+                                  const void* C, const float* D, const float* initial_state,
+                                  void* y, float* final_state, hipStream_t stream);
 
 /*
  * One decode step of the recurrence, the state updated in place.

@@ -35,8 +35,9 @@ STATUS_NAMES = {0: "SSD_OK", 1: "SSD_ERR_INVALID_ARG", 2: "SSD_ERR_SHAPE", 3: "S
 SSD_VARIANT_DEFAULT = 0
 SSD_VARIANT_BF16_DECAY = 1
 SSD_VARIANT_LOADED_MASK = 2
+SSD_NOALLOC_MAX_WORKSPACE = 96 << 20
 EXPORTED = ("ssd_chunk_scan", "ssd_chunk_scan_timed", "ssd_chunk_scan_workspace_bytes",
-            "ssd_chunk_scan_schedule", "ssd_chunk_scan_ablation",
+            "ssd_chunk_scan_schedule", "ssd_chunk_scan_ablation", "ssd_chunk_scan_noalloc",
             "ssd_step", "ssd_conv1d", "ssd_conv1d_step",
             "ssd_chunk_scan_backward", "ssd_chunk_scan_backward_workspace_bytes",
             "ssd_status_string", "ssd_abi_version")
@@ -87,6 +88,8 @@ def _load() -> ctypes.CDLL:
                                        + [ctypes.POINTER(vp), ctypes.c_int])
     L.ssd_chunk_scan_ablation.restype = i32
     L.ssd_chunk_scan_ablation.argtypes = ([ctypes.POINTER(ScanDesc), i32] + [vp] * 11 + [sz, vp])
+    L.ssd_chunk_scan_noalloc.restype = i32
+    L.ssd_chunk_scan_noalloc.argtypes = [ctypes.POINTER(ScanDesc)] + [vp] * 10 + [vp]
     L.ssd_chunk_scan_workspace_bytes.restype = sz
     L.ssd_chunk_scan_workspace_bytes.argtypes = [ctypes.POINTER(ScanDesc)]
     L.ssd_chunk_scan_schedule.restype = i32
@@ -251,6 +254,40 @@ def ssd_chunk_scan(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
         st = lib.ssd_chunk_scan_timed(*args, evs, len(phase_events))
     if st != SSD_OK:
         raise SSDError(st, "ssd_chunk_scan")
+    return y, final_state
+
+
+def ssd_chunk_scan_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                           C: torch.Tensor, D: Optional[torch.Tensor] = None, *, chunk: int = 256,
+                           dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True,
+                           dt_limit: Sequence[float] = (1e-4, 0.5),
+                           initial_state: Optional[torch.Tensor] = None,
+                           y: Optional[torch.Tensor] = None,
+                           final_state: Optional[torch.Tensor] = None
+                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """ssd_chunk_scan through the allocation-free entry point: the library
+    uses its static per-device scratch (at most SSD_NOALLOC_MAX_WORKSPACE
+    bytes) instead of a workspace.  Pass y (and final_state, or None for no
+    final state) to make the call allocate nothing here either."""
+    _scan_shapes(x, dt, A, B, C, D, dt_bias, initial_state)
+    Bt, T, H, P = x.shape
+    N = B.shape[3]
+    _shape(y, "y", (Bt, T, H, P))
+    _shape(final_state, "final_state", (Bt, H, P, N))
+    for t, n, dt_ in ((x, "x", None), (B, "B", x.dtype), (C, "C", x.dtype), (dt, "dt", torch.float32),
+                      (A, "A", torch.float32), (D, "D", torch.float32),
+                      (dt_bias, "dt_bias", torch.float32),
+                      (initial_state, "initial_state", torch.float32), (y, "y", x.dtype),
+                      (final_state, "final_state", torch.float32)):
+        _check(t, n, dt_)
+    desc = scan_desc(x, B, chunk, dt_softplus, dt_limit)
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib.ssd_chunk_scan_noalloc(ctypes.byref(desc), _ptr(x), _ptr(dt), _ptr(dt_bias), _ptr(A),
+                                    _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state), _ptr(y),
+                                    _ptr(final_state), _stream(x.device))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_chunk_scan_noalloc")
     return y, final_state
 
 

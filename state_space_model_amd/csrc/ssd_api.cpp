@@ -3,12 +3,16 @@
 //
 // Everything here runs on the host.  Validation is complete before the first
 // launch, so an invalid call writes nothing.  No allocation, no
-// synchronisation, no global mutable state.
+// synchronisation.  The only global state is the per-device address of the
+// static scratch that ssd_chunk_scan_noalloc uses, set once per device.
 #include "ssd.h"
 
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "ssd_launch.h"
 
@@ -351,6 +355,49 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Scratch of ssd_chunk_scan_noalloc: a file-scope device array, one copy per
+// GPU (allocated when the library's code object is loaded on it, held until
+// the process ends).  Host code never passes `scratch` itself to a kernel (in
+// host code the name is only a stand-in for the symbol): its address on a
+// device comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept below.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)SSD_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on the device `stream` runs on, which must be the
+// current device (the symbol's address is taken with its device current).
+ssd_status scratch_of_stream(hipStream_t stream, void** out) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SSD_ERR_HIP;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return SSD_ERR_HIP;
+    if ((int)sd != cur) return SSD_ERR_INVALID_ARG;
+  }
+  if (cur < 0 || cur >= kMaxDevices) return SSD_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[cur].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[cur].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+      g_scratch_ptr[cur].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SSD_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t ssd_chunk_scan_workspace_bytes(const ssd_scan_desc* desc) {
@@ -392,6 +439,23 @@ ssd_status ssd_chunk_scan_ablation(const ssd_scan_desc* desc, int32_t variant, c
                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return scan_impl(desc, x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, workspace,
                    workspace_bytes, stream, nullptr, 0, false, false, false, variant);
+}
+
+ssd_status ssd_chunk_scan_noalloc(const ssd_scan_desc* desc, const void* x, const float* dt,
+                                  const float* dt_bias, const float* A, const void* B,
+                                  const void* C, const float* D, const float* initial_state,
+                                  void* y, float* final_state, hipStream_t stream) {
+  ScanSizes s;
+  const ssd_status st = check_scan_desc(desc, &s);
+  if (st != SSD_OK) return st;
+  if (s.ws_total > kScratchBytes) return SSD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (desc->batch > 0 && desc->seqlen > 0) {
+    const ssd_status sst = scratch_of_stream(stream, &ws);
+    if (sst != SSD_OK) return sst;
+  }
+  return scan_impl(desc, x, dt, dt_bias, A, B, C, D, initial_state, y, final_state, ws,
+                   kScratchBytes, stream, nullptr, 0);
 }
 
 ssd_status ssd_step(const ssd_step_desc* d, float* state, const void* x_t, const float* dt_t,

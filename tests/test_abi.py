@@ -350,3 +350,30 @@ def test_ablation_shares_the_scan_validation():
     assert ablation_status(d, 1, ws_bytes=16) == WS               # workspace too small
     # batch 0 writes nothing and is valid for every variant
     assert ablation_status(desc(io_dtype=1, headdim=64, dstate=128, chunk=256, batch=0), 2) == OK
+
+
+def noalloc_status(d, **over):
+    a = fake_args(d, **over)
+    # the same arguments without the workspace pointer and size
+    return lib.ssd_chunk_scan_noalloc(*a[:11], a[13])
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """Sizes beyond the static scratch are refused on the host, before the
+    scratch's address is looked up or anything is launched."""
+    big = desc(io_dtype=1, batch=16, seqlen=16384, nheads=64, headdim=64, dstate=128, chunk=256)
+    need = lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(big))
+    assert need > ssd.SSD_NOALLOC_MAX_WORKSPACE
+    assert noalloc_status(big) == WS
+    # the 2.7B-shaped 4096-token layer and the 8 x 16384 batched prefill fit
+    for fits in (desc(io_dtype=1, batch=1, seqlen=4096, nheads=80, headdim=64, dstate=128,
+                      chunk=256),
+                 desc(io_dtype=1, batch=8, seqlen=16384, nheads=64, headdim=64, dstate=128,
+                      chunk=256)):
+        assert lib.ssd_chunk_scan_workspace_bytes(ctypes.byref(fits)) <= ssd.SSD_NOALLOC_MAX_WORKSPACE
+    # descriptor errors come first
+    assert noalloc_status(desc(headdim=24)) == UNSUP
+    assert noalloc_status(desc(io_dtype=3)) == DTYPE
+    assert lib.ssd_chunk_scan_noalloc(None, *fake_args(desc())[1:11], None) == INVALID
+    # batch 0: nothing to do, no scratch needed
+    assert noalloc_status(desc(batch=0)) == OK
