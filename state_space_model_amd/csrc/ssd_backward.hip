@@ -899,7 +899,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
     const float da = (inc_d - dv) + (tot_u - (inc_u - uu)) + (inc_v - vv) + sc;
     const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
     const float z = a.dt[row] + bias;
-    const float pre = a.softplus ? (fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)))) : z;
+    const float pre = a.softplus ? softplus_of(z) : z;   // as in delta_of: the same clip decision
     float gate = (pre >= a.dt_min && pre <= a.dt_max) ? 1.0f : 0.0f;
     if (a.softplus) gate *= 1.0f / (1.0f + expf(-z));
     const float gd = __fmaf_rn(a.A[h], da, a.ddin[row]) * gate;

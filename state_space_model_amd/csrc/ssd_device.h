@@ -23,13 +23,29 @@ __device__ __forceinline__ float fast_exp(float x) {
   return __builtin_amdgcn_exp2f(x * kLog2e);
 }
 
+constexpr float kLn2 = 0.6931471805599453f;
+
+// softplus(z) = max(z, 0) + log1p(exp(-|z|)), which never overflows, on the
+// hardware base-2 exponential and logarithm.  log1p(e) for e = exp(-|z|) in
+// (0, 1] is formed as log(u) e / (u - 1) with u = 1 + e rounded to float32
+// (Goldberg, "What every computer scientist should know about floating-point
+// arithmetic", 1991, Theorem 4): the quotient e / (u - 1) cancels the rounding
+// of u, so the result keeps a few-ulp relative error for tiny e as well; when
+// u rounds to 1, log1p(e) = e to working precision.
+__device__ __forceinline__ float softplus_of(float z) {
+  const float e = __builtin_amdgcn_exp2f(-fabsf(z) * kLog2e);
+  const float u = 1.0f + e;
+  const float l = u == 1.0f ? e
+                            : __builtin_amdgcn_logf(u) * kLn2 * e * __builtin_amdgcn_rcpf(u - 1.0f);
+  return fmaxf(z, 0.0f) + l;
+}
+
 // Delta = clip(softplus(dt + dt_bias), lo, hi)  ("Compiler-First State Space
 // Duality ...", Implementation: einsum shaping names softplus and clip).
-// softplus(z) = max(z, 0) + log1p(exp(-|z|)), which never overflows.  The
-// device library's accurate expf/log1pf are used: this runs once per
-// (token, head), not per state element.
+// Every kernel forms Delta through this one function, so all of them see the
+// same bits for a token.
 __device__ __forceinline__ float delta_of(float z, int softplus, float lo, float hi) {
-  float d = softplus ? (fmaxf(z, 0.0f) + log1pf(expf(-fabsf(z)))) : z;
+  float d = softplus ? softplus_of(z) : z;
   return fminf(fmaxf(d, lo), hi);
 }
 
@@ -84,6 +100,16 @@ __device__ __forceinline__ typename Mfma<T>::frag load_frag(const T* p) {
 // Wavefront helpers
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// The thread index through an opaque copy.  Inside a kernel's long loop the
+// indices and addresses derived from it are then formed where they are used
+// instead of being hoisted out of the loop and held in (or spilled from)
+// registers across it.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele,
 // log2(64) = 6 shuffle steps; a fixed order, so the result is reproducible).

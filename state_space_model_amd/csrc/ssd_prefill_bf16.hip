@@ -178,8 +178,10 @@ __device__ __forceinline__ void cb_block_bf16(const ScanArgs& a, int ntiles, int
 
 // x of one chunk, in blocks of 8 token rows x CW head columns (CW = 8, or 4
 // when the workgroup has threads enough for the smaller blocks): block id ->
-// token block id / (P/CW), column block id % (P/CW).  Rows past the chunk's
-// end are zeros.  NXB blocks per thread cover LMAX rows.
+// token block id / (P/CW), column block id % (P/CW).  NXB blocks per thread
+// cover LMAX rows.  Rows past the chunk's end read its last row and are
+// zeroed when stored: a select on loaded data right after the loads would
+// make the compiler wait for them there.
 template <int P, int LMAX, int NTH = kThreads>
 struct XStage {
   static constexpr int CW = (LMAX / 8) * (P / 8) >= NTH ? 8 : 4;
@@ -187,46 +189,40 @@ struct XStage {
   static constexpr int NXB = (NBLK + NTH - 1) / NTH;
   typedef __bf16 vrow __attribute__((ext_vector_type(CW)));
   vrow v[NXB][8];
+  int Lc = 0;
 
   __device__ __forceinline__ void load(const ScanArgs& a, int64_t b, int64_t c, int64_t h) {
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
     const int64_t t0 = c * a.L;
-    const int Lc = chunk_len(a, c);
+    Lc = chunk_len(a, c);
     const bf16* xg = reinterpret_cast<const bf16*>(a.x) + ((b * a.T + t0) * a.H + h) * P;
-    const int64_t xs = a.H * P;
+    const int xs = (int)(a.H * P);
 #pragma unroll
     for (int i = 0; i < NXB; ++i) {
       const int id = min(tid + i * NTH, NBLK - 1);
       const int lb = id / (P / CW), cb = id % (P / CW);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int l = 8 * lb + r;
-        const bf16* src = xg + min(l, Lc - 1) * xs + CW * cb;
-        if constexpr (CW == 8) {
-          v[i][r] = ld8_masked(src, l < Lc);
-        } else {
-          uint2 u = *reinterpret_cast<const uint2*>(src);
-          u.x = l < Lc ? u.x : 0u;
-          u.y = l < Lc ? u.y : 0u;
-          v[i][r] = __builtin_bit_cast(vrow, u);
-        }
-      }
+      for (int r = 0; r < 8; ++r)
+        v[i][r] = *reinterpret_cast<const vrow*>(xg + min(8 * lb + r, Lc - 1) * xs + CW * cb);
     }
   }
-  // x^T[p][l] into s_xt (row stride XTS)
+  // x^T[p][l] into s_xt (row stride XTS), zero past the chunk
   __device__ __forceinline__ void store(bf16* s_xt) {
     constexpr int XTS = LMAX + 8;
-    const int tid = threadIdx.x;
+    const int tid = opaque_tid();
 #pragma unroll
     for (int i = 0; i < NXB; ++i) {
       const int id = tid + i * NTH;
       if (id < NBLK) {
         const int lb = id / (P / CW), cb = id % (P / CW);
+        bool in[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) in[r] = 8 * lb + r < Lc;
 #pragma unroll
         for (int cc = 0; cc < CW; ++cc) {
           bf16x8 col;
 #pragma unroll
-          for (int r = 0; r < 8; ++r) col[r] = v[i][r][cc];
+          for (int r = 0; r < 8; ++r) col[r] = in[r] ? v[i][r][cc] : (bf16)0.0f;
           st8(s_xt + (CW * cb + cc) * XTS + 8 * lb, col);
         }
       }
@@ -273,17 +269,34 @@ __device__ const TrilBits kTrilBits = make_tril_bits();
 // only the rows of the chunk's tiles are written.
 constexpr int tile_table_size(int LMAX) { return 8 * (LMAX / 16) * (LMAX / 16 - 1); }
 
-template <int VAR, int NTH>
+template <int VAR, int NTH, int LMAX>
 __device__ __forceinline__ void tile_decay_table(int Lc, const float* s_d, const float* s_cum,
                                                  float* s_w) {
+  constexpr int NT = LMAX / 16, NW = NTH / 64;
   const int nrt = (Lc + 15) / 16;
-  const int n = 8 * nrt * (nrt - 1);
-  for (int e = threadIdx.x; e < n; e += NTH) {
-    int I = (int)(0.5f + sqrtf(0.25f + 0.125f * (float)e));   // row: 8 I (I-1) <= e
-    if (8 * I * (I - 1) > e) --I;
-    else if (8 * I * (I + 1) <= e) ++I;
-    const int j = e - 8 * I * (I - 1);
-    s_w[e] = __fmul_rn(decay_factor<VAR>(fast_exp(__fsub_rn(s_cum[16 * I], s_cum[j]))), s_d[j]);
+  auto entry = [&](int I, int j) {
+    s_w[8 * I * (I - 1) + j] =
+        __fmul_rn(decay_factor<VAR>(fast_exp(__fsub_rn(s_cum[16 * I], s_cum[j]))), s_d[j]);
+  };
+  if constexpr (NW == NT / 2) {
+    // wavefront w > 0 fills rows w and NT - w (16 NT entries together),
+    // wavefront 0 row NT/2: every wavefront the same 16 NT / 64 sweeps
+    const int tid = opaque_tid();
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int I1 = w > 0 ? w : NT / 2, I2 = w > 0 ? NT - w : 0;
+    const int n1 = I1 < nrt ? 16 * I1 : 0, n2 = I2 > 0 && I2 < nrt ? 16 * I2 : 0;
+    for (int e = lane; e < n1 + n2; e += 64) {
+      if (e < n1) entry(I1, e);
+      else entry(I2, e - n1);
+    }
+  } else {
+    const int n = 8 * nrt * (nrt - 1);
+    for (int e = opaque_tid(); e < n; e += NTH) {
+      int I = (int)(0.5f + sqrtf(0.25f + 0.125f * (float)e));   // row: 8 I (I-1) <= e
+      if (8 * I * (I - 1) > e) --I;
+      else if (8 * I * (I + 1) <= e) ++I;
+      entry(I, e - 8 * I * (I - 1));
+    }
   }
 }
 
@@ -292,7 +305,7 @@ template <int LMAX, int NTH = kThreads>
 __device__ __forceinline__ void state_weights(int Lc, const float* s_d, const float* s_cum,
                                               float* s_ws) {
   const float cum_last = s_cum[Lc - 1];
-  for (int l = threadIdx.x; l < LMAX; l += NTH)
+  for (int l = opaque_tid(); l < LMAX; l += NTH)
     s_ws[l] = (l < Lc) ? __fmul_rn(s_d[l], fast_exp(__fsub_rn(cum_last, s_cum[l]))) : 0.0f;
 }
 
@@ -316,7 +329,10 @@ __device__ __forceinline__ int col_tile_of(int wave, int k) {
 //   acc += sum_{j < r} x^T[p][j] bf16(S[i][j] W_I[j])               earlier key tiles
 //   acc *= exp(cum_i - cum_r)
 //   acc += sum_{r <= j <= i} x^T[p][j] bf16(S[i][j] exp(cum_i - cum_j) Delta_j)
-//   y[i][p] = bf16(acc + D x[i][p])
+//   acc += sum_k x^T[p][16I + k] E_m[k][i - 16I],  m = 1..3  (the skip term D x:
+//          E_m = d_m I with D = d_1 + d_2 + d_3 split exactly into three
+//          bfloat16 parts, so each product is exact in float32)
+//   y[i][p] = bf16(acc)
 // so an earlier key costs one multiply (the exponentials are in the table)
 // and only the 16 x 16 diagonal tile takes exponentials and the causal
 // select (made before the exponential's result is used).  Earlier keys go 32
@@ -327,10 +343,12 @@ __device__ __forceinline__ int col_tile_of(int wave, int k) {
 //   s_xt  bf16 x^T[p][j]     (row stride LMAX + 8), zero past the chunk
 //   s_d, s_cum, s_w: Delta, cum and the per-tile decay tables of the chunk
 // S (C B^T, bfloat16) and C come from global memory (L2: shared by all heads
-// of a group).  Every S row a wavefront needs is requested at once by
-// prefetch() (one round trip instead of one per key step), together with the
-// first tile's C: tile 0's 32-key steps fill sf from the front, tile 1's from
-// the back (their counts add up to NS), so every register index is static.
+// of a group).  The S rows of every 32-key step a wavefront needs are
+// requested at once by prefetch() (one round trip instead of one per key
+// step), together with the first tile's C: tile 0's steps fill sf from the
+// front, tile 1's from the back (their counts add up to NS), so every
+// register index is static.  The two 16-key blocks of a tile (before and on
+// the diagonal) are requested at the tile's start.
 // C_AHEAD: the second tile's C is loaded behind the first tile's intra term
 // (else at the second tile's start, 16 registers fewer).
 template <int P, int N, int LMAX, int NW, int VAR = kDecayF32, bool C_AHEAD = true>
@@ -349,7 +367,6 @@ struct ChunkOut {
   int Lc;
   bf16x8 cf[N / 32];              // C[i][32 nb + 8q ..] of the tile about to run
   bf16x8 sf[NS > 0 ? NS : 1];     // S[i][32 ks + 8q ..] of the 32-key steps
-  bf16x4 sod[CT], sdg[CT];        // S of the 16-key step before the diagonal, and of the diagonal
 
   __device__ __forceinline__ ChunkOut(const ScanArgs& a_, int64_t b_, int64_t c_, int64_t h_,
                                       int64_t g_, int Lc_)
@@ -395,8 +412,6 @@ struct ChunkOut {
       const int Ic = v ? I : n_rt - 1;
       row[k] = S + (int64_t)(16 * Ic + r16) * a.L;
       nf[k] = v ? I >> 1 : 0;
-      sod[k] = ld4b(row[k] + 16 * (Ic - (Ic & 1)) + 4 * q);
-      sdg[k] = ld4b(row[k] + 16 * Ic + 4 * q);
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
@@ -417,14 +432,37 @@ struct ChunkOut {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
     const int wave = wave_id(), n_rt = nrt();
     const int64_t t0 = c * a.L;
-    const float Dh = a.D ? a.D[h] : 0.0f;
     bf16* yg = reinterpret_cast<bf16*>(a.y);
+    // skip-term operands: D = d1 + d2 + d3 exactly (bfloat16 parts of the
+    // float32 value and of its remainders), on the diagonal of a 16 x 16 block
+    bf16x4 e1, e2, e3;
+    {
+      const float Dh = a.D ? a.D[h] : 0.0f;
+      const bf16 d1 = (bf16)Dh;
+      const float r1 = __fsub_rn(Dh, (float)d1);
+      const bf16 d2 = (bf16)r1;
+      const bf16 d3 = (bf16)__fsub_rn(r1, (float)d2);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool on = 4 * q + e == r16;
+        e1[e] = on ? d1 : (bf16)0.0f;
+        e2[e] = on ? d2 : (bf16)0.0f;
+        e3[e] = on ? d3 : (bf16)0.0f;
+      }
+    }
 
 #pragma unroll
     for (int k = 0; k < CT; ++k) {
       const int I = col_tile_of<NW>(wave, k);
       if (I >= n_rt) break;                 // later tiles lie further on
       if (!C_AHEAD && k > 0) load_c(I);
+      const int ri = 16 * I + r16;
+      // the 16-key block before the diagonal (re-reading the diagonal one when
+      // I is even) and the diagonal block: consumed after the 32-key steps
+      const bf16* srow = reinterpret_cast<const bf16*>(a.ws_cb) +
+                         ((b * a.Nc + c) * a.G + g) * a.L * a.L + (int64_t)ri * a.L;
+      const bf16x4 sod = ld4b(srow + 16 * (I - (I & 1)) + 4 * q);
+      const bf16x4 sdg = ld4b(srow + 16 * I + 4 * q);
       f32x4 acc[TP];
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -450,7 +488,6 @@ struct ChunkOut {
       }
 
       // ---- earlier key tiles: 32-key steps, then the odd 16-key one ----
-      const int ri = 16 * I + r16;
       const float* wI = s_w + 8 * I * (I - 1);
       const int nfull = I >> 1;
 #pragma unroll
@@ -476,7 +513,7 @@ struct ChunkOut {
       if (I & 1) {   // the key tile just before the diagonal one
         const int k0 = 16 * (I - 1) + 4 * q;
         const float4 w = ld4(wI + k0);
-        const bf16x4 st = sod[k];
+        const bf16x4 st = sod;
         bf16x4 m;
         m[0] = (bf16)__fmul_rn((float)st[0], w.x);
         m[1] = (bf16)__fmul_rn((float)st[1], w.y);
@@ -499,7 +536,7 @@ struct ChunkOut {
       {
         const int j0 = 16 * I + 4 * q;
         const float4 cj = ld4(s_cum + j0), dj = ld4(s_d + j0);
-        const bf16x4 st = sdg[k];
+        const bf16x4 st = sdg;
         bool mk[4];
         if constexpr (VAR == kMaskLoaded) {
           const uint32_t bits = kTrilBits.w[ri * (kMaxL / 32) + (j0 >> 5)] >> (j0 & 31);
@@ -519,21 +556,25 @@ struct ChunkOut {
         m[2] = dec(mk[2], (float)st[2], cj.z, dj.z);
         m[3] = dec(mk[3], (float)st[3], cj.w, dj.w);
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt)
-          acc[pt] = mma16(ld4b(s_xt + (16 * pt + r16) * XTS + j0), m, acc[pt]);
+        for (int pt = 0; pt < TP; ++pt) {
+          const bf16x4 xd = ld4b(s_xt + (16 * pt + r16) * XTS + j0);
+          acc[pt] = mma16(xd, m, acc[pt]);
+          // the skip term D x of the tile's own tokens, on the same x^T fragment
+          acc[pt] = mma16(xd, e1, acc[pt]);
+          acc[pt] = mma16(xd, e2, acc[pt]);
+          acc[pt] = mma16(xd, e3, acc[pt]);
+        }
       }
 
-      // ---- skip term and store: lane holds y[i][p..p+3], p = 16 pt + 4q ----
+      // ---- store: lane holds y[i][p..p+3], p = 16 pt + 4q ----
       if (ri < Lc) {
         const int64_t rowy = ((b * a.T + t0 + ri) * a.H + h) * P;
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
-          const int p0 = 16 * pt + 4 * q;
           bf16x4 o;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            o[r] = (bf16)__fmaf_rn(Dh, (float)s_xt[(p0 + r) * XTS + ri], acc[pt][r]);
-          st4b(yg + rowy + p0, o);
+          for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[pt][r];
+          st4b(yg + rowy + 16 * pt + 4 * q, o);
         }
       }
     }
@@ -771,7 +812,7 @@ void k_chunk_out_bf16(ScanArgs a) {
   ChunkOut<P, N, LMAX, NW, VAR> out(a, b, c, h, g, Lc);
   out.prefetch();
   chunk_delta_cumsum_wide(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
-  tile_decay_table<VAR, NTH>(Lc, s_d, s_cum, s_w);
+  tile_decay_table<VAR, NTH, LMAX>(Lc, s_d, s_cum, s_w);
   xs.store(s_xt);
 #pragma unroll
   for (int i = 0; i < NHV; ++i) {
@@ -829,8 +870,9 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int nti
 //   state:   S_c = sum_ks (B^T w)_bf16 x into a fresh accumulator, then
 //            h_c = fma(alpha_c, h_{c-1}, S_c)
 // Load order (memory counters retire loads in order, so a wait for a load
-// also waits for every older one): the state step's B^T fragments first,
-// then the next chunk's x and dt (consumed after the next barrier); the next
+// also waits for every older one): the next chunk's dt before the outputs;
+// the state step's B^T fragments, then the next chunk's x (consumed after
+// the next barrier); the next
 // chunk's first output-pass operands right after that barrier, so they fly
 // during the staging.
 template <int P, int N, int LMAX, int VAR>
@@ -904,10 +946,14 @@ void k_chain_bf16(ScanArgs a) {
     out.c = c;
     out.Lc = Lc;
     out.prefetch();
-    tile_decay_table<VAR, NTH>(Lc, s_d, s_cum, s_w);
+    tile_decay_table<VAR, NTH, LMAX>(Lc, s_d, s_cum, s_w);
     state_weights<LMAX, NTH>(Lc, s_d, s_cum, s_ws);
     const float alpha = fast_exp(s_cum[Lc - 1]);
     __syncthreads();
+
+    // the next chunk's dt (the last chunk re-reads itself), ahead of the
+    // state step's loads so that the next staging does not wait behind them
+    if (scan_thread) dtv = chunk_dt_load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
 
     // ---- outputs of chunk c ----
     out.run(s_d, s_cum, s_w, s_xt, s_h);
@@ -916,7 +962,8 @@ void k_chain_bf16(ScanArgs a) {
     // 32-token steps: the wavefront's B^T fragment (n-tile nt), scaled by the
     // state weights, against its p-tiles' x^T fragments.  All the chunk's
     // fragments are requested at once (steps past the chunk re-read its
-    // last), then the next chunk's x and dt.
+    // last), then the next chunk's x (its dt was requested before the
+    // outputs).
     {
       const int nks = (Lc + 31) / 32;
       const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
@@ -928,9 +975,7 @@ void k_chain_bf16(ScanArgs a) {
       for (int ks = 0; ks < NKS; ++ks) bt[ks] = ld8(btc + 32 * min(ks, nks - 1));
       {
         // the last chunk re-reads itself: the same loads on every path
-        const int64_t cn = c + 1 < a.Nc ? c + 1 : c;
-        xs.load(a, b, cn, h);
-        if (scan_thread) dtv = chunk_dt_load(a, b, cn, h);
+        xs.load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
       }
       f32x4 t[TPW];
 #pragma unroll

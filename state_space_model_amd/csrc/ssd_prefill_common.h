@@ -30,7 +30,7 @@ struct DeltaScan {
 // Raw dt of this thread's two tokens (0 past the chunk or past T).
 __device__ __forceinline__ float2 chunk_dt_load(const ScanArgs& a, int64_t b, int64_t c,
                                                 int64_t h) {
-  const int l0 = 2 * (int)threadIdx.x, l1 = l0 + 1;
+  const int l0 = 2 * opaque_tid(), l1 = l0 + 1;
   const int64_t t0 = c * a.L;
   const int last = (int)min<int64_t>(a.L, a.T - t0) - 1;   // last token of the chunk
   // unconditional loads of clamped rows, then a select: no branch per load
@@ -43,7 +43,7 @@ __device__ __forceinline__ float2 chunk_dt_load(const ScanArgs& a, int64_t b, in
 // wavefront's total in s_wsum[wave].  No barrier inside.
 __device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_t c, int64_t h,
                                                        float2 dtv, float* s_wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int l0 = 2 * tid, l1 = l0 + 1;
   const int64_t t0 = c * a.L;
   const float Ah = a.A[h];
@@ -65,7 +65,7 @@ __device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_
 // writes s_d and s_cum for this thread's tokens.  No barrier inside.
 __device__ __forceinline__ void chunk_scan_stage2(const ScanArgs& a, const DeltaScan& s,
                                                   const float* s_wsum, float* s_d, float* s_cum) {
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = opaque_tid(), wave = tid >> 6;
   const int l0 = 2 * tid, l1 = l0 + 1;
   float off = 0.0f;
   for (int w = 0; w < wave; ++w) off = __fadd_rn(off, s_wsum[w]);
