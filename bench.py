@@ -77,33 +77,50 @@ def prefill_flops_per_token(w):
     return H * ((L + 1) * P + 4 * N * P + 2 * P * N / L) + G * (L + 1) * N
 
 
+def uses_prepass(w, chain):
+    """The bfloat16 scan at the chain kernel's head shapes (P in {32, 64}, N in
+    {64, 128}, L <= 256) starts with the C B^T / B^T pre-pass on both schedules."""
+    return chain or (w.io_dtype == "bf16" and w.headdim in (32, 64) and w.dstate in (64, 128)
+                     and w.chunk <= 256)
+
+
 def phase_flops_per_token(w, chain):
     """Algorithmic FLOP/token of each kernel of the scan, by schedule.
-    phased: C B^T rides in the chunk-state launch; chain: a C B^T / B^T
-    pre-pass, then one kernel doing the chunk states, the inter-chunk
-    recurrence and the outputs (a5-a8)."""
+    chain: a C B^T / B^T pre-pass, then one kernel doing the chunk states,
+    the inter-chunk recurrence and the outputs (a5-a8).  phased: chunk
+    states (with C B^T in the same launch, or after the pre-pass), the state
+    pass, the outputs."""
     H, P, N, G, L = w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    cb = G * (L + 1) * N
     if chain:
-        return {"cb_bt_prepass": G * (L + 1) * N,
-                "chain": H * ((L + 1) * P + 4 * N * P + 2 * P * N / L)}
-    return {
-        "chunk_state": H * 2 * N * P + G * (L + 1) * N,                 # chunk states + C B^T
-        "state_pass": H * 2 * P * N / L,                                # inter-chunk recurrence
-        "chunk_out": H * ((L + 1) * P + 2 * N * P),                     # decay, products
-    }
+        return {"cb_bt_prepass": cb, "chain": H * ((L + 1) * P + 4 * N * P + 2 * P * N / L)}
+    per = {"chunk_state": H * 2 * N * P,
+           "state_pass": H * 2 * P * N / L,                                # inter-chunk recurrence
+           "chunk_out": H * ((L + 1) * P + 2 * N * P)}                     # decay, products
+    if uses_prepass(w, chain):
+        per["cb_bt_prepass"] = cb
+    else:
+        per["chunk_state"] += cb
+    return per
 
 
 # kernel (phase) names of each schedule, and the event interval that times
 # each: the timed call records an event before each of its 4 phases and one
 # after the last; an empty phase's two events add only event overhead, so
 # empty phases are not reported.
-PHASES = {
-    False: {"chunk_state": (1, 2), "state_pass": (2, 3), "chunk_out": (3, 4)},
-    True: {"cb_bt_prepass": (0, 1), "chain": (3, 4)},
-}
-KERNEL_NAMES = {"chunk_state": "k_cb_and_chunk_state", "state_pass": "k_state_pass",
-                "chunk_out": "k_chunk_out", "cb_bt_prepass": "k_cb_and_bt_bf16",
-                "chain": "k_chain_bf16"}
+def phase_plan(w, chain):
+    if chain:
+        return {"cb_bt_prepass": (0, 1), "chain": (3, 4)}
+    plan = {"chunk_state": (1, 2), "state_pass": (2, 3), "chunk_out": (3, 4)}
+    if uses_prepass(w, chain):
+        plan = {"cb_bt_prepass": (0, 1), **plan}
+    return plan
+
+
+def kernel_names(w, chain):
+    return {"chunk_state": "k_chunk_state_bf16" if uses_prepass(w, chain) else "k_cb_and_chunk_state",
+            "state_pass": "k_state_pass", "chunk_out": "k_chunk_out",
+            "cb_bt_prepass": "k_cb_and_bt_bf16", "chain": "k_chain_bf16"}
 
 
 def prefill_bytes_per_token(w, T):
@@ -220,7 +237,7 @@ def bench_prefill(ssd, torch, w, steps, warmup):
         run(i, evs[i])
     torch.cuda.synchronize()
     phase_ms = {n: sum(evs[i][a].elapsed_time(evs[i][b]) for i in range(steps)) / steps
-                for n, (a, b) in PHASES[chain].items()}
+                for n, (a, b) in phase_plan(w, chain).items()}
     return {"ms": ms, "wall_ms": wall * 1e3 / steps, "phase_ms": phase_ms, "nsets": nsets,
             "set_bytes": set_bytes, "tokens": Bt * T, "rep_ms": rep_ms, "chain": chain}
 
@@ -240,7 +257,7 @@ def prefill_report(w, pf, headline=False):
     key = f"{dom}/{w.io_dtype}"
     whole_tflops = fpt * pf["tokens"] / (pf["ms"] * 1e-3) / 1e12
     bpt = prefill_bytes_per_token(w, w.seqlen)
-    roof = {"bound": "mfma", "kernel": KERNEL_NAMES[dom], "achieved": achieved, "peak": peak,
+    roof = {"bound": "mfma", "kernel": kernel_names(w, pf["chain"])[dom], "achieved": achieved, "peak": peak,
             "unit": "TFLOP/s", "frac": achieved / peak,
             "traffic": traffic_for(key, w.name) if key in KERNEL_SOURCES else None,
             "flops_per_launch": dom_flops, "avg_launch_ms": dom_ms}

@@ -105,7 +105,9 @@ ssd_status check_scan_desc(const ssd_scan_desc* d, ScanSizes* s, bool force_phas
     return SSD_ERR_UNSUPPORTED;
   s->cb_bf16 = d->io_dtype == SSD_BF16 && !cb_f32;
   s->ws_cb_bytes = round_up((size_t)cb_elems * (s->cb_bf16 ? 2 : 4), kAlign);
-  s->ws_bt_bytes = s->chain ? round_up((size_t)bt_elems * 2, kAlign) : 0;
+  const bool use_bt = s->chain || (d->io_dtype == SSD_BF16 &&
+                                ssd::phased_prepass(d->headdim, d->dstate, d->chunk));
+  s->ws_bt_bytes = use_bt ? round_up((size_t)bt_elems * 2, kAlign) : 0;
   // the bfloat16 phased schedule hands the entering states to its output kernel in bf16
   s->ws_hb_bytes = (!s->chain && d->io_dtype == SSD_BF16) ? round_up((size_t)ws_elems * 2, kAlign) : 0;
   s->ws_total = s->ws_state_bytes + s->ws_alpha_bytes + s->ws_cb_bytes + s->ws_bt_bytes +

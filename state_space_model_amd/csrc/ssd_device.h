@@ -113,14 +113,21 @@ __device__ __forceinline__ int opaque_tid() {
 
 // Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele,
 // log2(64) = 6 shuffle steps; a fixed order, so the result is reproducible).
-__device__ __forceinline__ float wave_inclusive_scan(float v) {
-  const int lane = lane_id();
+// `lane` is the caller's lane index; a caller in a loop passes an opaque copy
+// so that the six source-lane addresses are formed at each use rather than
+// held in registers across the loop.
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    float o = __shfl_up(v, off, 64);
+    // lanes below `off` read some lane and discard it
+    const float o = __int_as_float(__builtin_amdgcn_ds_bpermute((lane - off) << 2,
+                                                                __float_as_int(v)));
     if (lane >= off) v += o;
   }
   return v;
+}
+__device__ __forceinline__ float wave_inclusive_scan(float v) {
+  return wave_inclusive_scan(v, lane_id());
 }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).

@@ -134,6 +134,12 @@ constexpr bool ablation_shape(int64_t P, int64_t N) { return P == 64 && N == 128
 constexpr bool chain_variant(int64_t P, int64_t N) {
   return (P == 32 || P == 64) && (N == 64 || N == 128);
 }
+// The phased bfloat16 schedule of the chain shapes at chunks up to 256 also
+// starts with the C B^T / B^T pre-pass and forms its chunk states from B^T.
+constexpr bool phased_prepass(int64_t P, int64_t N, int64_t L) {
+  return chain_variant(P, N) && L <= 256;
+}
+
 // The chain schedule runs one workgroup per (batch, head) for the whole
 // sequence; it is chosen once batch x heads alone fill the GPU's 256 compute
 // units (two workgroups per unit at most).  Both schedules give bit-identical

@@ -185,11 +185,22 @@ __device__ __forceinline__ void cb_block_bf16(const ScanArgs& a, int ntiles, int
 template <int P, int LMAX, int NTH = kThreads>
 struct XStage {
   static constexpr int CW = (LMAX / 8) * (P / 8) >= NTH ? 8 : 4;
-  static constexpr int NBLK = (LMAX / 8) * (P / CW);
+  static constexpr int NCB = P / CW;
+  static constexpr int NBLK = (LMAX / 8) * NCB;
   static constexpr int NXB = (NBLK + NTH - 1) / NTH;
   typedef __bf16 vrow __attribute__((ext_vector_type(CW)));
   vrow v[NXB][8];
   int Lc = 0;
+
+  static_assert((LMAX / 8) % 8 == 0, "token blocks in groups of 8");
+  // block id -> (token block, column block): 8 consecutive ids take 8
+  // consecutive token blocks of one column block, so the 8 lanes the LDS
+  // serves together store x^T rows' 16-byte units side by side (all banks)
+  __device__ __forceinline__ static void block_of(int id, int& lb, int& cb) {
+    const int g8 = id >> 3;
+    cb = g8 % NCB;
+    lb = (g8 / NCB) * 8 + (id & 7);
+  }
 
   __device__ __forceinline__ void load(const ScanArgs& a, int64_t b, int64_t c, int64_t h) {
     const int tid = opaque_tid();
@@ -199,8 +210,8 @@ struct XStage {
     const int xs = (int)(a.H * P);
 #pragma unroll
     for (int i = 0; i < NXB; ++i) {
-      const int id = min(tid + i * NTH, NBLK - 1);
-      const int lb = id / (P / CW), cb = id % (P / CW);
+      int lb, cb;
+      block_of(min(tid + i * NTH, NBLK - 1), lb, cb);
 #pragma unroll
       for (int r = 0; r < 8; ++r)
         v[i][r] = *reinterpret_cast<const vrow*>(xg + min(8 * lb + r, Lc - 1) * xs + CW * cb);
@@ -214,7 +225,8 @@ struct XStage {
     for (int i = 0; i < NXB; ++i) {
       const int id = tid + i * NTH;
       if (id < NBLK) {
-        const int lb = id / (P / CW), cb = id % (P / CW);
+        int lb, cb;
+        block_of(id, lb, cb);
         bool in[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) in[r] = 8 * lb + r < Lc;
@@ -365,12 +377,13 @@ struct ChunkOut {
   const ScanArgs& a;
   int64_t b, c, h, g;
   int Lc;
+  float Dh;                       // D of head h (0 without D)
   bf16x8 cf[N / 32];              // C[i][32 nb + 8q ..] of the tile about to run
   bf16x8 sf[NS > 0 ? NS : 1];     // S[i][32 ks + 8q ..] of the 32-key steps
 
   __device__ __forceinline__ ChunkOut(const ScanArgs& a_, int64_t b_, int64_t c_, int64_t h_,
                                       int64_t g_, int Lc_)
-      : a(a_), b(b_), c(c_), h(h_), g(g_), Lc(Lc_) {}
+      : a(a_), b(b_), c(c_), h(h_), g(g_), Lc(Lc_), Dh(a_.D ? a_.D[h_] : 0.0f) {}
 
   // Lane index through an opaque copy: inside the chain kernel's chunk loop
   // the many lane-dependent addresses are then formed where they are used
@@ -437,7 +450,6 @@ struct ChunkOut {
     // float32 value and of its remainders), on the diagonal of a 16 x 16 block
     bf16x4 e1, e2, e3;
     {
-      const float Dh = a.D ? a.D[h] : 0.0f;
       const bf16 d1 = (bf16)Dh;
       const float r1 = __fsub_rn(Dh, (float)d1);
       const bf16 d2 = (bf16)r1;
@@ -860,6 +872,102 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int nti
   for (int cc = 0; cc < 8; ++cc) st8(dst + cc * a.L, tr[cc]);
 }
 
+// Chunk summary state of one wavefront's tiles, from zero, in 32-token
+// steps: t[ip][n = 16 nt + 4q + r][p = 16 (pt0 + ip) + lane%16] = sum over the
+// chunk of (B^T w)_bf16 x, with B^T w the wavefront's B^T fragment (n-tile
+// nt, from the pre-pass copy ws_bt) scaled by the state weights in LDS and
+// x^T from LDS.  state_bt_load requests every fragment of the chunk at once
+// (steps past the chunk re-read its last); state_tiles consumes them.  The
+// chain kernel and the phased chunk-state kernel share both, so they form
+// S_c with the same instructions in the same order.
+template <int N, int LMAX>
+__device__ __forceinline__ void state_bt_load(const ScanArgs& a, int64_t b, int64_t c, int64_t g,
+                                              int nt, int Lc, bf16x8 (&bt)[LMAX / 32]) {
+  const int nks = (Lc + 31) / 32;
+  const int lane = opaque_tid() & 63, q = lane >> 4, r16 = lane & 15;
+  const bf16* btc = reinterpret_cast<const bf16*>(a.ws_bt) +
+                    ((b * a.Nc + c) * a.G + g) * (int64_t)(N * a.L) +
+                    (int64_t)(16 * nt + r16) * a.L + 8 * q;
+#pragma unroll
+  for (int ks = 0; ks < LMAX / 32; ++ks) bt[ks] = ld8(btc + 32 * min(ks, nks - 1));
+}
+
+template <int LMAX, int TPW>
+__device__ __forceinline__ void state_tiles(const bf16x8 (&bt)[LMAX / 32], int pt0, int Lc,
+                                            const bf16* s_xt, const float* s_ws,
+                                            f32x4 (&t)[TPW]) {
+  constexpr int NKS = LMAX / 32, XTS = LMAX + 8;
+  const int nks = (Lc + 31) / 32;
+  const int lane = opaque_tid() & 63, q = lane >> 4, r16 = lane & 15;
+#pragma unroll
+  for (int ip = 0; ip < TPW; ++ip) t[ip] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks < nks) {
+      const int l0 = 32 * ks + 8 * q;
+      const bf16x8 bw = scale8(bt[ks], ld4(&s_ws[l0]), ld4(&s_ws[l0 + 4]));
+#pragma unroll
+      for (int ip = 0; ip < TPW; ++ip)
+        t[ip] = mma(bw, ld8(s_xt + (16 * (pt0 + ip) + r16) * XTS + l0), t[ip]);
+    }
+  }
+}
+
+// Wavefronts per state n-tile and p-tiles per wavefront when 8 wavefronts
+// share the P x N state of a head.
+template <int P, int N>
+struct StateSplit {
+  static constexpr int TP = P / 16, TN = N / 16, NW = 8;
+  static constexpr int WPN = NW / TN;
+  static constexpr int TPW = TP / WPN;
+  static_assert(TN <= NW && NW % TN == 0 && TP % WPN == 0, "whole state tiles per wavefront");
+};
+
+// Phased schedule, phase 1 for the chain shapes (chain_variant, L <= 256):
+// chunk summary states S_c, one workgroup of 8 wavefronts per (b, c, h), from
+// the pre-pass's B^T (k_cb_and_bt_bf16, which also forms C B^T).  Stored as
+// [p][n] to ws_state; exp(cum_last) to ws_alpha.
+template <int P, int N>
+__global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void k_chunk_state_bf16(ScanArgs a) {
+  constexpr int LMAX = 256, NTH = kOutThreads, XTS = LMAX + 8;
+  using SP = StateSplit<P, N>;
+  __shared__ __attribute__((aligned(16))) float s_d[LMAX];
+  __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
+  __shared__ __attribute__((aligned(16))) float s_ws[LMAX];
+  __shared__ float s_wsum[4];
+  __shared__ __attribute__((aligned(16))) bf16 s_xt[P * XTS];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nt = wave % SP::TN, pt0 = (wave / SP::TN) * SP::TPW;
+  const int64_t u = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t h = u % a.H, bc = u / a.H, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t g = h / (a.H / a.G);
+  const int Lc = chunk_len(a, c);
+
+  // every global load is issued before the first wait: B^T, x, dt
+  bf16x8 bt[LMAX / 32];
+  state_bt_load<N, LMAX>(a, b, c, g, nt, Lc, bt);
+  XStage<P, LMAX, NTH> xs;
+  xs.load(a, b, c, h);
+  chunk_delta_cumsum_wide(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
+  xs.store(s_xt);
+  state_weights<LMAX, NTH>(Lc, s_d, s_cum, s_ws);
+  if (tid == 0) a.ws_alpha[(b * a.H + h) * a.Nc + c] = fast_exp(s_cum[Lc - 1]);
+  __syncthreads();
+
+  f32x4 t[SP::TPW];
+  state_tiles<LMAX, SP::TPW>(bt, pt0, Lc, s_xt, s_ws, t);
+  // lane holds S[n = 16 nt + 4q + r][p = 16 (pt0 + ip) + r16]: 4 consecutive n of one p
+  const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  float* out = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
+#pragma unroll
+  for (int ip = 0; ip < SP::TPW; ++ip)
+    st4(out + (16 * (pt0 + ip) + r16) * N + 16 * nt + 4 * q,
+        make_float4(t[ip][0], t[ip][1], t[ip][2], t[ip][3]));
+}
+
 // Chain kernel: one workgroup of 8 wavefronts per (b, h), chunks in order.
 // The float32 state [n][p] lives in matrix-core accumulators for the whole
 // sequence: wavefront w keeps n-tile w % (N/16) and P/16 / (8 / (N/16))
@@ -879,12 +987,8 @@ template <int P, int N, int LMAX, int VAR>
 __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void k_chain_bf16(ScanArgs a) {
   constexpr int NTH = kOutThreads, NW = kOutWaves;
-  constexpr int TP = P / 16, TN = N / 16;
-  constexpr int WPN = NW / TN;          // wavefronts per n-tile
-  constexpr int TPW = TP / WPN;         // p-tiles per wavefront
-  constexpr int NKS = LMAX / 32;
+  constexpr int TN = StateSplit<P, N>::TN, TPW = StateSplit<P, N>::TPW;
   constexpr int XTS = LMAX + 8, HS = N + 8;
-  static_assert(TN <= NW && NW % TN == 0 && TP % WPN == 0, "whole state tiles per wavefront");
   using Out = ChunkOut<P, N, LMAX, NW, VAR, false>;
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
@@ -902,10 +1006,11 @@ void k_chain_bf16(ScanArgs a) {
   const int64_t g = h / (a.H / a.G);
   const int64_t sbase = (b * a.H + h) * (int64_t)(P * N);
 
+  const HeadConsts hc = head_consts(a, h);
+  float2 dtv = scan_thread ? chunk_dt_load(a, b, 0, h) : make_float2(0.f, 0.f);
   Out out(a, b, 0, h, g, chunk_len(a, 0));
   XStage<P, LMAX, NTH> xs;
   xs.load(a, b, 0, h);
-  float2 dtv = scan_thread ? chunk_dt_load(a, b, 0, h) : make_float2(0.f, 0.f);
 
   // state tiles: acc_h[ip] holds h[p = 16 (pt0 + ip) + r16][n = 16 nt + 4q + r]
   f32x4 acc_h[TPW];
@@ -926,7 +1031,7 @@ void k_chain_bf16(ScanArgs a) {
     const int Lc = chunk_len(a, c);
     // ---- stage chunk c ----
     DeltaScan ds{};
-    if (scan_thread) ds = chunk_scan_stage1(a, c, h, dtv, s_wsum);
+    if (scan_thread) ds = chunk_scan_stage1(a, c, hc, dtv, s_wsum);
     __syncthreads();   // every wavefront is done with chunk c-1's LDS; s_wsum published
     if (scan_thread) chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
     xs.store(s_xt);
@@ -959,37 +1064,14 @@ void k_chain_bf16(ScanArgs a) {
     out.run(s_d, s_cum, s_w, s_xt, s_h);
 
     // ---- chunk summary state S_c, then h_c = fma(alpha, h_{c-1}, S_c) ----
-    // 32-token steps: the wavefront's B^T fragment (n-tile nt), scaled by the
-    // state weights, against its p-tiles' x^T fragments.  All the chunk's
-    // fragments are requested at once (steps past the chunk re-read its
-    // last), then the next chunk's x (its dt was requested before the
-    // outputs).
+    // the next chunk's x is issued right behind the state step's fragments
+    // (the last chunk re-reads itself: the same loads on every path)
     {
-      const int nks = (Lc + 31) / 32;
-      const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
-      const bf16* btc = reinterpret_cast<const bf16*>(a.ws_bt) +
-                        ((b * a.Nc + c) * a.G + g) * (int64_t)(N * a.L) +
-                        (int64_t)(16 * nt + r16) * a.L + 8 * q;
-      bf16x8 bt[NKS];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) bt[ks] = ld8(btc + 32 * min(ks, nks - 1));
-      {
-        // the last chunk re-reads itself: the same loads on every path
-        xs.load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
-      }
+      bf16x8 bt[LMAX / 32];
+      state_bt_load<N, LMAX>(a, b, c, g, nt, Lc, bt);
+      xs.load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
       f32x4 t[TPW];
-#pragma unroll
-      for (int ip = 0; ip < TPW; ++ip) t[ip] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ks < nks) {
-          const int l0 = 32 * ks + 8 * q;
-          const bf16x8 bw = scale8(bt[ks], ld4(&s_ws[l0]), ld4(&s_ws[l0 + 4]));
-#pragma unroll
-          for (int ip = 0; ip < TPW; ++ip)
-            t[ip] = mma(bw, ld8(s_xt + (16 * (pt0 + ip) + r16) * XTS + l0), t[ip]);
-        }
-      }
+      state_tiles<LMAX, TPW>(bt, pt0, Lc, s_xt, s_ws, t);
 #pragma unroll
       for (int ip = 0; ip < TPW; ++ip)
 #pragma unroll
@@ -1016,10 +1098,24 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
   hipError_t e;
   auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
   if ((e = rec(0)) != hipSuccess) return e;
-  if ((e = rec(1)) != hipSuccess) return e;
   const int64_t units = a.Bt * a.Nc * a.H;
-  hipLaunchKernelGGL((k_cb_and_chunk_state_bf16<P, N>), dim3((unsigned)units), dim3(kThreads), 0,
-                     stream, a, cb_tiles(a));
+  if (phased_prepass(P, N, a.L)) {
+    // C B^T and B^T of every (b, c, g), then the chunk states from B^T
+    const int64_t ncb = cb_blocks(a);
+    const int64_t nbt = (a.Bt * a.Nc * a.G * (a.L / 8) * (N / 8) + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL((k_cb_and_bt_bf16<N>), dim3((unsigned)(ncb + nbt)), dim3(kThreads), 0,
+                       stream, a, cb_tiles(a), ncb);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = rec(1)) != hipSuccess) return e;
+    if constexpr (chain_variant(P, N)) {
+      hipLaunchKernelGGL((k_chunk_state_bf16<P, N>), dim3((unsigned)units), dim3(kOutThreads), 0,
+                         stream, a);
+    }
+  } else {
+    if ((e = rec(1)) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_cb_and_chunk_state_bf16<P, N>), dim3((unsigned)units), dim3(kThreads), 0,
+                       stream, a, cb_tiles(a));
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = rec(2)) != hipSuccess) return e;
   if ((e = launch_state_pass(a, P, N, stream, true)) != hipSuccess) return e;

@@ -27,27 +27,40 @@ struct DeltaScan {
   float d0, d1, a0, a1, local, incl;
 };
 
-// Raw dt of this thread's two tokens (0 past the chunk or past T).
+// Raw dt of this thread's two tokens.  Tokens past the chunk or past T
+// re-read the chunk's last token: unconditional loads and no select on the
+// loaded values (a select would wait for them at once); stage 1 gives those
+// tokens Delta = 0.
 __device__ __forceinline__ float2 chunk_dt_load(const ScanArgs& a, int64_t b, int64_t c,
                                                 int64_t h) {
   const int l0 = 2 * opaque_tid(), l1 = l0 + 1;
   const int64_t t0 = c * a.L;
   const int last = (int)min<int64_t>(a.L, a.T - t0) - 1;   // last token of the chunk
-  // unconditional loads of clamped rows, then a select: no branch per load
   const float v0 = a.dt[(b * a.T + t0 + min(l0, last)) * a.H + h];
   const float v1 = a.dt[(b * a.T + t0 + min(l1, last)) * a.H + h];
-  return make_float2(l0 <= last ? v0 : 0.0f, l1 <= last ? v1 : 0.0f);
+  return make_float2(v0, v1);
+}
+
+// A and the dt bias of head h.  A kernel that walks several chunks of one
+// head loads them once: a load inside the walk would be waited for next to
+// the loads of the following chunk.
+struct HeadConsts {
+  float A, bias;
+};
+__device__ __forceinline__ HeadConsts head_consts(const ScanArgs& a, int64_t h) {
+  return HeadConsts{a.A[h], a.dt_bias ? a.dt_bias[h] : 0.0f};
 }
 
 // Stage 1: Delta, a and the wavefront-inclusive scan; publishes each
 // wavefront's total in s_wsum[wave].  No barrier inside.
-__device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_t c, int64_t h,
-                                                       float2 dtv, float* s_wsum) {
+__device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_t c,
+                                                       HeadConsts hc, float2 dtv,
+                                                       float* s_wsum) {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6;
   const int l0 = 2 * tid, l1 = l0 + 1;
   const int64_t t0 = c * a.L;
-  const float Ah = a.A[h];
-  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const float Ah = hc.A;
+  const float bias = hc.bias;
   DeltaScan s;
   s.d0 = (l0 < a.L && t0 + l0 < a.T)
              ? delta_of(__fadd_rn(dtv.x, bias), a.softplus, a.dt_min, a.dt_max) : 0.0f;
@@ -56,9 +69,13 @@ __device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_
   s.a0 = __fmul_rn(s.d0, Ah);
   s.a1 = __fmul_rn(s.d1, Ah);
   s.local = __fadd_rn(s.a0, s.a1);
-  s.incl = wave_inclusive_scan(s.local);
+  s.incl = wave_inclusive_scan(s.local, lane);
   if (lane == 63) s_wsum[wave] = s.incl;
   return s;
+}
+__device__ __forceinline__ DeltaScan chunk_scan_stage1(const ScanArgs& a, int64_t c, int64_t h,
+                                                       float2 dtv, float* s_wsum) {
+  return chunk_scan_stage1(a, c, head_consts(a, h), dtv, s_wsum);
 }
 
 // Stage 2 (after a barrier that follows stage 1): cross-wavefront offsets;
