@@ -151,25 +151,10 @@ __device__ __forceinline__ void cb_tile_bf16(const ScanArgs& a, int64_t bcg, int
   }
 }
 
-// Number of causal 16x16 tiles of one chunk and the C B^T blocks of a grid
-// that gives them workgroups of their own (4 tiles per block, rounded up to
-// whole rounds of the 8 XCDs).
+// Number of causal 16x16 tiles of one chunk.
 inline int cb_tiles(const ScanArgs& a) {
   const int nrt = (int)((a.L + 15) / 16);
   return nrt * (nrt + 1) / 2;
-}
-inline int64_t cb_blocks(const ScanArgs& a) {
-  const int64_t items = a.Bt * a.Nc * a.G * cb_tiles(a);
-  return ((items + 3) / 4 + 7) / 8 * 8;
-}
-// Tile work of C B^T block `block` (4 tiles, one per wavefront).
-template <int N>
-__device__ __forceinline__ void cb_block_bf16(const ScanArgs& a, int ntiles, int64_t block) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t item = block * 4 + wave;
-  const int64_t bcg = item / ntiles;
-  if (bcg >= a.Bt * a.Nc * a.G) return;
-  cb_tile_bf16<N>(a, bcg, (int)(item % ntiles));
 }
 
 // ---------------------------------------------------------------------------
@@ -378,12 +363,14 @@ struct ChunkOut {
   int64_t b, c, h, g;
   int Lc;
   float Dh;                       // D of head h (0 without D)
+  f32x4 yacc[TP];                 // y of the last tile run() computed, not yet stored
+  int yrow;                       // its token (per lane; >= Lc: nothing to store)
   bf16x8 cf[N / 32];              // C[i][32 nb + 8q ..] of the tile about to run
   bf16x8 sf[NS > 0 ? NS : 1];     // S[i][32 ks + 8q ..] of the 32-key steps
 
   __device__ __forceinline__ ChunkOut(const ScanArgs& a_, int64_t b_, int64_t c_, int64_t h_,
                                       int64_t g_, int Lc_)
-      : a(a_), b(b_), c(c_), h(h_), g(g_), Lc(Lc_), Dh(a_.D ? a_.D[h_] : 0.0f) {}
+      : a(a_), b(b_), c(c_), h(h_), g(g_), Lc(Lc_), Dh(a_.D ? a_.D[h_] : 0.0f), yrow(0) {}
 
   // Lane index through an opaque copy: inside the chain kernel's chunk loop
   // the many lane-dependent addresses are then formed where they are used
@@ -439,13 +426,33 @@ struct ChunkOut {
     }
   }
 
-  // Both tiles; prefetch() must have been called.
+  // y of the pending tile: lane holds y[yrow][p..p+3], p = 16 pt + 4q.
+  // Stores and loads share one in-order completion counter, so a store issued
+  // ahead of a load makes every wait for that load wait for the store too:
+  // each tile's store is issued after the next tile's loads, and the last
+  // one by the caller, after the loads it issues next.
+  __device__ __forceinline__ void store_pending() {
+    const int lane = lane_opaque(), q = lane >> 4;
+    if (yrow < Lc) {
+      bf16* yg = reinterpret_cast<bf16*>(a.y);
+      const int64_t rowy = ((b * a.T + c * a.L + yrow) * a.H + h) * P;
+#pragma unroll
+      for (int pt = 0; pt < TP; ++pt) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (bf16)yacc[pt][r];
+        st4b(yg + rowy + 16 * pt + 4 * q, o);
+      }
+    }
+  }
+
+  // Both tiles; prefetch() must have been called, and store_pending() must
+  // follow.
   __device__ __forceinline__ void run(const float* s_d, const float* s_cum, const float* s_w,
                                       const bf16* s_xt, const bf16* s_h) {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
     const int wave = wave_id(), n_rt = nrt();
-    const int64_t t0 = c * a.L;
-    bf16* yg = reinterpret_cast<bf16*>(a.y);
+    yrow = Lc;   // nothing pending unless a tile runs
     // skip-term operands: D = d1 + d2 + d3 exactly (bfloat16 parts of the
     // float32 value and of its remainders), on the diagonal of a 16 x 16 block
     bf16x4 e1, e2, e3;
@@ -475,6 +482,7 @@ struct ChunkOut {
                          ((b * a.Nc + c) * a.G + g) * a.L * a.L + (int64_t)ri * a.L;
       const bf16x4 sod = ld4b(srow + 16 * (I - (I & 1)) + 4 * q);
       const bf16x4 sdg = ld4b(srow + 16 * I + 4 * q);
+      if (k > 0) store_pending();   // the previous tile's y, behind this tile's loads
       f32x4 acc[TP];
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -578,17 +586,10 @@ struct ChunkOut {
         }
       }
 
-      // ---- store: lane holds y[i][p..p+3], p = 16 pt + 4q ----
-      if (ri < Lc) {
-        const int64_t rowy = ((b * a.T + t0 + ri) * a.H + h) * P;
+      // ---- y of this tile: stored later (store_pending) ----
 #pragma unroll
-        for (int pt = 0; pt < TP; ++pt) {
-          bf16x4 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[pt][r];
-          st4b(yg + rowy + 16 * pt + 4 * q, o);
-        }
-      }
+      for (int pt = 0; pt < TP; ++pt) yacc[pt] = acc[pt];
+      yrow = ri;
     }
   }
 };
@@ -833,25 +834,102 @@ void k_chunk_out_bf16(ScanArgs a) {
   }
   __syncthreads();
   out.run(s_d, s_cum, s_w, s_xt, s_h);
+  out.store_pending();
 }
 
 // ---------------------------------------------------------------------------
-// Chain schedule.
-// Pre-pass: C B^T tiles (first ncb blocks) and the transposed copy of B:
-// ws_bt[(b, c, g)][n][l] = B[b, cL + l, g, n], zero past the chunk's end.
-// One thread per 8 x 8 block (8 tokens x 8 state columns); consecutive
-// threads take consecutive token blocks, so a row of ws_bt is written by
-// consecutive threads.
+// Pre-pass of the chain's head shapes (chunks up to 256), both schedules.
+// Blocks [0, ncb): C B^T of one (b, c, g) per workgroup of 8 wavefronts.  B of
+// the chunk is staged in LDS, zero past the chunk's end, rows padded to N + 8
+// elements so that the 16 rows one fragment read touches fall in distinct
+// banks; wavefront w computes the tiles (I, J <= I) of its row tiles
+// I = col_tile_of<8>(w, k) (16 - I + 1 + I + 1 tiles whatever w: balanced)
+// with the C fragments of the row tile held in registers.  B and C are read
+// from memory once per chunk (one tile per wavefront had read each row once
+// per tile it enters: 4.6 times the bytes of B and C at 8 x 16384).  The
+// products are those of cb_tile_bf16, in the same order.
+// Blocks from ncb: the transposed copy of B, ws_bt[(b, c, g)][n][l] =
+// B[b, cL + l, g, n], zero past the chunk's end: one thread per 8 x 8 block
+// (8 tokens x 8 state columns); consecutive threads take consecutive token
+// blocks, so a row of ws_bt is written by consecutive threads.
 // ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 512;
+
 template <int N>
-__global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int ntiles, int64_t ncb) {
+__device__ __forceinline__ void cb_chunk_bf16(const ScanArgs& a, int64_t bcg, bf16* s_b) {
+  constexpr int BS = N + 8, NU = N / 8;
+  constexpr int NS8 = 256 * NU / kPrepThreads;    // 16-byte units of B per thread
+  const int tid = opaque_tid();
+  const int64_t g = bcg % a.G, bc = bcg / a.G, c = bc % a.Nc, b = bc / a.Nc;
+  const int Lc = chunk_len(a, c);
+  const int64_t rs = a.G * N;
+  const bf16* Bg = reinterpret_cast<const bf16*>(a.B) + ((b * a.T + c * a.L) * a.G + g) * N;
+  const bf16* Cg = reinterpret_cast<const bf16*>(a.C) + ((b * a.T + c * a.L) * a.G + g) * N;
+  {
+    bf16x8 v[NS8];
+#pragma unroll
+    for (int k = 0; k < NS8; ++k) {
+      const int e = tid + k * kPrepThreads, l = e / NU, u = e % NU;
+      v[k] = ld8(Bg + min(l, Lc - 1) * rs + 8 * u);
+    }
+#pragma unroll
+    for (int k = 0; k < NS8; ++k) {
+      const int e = tid + k * kPrepThreads, l = e / NU, u = e % NU;
+      st8(s_b + l * BS + 8 * u, l < Lc ? v[k] : bf16x8{});
+    }
+  }
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
+  const int n_rt = (Lc + 15) / 16;
+#pragma unroll 1
+  for (int k = 0; k < 2; ++k) {
+    const int I = col_tile_of<8>(wave, k);
+    if (I >= n_rt) continue;                  // uniform
+    const int ri = 16 * I + r16;
+    bf16x8 cf[N / 32];
+#pragma unroll
+    for (int nb = 0; nb < N / 32; ++nb)
+      cf[nb] = ld8_masked(Cg + min(ri, Lc - 1) * rs + nb * 32 + 8 * q, ri < Lc);
+#pragma unroll 2
+    for (int J = 0; J <= I; ++J) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < N / 32; ++nb)
+        acc = mma(ld8(s_b + (16 * J + r16) * BS + nb * 32 + 8 * q), cf[nb], acc);
+      // lane holds S[16I + r16][16J + 4q + r], r = 0..3
+      const int64_t at = bcg * a.L * a.L + (int64_t)(16 * I + r16) * a.L + 16 * J + 4 * q;
+      if (a.cb_bf16) {
+        bf16x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[r] = (bf16)acc[r];
+        st4b(reinterpret_cast<bf16*>(a.ws_cb) + at, o);
+      } else {
+        st4(a.ws_cb + at, make_float4(acc[0], acc[1], acc[2], acc[3]));
+      }
+    }
+  }
+}
+
+// per_chunk = 0 (too few chunks to fill the GPU): block k of [0, ncb) gives
+// its 8 wavefronts the tiles 8k .. 8k+7 of the chunks' tile list, one each
+// (cb_tile_bf16, the same products).
+template <int N>
+__global__ __launch_bounds__(kPrepThreads) void k_cb_and_bt_bf16(ScanArgs a, int64_t ncb,
+                                                                 int per_chunk, int ntiles) {
+  __shared__ __attribute__((aligned(16))) bf16 s_b[256 * (N + 8)];
   if ((int64_t)blockIdx.x < ncb) {
-    cb_block_bf16<N>(a, ntiles, blockIdx.x);
+    if (per_chunk) {
+      cb_chunk_bf16<N>(a, blockIdx.x, s_b);
+    } else {
+      const int64_t item = (int64_t)blockIdx.x * kOutWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      if (item < a.Bt * a.Nc * a.G * ntiles) cb_tile_bf16<N>(a, item / ntiles, (int)(item % ntiles));
+    }
     return;
   }
   const int LB = (int)(a.L / 8);
   const int64_t per = (int64_t)LB * (N / 8);
-  const int64_t id = ((int64_t)blockIdx.x - ncb) * kThreads + threadIdx.x;
+  const int64_t id = ((int64_t)blockIdx.x - ncb) * kPrepThreads + threadIdx.x;
   const int64_t unit = id / per;
   if (unit >= a.Bt * a.Nc * a.G) return;
   const int e = (int)(id % per);
@@ -870,6 +948,22 @@ __global__ __launch_bounds__(kThreads) void k_cb_and_bt_bf16(ScanArgs a, int nti
   bf16* dst = reinterpret_cast<bf16*>(a.ws_bt) + unit * N * a.L + (int64_t)(8 * nb) * a.L + 8 * lb;
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) st8(dst + cc * a.L, tr[cc]);
+}
+
+// Launch of the pre-pass (both schedules, chain shapes, L <= 256): a
+// workgroup per chunk once the chunks fill the GPU (two workgroups per
+// compute unit), else a wavefront per tile.
+constexpr int64_t kPrepChunkMin = 256;
+template <int N>
+hipError_t launch_prepass(const ScanArgs& a, hipStream_t stream) {
+  const int64_t chunks = a.Bt * a.Nc * a.G;
+  const int ntiles = cb_tiles(a);
+  const int per_chunk = chunks >= kPrepChunkMin ? 1 : 0;
+  const int64_t ncb = per_chunk ? chunks : (chunks * ntiles + kOutWaves - 1) / kOutWaves;
+  const int64_t nbt = (chunks * (a.L / 8) * (N / 8) + kPrepThreads - 1) / kPrepThreads;
+  hipLaunchKernelGGL((k_cb_and_bt_bf16<N>), dim3((unsigned)(ncb + nbt)), dim3(kPrepThreads), 0,
+                     stream, a, ncb, per_chunk, ntiles);
+  return hipGetLastError();
 }
 
 // Chunk summary state of one wavefront's tiles, from zero, in 32-token
@@ -1070,6 +1164,7 @@ void k_chain_bf16(ScanArgs a) {
       bf16x8 bt[LMAX / 32];
       state_bt_load<N, LMAX>(a, b, c, g, nt, Lc, bt);
       xs.load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
+      out.store_pending();
       f32x4 t[TPW];
       state_tiles<LMAX, TPW>(bt, pt0, Lc, s_xt, s_ws, t);
 #pragma unroll
@@ -1101,11 +1196,7 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
   const int64_t units = a.Bt * a.Nc * a.H;
   if (phased_prepass(P, N, a.L)) {
     // C B^T and B^T of every (b, c, g), then the chunk states from B^T
-    const int64_t ncb = cb_blocks(a);
-    const int64_t nbt = (a.Bt * a.Nc * a.G * (a.L / 8) * (N / 8) + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL((k_cb_and_bt_bf16<N>), dim3((unsigned)(ncb + nbt)), dim3(kThreads), 0,
-                       stream, a, cb_tiles(a), ncb);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_prepass<N>(a, stream)) != hipSuccess) return e;
     if ((e = rec(1)) != hipSuccess) return e;
     if constexpr (chain_variant(P, N)) {
       hipLaunchKernelGGL((k_chunk_state_bf16<P, N>), dim3((unsigned)units), dim3(kOutThreads), 0,
@@ -1155,11 +1246,7 @@ hipError_t launch_chain(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
     hipError_t e;
     auto rec = [&](int k) -> hipError_t { return ev ? hipEventRecord(ev[k], stream) : hipSuccess; };
     if ((e = rec(0)) != hipSuccess) return e;
-    const int64_t ncb = cb_blocks(a);
-    const int64_t nbt = (a.Bt * a.Nc * a.G * (a.L / 8) * (N / 8) + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL((k_cb_and_bt_bf16<N>), dim3((unsigned)(ncb + nbt)), dim3(kThreads), 0,
-                       stream, a, cb_tiles(a), ncb);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_prepass<N>(a, stream)) != hipSuccess) return e;
     if ((e = rec(1)) != hipSuccess) return e;
     if ((e = rec(2)) != hipSuccess) return e;
     if ((e = rec(3)) != hipSuccess) return e;

@@ -263,14 +263,16 @@ def test_backward_of_a_split_sequence(io):
         return float((a_.double() - b_.double()).abs().max() / b_.double().abs().max())
 
     # bf16: each side rounds the reversed scan's operands and outputs to
-    # bfloat16 along its own chunk grid, so they agree to the bf16 bar only
-    bar = TOL[io]
-    for k in ("dx", "ddt", "dB", "dC"):
-        cat = torch.cat([first[k], second[k]], 1)
-        assert rel(cat, whole[k]) <= bar, (k, rel(cat, whole[k]))
-    for k in ("dA", "dD", "ddt_bias"):
-        assert rel(first[k] + second[k], whole[k]) <= bar, k
-    assert rel(first["dinitial_state"], whole["dinitial_state"]) <= bar
+    # bfloat16 along its own chunk grid, so the two differ by bf16 roundings
+    # of the same values: at most about one bf16 unit (2^-8 relative) of the
+    # largest gradient; measured at most 7.3e-4 (dB).  float32: the float32 bar.
+    bar = 4e-3 if io == "bf16" else TOL[io]
+    gg = {k: rel(torch.cat([first[k], second[k]], 1), whole[k]) for k in ("dx", "ddt", "dB", "dC")}
+    gg.update({k: rel(first[k] + second[k], whole[k]) for k in ("dA", "dD", "ddt_bias")})
+    gg["dh0"] = rel(first["dinitial_state"], whole["dinitial_state"])
+    print(f"split {io} joined against whole:", {k: f"{v:.2e}" for k, v in gg.items()})
+    bad = {k: v for k, v in gg.items() if not v <= bar}
+    assert not bad, bad
     # the two parts joined, against the fp64 adjoint oracle of the whole
     # sequence: a chunk-boundary or handoff error below the GPU-to-GPU bar
     # still shows here
