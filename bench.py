@@ -62,12 +62,15 @@ KERNEL_SOURCES = {
 }
 # HBM bytes per launch from the counter runs: (kernel key, workload) -> (bytes, digest)
 TRAFFIC = {
-    # counter runs and calibration: profiles/chunk_out_f32_m130_f32_decode_m2p7_b64_hbm_bytes.txt
-    ("chunk_out/f32", "m130_f32"): (38.19e6 + 30.45e6, "56909f5168ee5332"),
-    ("decode", "m2p7_decode_b64"): (169.13e6 + 168.43e6, "d164f32a0d3b83f2"),
-    # profiles/conv1d_m2p7_bf16_and_step_b64_hbm_bytes.txt
-    ("conv1d", "conv_m2p7_bf16"): (49.20e6 + 44.07e6, "fbbf46e4543e456b"),
-    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "fbbf46e4543e456b"),
+    # counter runs and calibration: profiles/hbm_bytes_prefill_decode_kernels.txt
+    ("chain/bf16", "m1p3_long_bf16"): (1504.64e6 + 1095.88e6, "db8ddd8e6e5c2080"),
+    ("chunk_out/bf16", "m2p7_bf16"): (67.16e6 + 41.94e6, "db8ddd8e6e5c2080"),
+    ("chunk_out/f32", "m130_f32"): (43.13e6 + 30.59e6, "5ebdc37ac5a171d8"),
+    ("decode", "m2p7_decode_b1"): (2.72e6 + 2.63e6, "4f7d0aaaa5d6836c"),
+    ("decode", "m2p7_decode_b16"): (42.37e6 + 42.11e6, "4f7d0aaaa5d6836c"),
+    ("decode", "m2p7_decode_b64"): (169.10e6 + 168.43e6, "4f7d0aaaa5d6836c"),
+    ("conv1d", "conv_m2p7_bf16"): (49.20e6 + 44.07e6, "126ba24eb97486e5"),
+    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "126ba24eb97486e5"),
 }
 COPY_CALIBRATION_BYTES = 1 << 30
 
