@@ -580,10 +580,23 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
   // go through LDS, double-buffered, the next head's slice loaded into
   // registers while this head's is consumed.  Each wavefront reads its own A
   // rows directly.
+  //
+  // bfloat16 inputs (kB): A (dy or x) holds bf16 values, exact as
+  // matrix-core operands, so the per-row scale is applied to the products
+  // instead of to A, and Z (float32) is split into two bf16 parts
+  // Z = Zh + Zl (Zh = bf16(Z), Zl = bf16(Z - Zh)): A Zh + A Zl on
+  // v_mfma_f32_16x16x32_bf16 is A Z to within the rounding of Zl (2^-16
+  // relative), at an eighth of the float32 matrix-core time.  Z is staged
+  // transposed, [n][p] bf16 (the contraction index p contiguous, as the
+  // operand wants it), its 16-byte units XOR-swizzled by the row's lane
+  // index so that the 8 lanes of a read group hit distinct banks.
+  constexpr bool kB = sizeof(T) == 2 && P % 32 == 0 && KK == 4;
   constexpr int ZS = NW + 4;                        // padded LDS row
   constexpr int ZQ = NW / 4;                        // float4 per Z row
   constexpr int ZL = (P * ZQ + kBwdThreads - 1) / kBwdThreads;
-  __shared__ __attribute__((aligned(16))) float s_z[2][P * ZS];
+  constexpr int ZU = (P / 8 < 8 ? P / 8 : 8) - 1;   // swizzle mask of a [n][p] row's units
+  __shared__ __attribute__((aligned(16))) float s_z[2][kB ? 4 : P * ZS];
+  __shared__ __attribute__((aligned(16))) bf16 s_zt[2][kB ? 2 * NW * P : 8];
   auto load_z = [&](int64_t h, float4 (&zr)[ZL]) {
     const float* Z = zptr(h);
     const bool zok = Z != nullptr;
@@ -598,30 +611,88 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
 #pragma unroll
     for (int k = 0; k < ZL; ++k) {
       const int e = tid + k * kBwdThreads, pr = e / ZQ, cq = e % ZQ;
-      if (e < P * ZQ) *reinterpret_cast<float4*>(&s_z[buf][pr * ZS + 4 * cq]) = zr[k];
+      if (e < P * ZQ) {
+        if constexpr (kB) {
+          const float v[4] = {zr[k].x, zr[k].y, zr[k].z, zr[k].w};
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const int n = 4 * cq + cc;
+            const bf16 hi = (bf16)v[cc];
+            const bf16 lo = (bf16)__fsub_rn(v[cc], (float)hi);
+            const int at = n * P + 8 * ((pr >> 3) ^ ((n >> 2) & ZU)) + (pr & 7);
+            s_zt[buf][at] = hi;
+            s_zt[buf][NW * P + at] = lo;
+          }
+        } else {
+          *reinterpret_cast<float4*>(&s_z[buf][pr * ZS + 4 * cq]) = zr[k];
+        }
+      }
     }
   };
   // A rows stay in their io type until used: converting bf16 as it arrives
   // put a wait for the next head's rows right after their loads (2.7B-shaped
   // backward 0.66 -> 0.64 ms)
   using RawA = typename std::conditional<sizeof(T) == 4, float4, bf16x4>::type;
+  // kB: the A fragments of the bf16 products (8 consecutive p per lane) and
+  // the prefix sums and Delta of the lane's four output rows
   struct Arow {
-    RawA av[P / 16];
-    double ci, clast;
-    float dj, wn;
+    RawA av[kB ? 1 : P / 16];
+    bf16x8 avb[kB ? P / 32 : 1];
+    double ci, clast, co[kB ? 4 : 1];
+    float dj, wn, djo[kB ? 4 : 1];
   };
   const T* amat = reinterpret_cast<const T*>(role ? a.x : a.dy);
   auto load_a = [&](int64_t h, Arow& o) {
     const int64_t rowi = (b * a.T + t0 + iac) * a.H + h;
     const T* arow = amat + rowi * P;
+    if constexpr (kB) {
 #pragma unroll
-    for (int pb = 0; pb < P / 16; ++pb) o.av[pb] = *reinterpret_cast<const RawA*>(arow + 16 * pb + 4 * q);
-    o.ci = a.cum[rowi];
+      for (int kb = 0; kb < P / 32; ++kb)
+        o.avb[kb] = *reinterpret_cast<const bf16x8*>(arow + 32 * kb + 8 * q);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t ro = (b * a.T + t0 + min(io[r], Lc - 1)) * a.H + h;
+        o.co[r] = a.cum[ro];
+        o.djo[r] = a.wd[ro];
+      }
+    } else {
+#pragma unroll
+      for (int pb = 0; pb < P / 16; ++pb) o.av[pb] = *reinterpret_cast<const RawA*>(arow + 16 * pb + 4 * q);
+      o.ci = a.cum[rowi];
+      o.dj = a.wd[rowi];
+    }
     o.clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
-    o.dj = a.wd[rowi];
     o.wn = (role == 1 && c + 1 < a.Nc) ? a.wd[(b * a.T + t0 + L) * a.H + h] : 0.0f;
   };
-  auto process_h = [&](int64_t h, const Arow& o, const float* sz) {
+  auto process_h = [&](int64_t h, const Arow& o, const float* sz, const bf16* szt) {
+    f32x4 ah[KK];
+#pragma unroll
+    for (int k = 0; k < KK; ++k) ah[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kB) {
+      // lane (q, r16): A[row r16][p = 32 kb + 8q ..], Z[p][n = KK r16 + kk]
+#pragma unroll
+      for (int kb = 0; kb < P / 32; ++kb) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int n = KK * r16 + kk;
+          const int at = n * P + 8 * ((4 * kb + q) ^ (r16 & ZU));
+          const bf16x8 zh = *reinterpret_cast<const bf16x8*>(szt + at);
+          const bf16x8 zl = *reinterpret_cast<const bf16x8*>(szt + NW * P + at);
+          ah[kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.avb[kb], zh, ah[kk], 0, 0, 0);
+          ah[kk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(o.avb[kb], zl, ah[kk], 0, 0, 0);
+        }
+      }
+      // the row scale of output row io[r] (0 past the chunk)
+      const float gs = (role == 1 && c + 1 < a.Nc) ? expf(o.wn * a.A[h]) : 1.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = io[r] < Lc;
+        const float sc = role == 0 ? (ok ? fast_exp((float)o.co[r]) : 0.0f)
+                                   : (ok ? gs * o.djo[r] * fast_exp((float)(o.clast - o.co[r])) : 0.0f);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) ah[kk][r] *= sc;
+      }
+    } else {
     float scale;
     if (role == 0) {
       scale = iok ? fast_exp((float)o.ci) : 0.0f;
@@ -630,9 +701,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
       const float gs = c + 1 < a.Nc ? expf(o.wn * a.A[h]) : 1.0f;
       scale = iok ? gs * o.dj * fast_exp((float)(o.clast - o.ci)) : 0.0f;
     }
-    f32x4 ah[KK];
-#pragma unroll
-    for (int k = 0; k < KK; ++k) ah[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int pb = 0; pb < P / 16; ++pb) {
       float4 avf;
@@ -659,6 +727,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) ah[kk] = mma(av[e], zv[kk], ah[kk]);
       }
+    }
     }
     // u_i (role 0) or v_j (role 1) over this split's columns
     float ds[4];
@@ -692,7 +761,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
         load_z(h + 1, zr);
         load_a(h + 1, nxt);
       }
-      process_h(h, cur, s_z[buf]);
+      process_h(h, cur, s_z[buf], s_zt[buf]);
       if (more) store_z(buf ^ 1, zr);
       __syncthreads();
       cur = nxt;
