@@ -848,10 +848,11 @@ void k_chunk_out_bf16(ScanArgs a) {
 // from memory once per chunk (one tile per wavefront had read each row once
 // per tile it enters: 4.6 times the bytes of B and C at 8 x 16384).  The
 // products are those of cb_tile_bf16, in the same order.
-// Blocks from ncb: the transposed copy of B, ws_bt[(b, c, g)][n][l] =
-// B[b, cL + l, g, n], zero past the chunk's end: one thread per 8 x 8 block
-// (8 tokens x 8 state columns); consecutive threads take consecutive token
-// blocks, so a row of ws_bt is written by consecutive threads.
+// The transposed copy of B, ws_bt[(b, c, g)][n][l] = B[b, cL + l, g, n], zero
+// past the chunk's end: one thread per 8 x 8 block (8 tokens x 8 state
+// columns), consecutive threads on consecutive token blocks, so a row of
+// ws_bt is written by consecutive threads; from the staged rows in the
+// workgroup-per-chunk mode, else in blocks from ncb.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 512;
 
@@ -879,6 +880,22 @@ __device__ __forceinline__ void cb_chunk_bf16(const ScanArgs& a, int64_t bcg, bf
     }
   }
   __syncthreads();
+  // the transposed copy ws_bt of the chunk, from the staged rows (zero past
+  // the chunk's end as staged): 8 x 8 blocks, consecutive threads on
+  // consecutive token blocks, as the B^T blocks of the tile-per-wavefront mode
+  {
+    const int LB = (int)(a.L / 8);
+    bf16* bt = reinterpret_cast<bf16*>(a.ws_bt) + bcg * N * a.L;
+    for (int e = tid; e < LB * (N / 8); e += kPrepThreads) {
+      const int lb = e % LB, nb = e / LB;
+      bf16x8 in[8], tr[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) in[r] = ld8(s_b + (8 * lb + r) * BS + 8 * nb);
+      transpose8(in, tr);
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) st8(bt + (int64_t)(8 * nb + cc) * a.L + 8 * lb, tr[cc]);
+    }
+  }
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int n_rt = (Lc + 15) / 16;
@@ -960,7 +977,9 @@ hipError_t launch_prepass(const ScanArgs& a, hipStream_t stream) {
   const int ntiles = cb_tiles(a);
   const int per_chunk = chunks >= kPrepChunkMin ? 1 : 0;
   const int64_t ncb = per_chunk ? chunks : (chunks * ntiles + kOutWaves - 1) / kOutWaves;
-  const int64_t nbt = (chunks * (a.L / 8) * (N / 8) + kPrepThreads - 1) / kPrepThreads;
+  // (a workgroup per chunk writes the chunk's B^T itself)
+  const int64_t nbt =
+      per_chunk ? 0 : (chunks * (a.L / 8) * (N / 8) + kPrepThreads - 1) / kPrepThreads;
   hipLaunchKernelGGL((k_cb_and_bt_bf16<N>), dim3((unsigned)(ncb + nbt)), dim3(kPrepThreads), 0,
                      stream, a, ncb, per_chunk, ntiles);
   return hipGetLastError();
