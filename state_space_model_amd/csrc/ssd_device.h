@@ -111,6 +111,20 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
+// base + elems elements, the offset formed in 32 bits (bytes): with a
+// wavefront-uniform base the load or store can take the scalar-base address
+// form (base in scalar registers, a 32-bit offset per lane) instead of a
+// 64-bit address computed per lane.  elems * sizeof(T) must fit in 32 bits.
+template <typename T>
+__device__ __forceinline__ T* off32(T* base, uint32_t elems) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + (elems * (uint32_t)sizeof(T)));
+}
+template <typename T>
+__device__ __forceinline__ const T* off32(const T* base, uint32_t elems) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) +
+                                    (elems * (uint32_t)sizeof(T)));
+}
+
 // Inclusive prefix sum across the 64 lanes of a wavefront (Hillis-Steele,
 // log2(64) = 6 shuffle steps; a fixed order, so the result is reproducible).
 // `lane` is the caller's lane index; a caller in a loop passes an opaque copy

@@ -192,14 +192,15 @@ struct XStage {
     const int64_t t0 = c * a.L;
     Lc = chunk_len(a, c);
     const bf16* xg = reinterpret_cast<const bf16*>(a.x) + ((b * a.T + t0) * a.H + h) * P;
-    const int xs = (int)(a.H * P);
+    const uint32_t xs = (uint32_t)(a.H * P);
 #pragma unroll
     for (int i = 0; i < NXB; ++i) {
       int lb, cb;
       block_of(min(tid + i * NTH, NBLK - 1), lb, cb);
 #pragma unroll
       for (int r = 0; r < 8; ++r)
-        v[i][r] = *reinterpret_cast<const vrow*>(xg + min(8 * lb + r, Lc - 1) * xs + CW * cb);
+        v[i][r] = *reinterpret_cast<const vrow*>(
+            off32(xg, (uint32_t)min(8 * lb + r, Lc - 1) * xs + CW * cb));
     }
   }
   // x^T[p][l] into s_xt (row stride XTS), zero past the chunk
@@ -389,10 +390,13 @@ struct ChunkOut {
   // no zeroing select: they feed only output columns that are never stored)
   __device__ __forceinline__ void load_c(int I) {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
-    const bf16* Cg = reinterpret_cast<const bf16*>(a.C) + ((b * a.T + c * a.L) * a.G + g) * N + 8 * q;
-    const int i = min(16 * I + r16, Lc - 1);
+    // chunk base (uniform) + a 32-bit lane offset: the loads take the
+    // scalar-base form, with no 64-bit address arithmetic per lane
+    const bf16* Cg = reinterpret_cast<const bf16*>(a.C) + ((b * a.T + c * a.L) * a.G + g) * N;
+    const uint32_t i = (uint32_t)min(16 * I + r16, Lc - 1);
+    const uint32_t rs = (uint32_t)(a.G * N);
 #pragma unroll
-    for (int nb = 0; nb < N / 32; ++nb) cf[nb] = ld8(Cg + i * a.G * N + nb * 32);
+    for (int nb = 0; nb < N / 32; ++nb) cf[nb] = ld8(off32(Cg, i * rs + nb * 32 + 8 * q));
   }
 
   // The first tile's C and every S row the wavefront's tiles need.  Each load
@@ -403,26 +407,26 @@ struct ChunkOut {
     const int wave = wave_id(), n_rt = nrt();
     load_c(min(col_tile_of<NW>(wave, 0), n_rt - 1));
     const bf16* S = reinterpret_cast<const bf16*>(a.ws_cb) + ((b * a.Nc + c) * a.G + g) * a.L * a.L;
-    const bf16* row[CT];
+    uint32_t row[CT];
     int nf[CT];
 #pragma unroll
     for (int k = 0; k < CT; ++k) {
       const int I = col_tile_of<NW>(wave, k);
       const bool v = I < n_rt;
       const int Ic = v ? I : n_rt - 1;
-      row[k] = S + (int64_t)(16 * Ic + r16) * a.L;
+      row[k] = (uint32_t)(16 * Ic + r16) * (uint32_t)a.L + 8 * q;
       nf[k] = v ? I >> 1 : 0;
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
-      const bf16* src;
+      uint32_t src;
       if constexpr (CT == 2) {
         const int ks1 = NS - 1 - j;
         src = j < nf[0] ? row[0] + 32 * j : (ks1 < nf[1] ? row[1] + 32 * ks1 : row[1]);
       } else {
         src = j < nf[0] ? row[0] + 32 * j : row[0];
       }
-      sf[j] = ld8(src + 8 * q);
+      sf[j] = ld8(off32(S, src));
     }
   }
 
@@ -434,14 +438,14 @@ struct ChunkOut {
   __device__ __forceinline__ void store_pending() {
     const int lane = lane_opaque(), q = lane >> 4;
     if (yrow < Lc) {
-      bf16* yg = reinterpret_cast<bf16*>(a.y);
-      const int64_t rowy = ((b * a.T + c * a.L + yrow) * a.H + h) * P;
+      bf16* yg = reinterpret_cast<bf16*>(a.y) + ((b * a.T + c * a.L) * a.H + h) * P;
+      const uint32_t rowy = (uint32_t)yrow * (uint32_t)(a.H * P) + 4 * q;
 #pragma unroll
       for (int pt = 0; pt < TP; ++pt) {
         bf16x4 o;
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[r] = (bf16)yacc[pt][r];
-        st4b(yg + rowy + 16 * pt + 4 * q, o);
+        st4b(off32(yg, rowy + 16 * pt), o);
       }
     }
   }
@@ -478,10 +482,11 @@ struct ChunkOut {
       const int ri = 16 * I + r16;
       // the 16-key block before the diagonal (re-reading the diagonal one when
       // I is even) and the diagonal block: consumed after the 32-key steps
-      const bf16* srow = reinterpret_cast<const bf16*>(a.ws_cb) +
-                         ((b * a.Nc + c) * a.G + g) * a.L * a.L + (int64_t)ri * a.L;
-      const bf16x4 sod = ld4b(srow + 16 * (I - (I & 1)) + 4 * q);
-      const bf16x4 sdg = ld4b(srow + 16 * I + 4 * q);
+      const bf16* sch = reinterpret_cast<const bf16*>(a.ws_cb) +
+                        ((b * a.Nc + c) * a.G + g) * a.L * a.L;
+      const uint32_t srow = (uint32_t)ri * (uint32_t)a.L + 4 * q;
+      const bf16x4 sod = ld4b(off32(sch, srow + 16 * (I - (I & 1))));
+      const bf16x4 sdg = ld4b(off32(sch, srow + 16 * I));
       if (k > 0) store_pending();   // the previous tile's y, behind this tile's loads
       f32x4 acc[TP];
 #pragma unroll
@@ -999,10 +1004,10 @@ __device__ __forceinline__ void state_bt_load(const ScanArgs& a, int64_t b, int6
   const int nks = (Lc + 31) / 32;
   const int lane = opaque_tid() & 63, q = lane >> 4, r16 = lane & 15;
   const bf16* btc = reinterpret_cast<const bf16*>(a.ws_bt) +
-                    ((b * a.Nc + c) * a.G + g) * (int64_t)(N * a.L) +
-                    (int64_t)(16 * nt + r16) * a.L + 8 * q;
+                    ((b * a.Nc + c) * a.G + g) * (int64_t)(N * a.L);
+  const uint32_t row = (uint32_t)(16 * nt + r16) * (uint32_t)a.L + 8 * q;
 #pragma unroll
-  for (int ks = 0; ks < LMAX / 32; ++ks) bt[ks] = ld8(btc + 32 * min(ks, nks - 1));
+  for (int ks = 0; ks < LMAX / 32; ++ks) bt[ks] = ld8(off32(btc, row + 32 * min(ks, nks - 1)));
 }
 
 template <int LMAX, int TPW>

@@ -36,8 +36,10 @@ __device__ __forceinline__ float2 chunk_dt_load(const ScanArgs& a, int64_t b, in
   const int l0 = 2 * opaque_tid(), l1 = l0 + 1;
   const int64_t t0 = c * a.L;
   const int last = (int)min<int64_t>(a.L, a.T - t0) - 1;   // last token of the chunk
-  const float v0 = a.dt[(b * a.T + t0 + min(l0, last)) * a.H + h];
-  const float v1 = a.dt[(b * a.T + t0 + min(l1, last)) * a.H + h];
+  const float* dg = a.dt + (b * a.T + t0) * a.H + h;        // uniform base, 32-bit lane offsets
+  const uint32_t hs = (uint32_t)a.H;
+  const float v0 = *off32(dg, (uint32_t)min(l0, last) * hs);
+  const float v1 = *off32(dg, (uint32_t)min(l1, last) * hs);
   return make_float2(v0, v1);
 }
 
