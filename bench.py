@@ -63,14 +63,14 @@ KERNEL_SOURCES = {
 # HBM bytes per launch from the counter runs: (kernel key, workload) -> (bytes, digest)
 TRAFFIC = {
     # counter runs and calibration: profiles/hbm_bytes_prefill_decode_kernels.txt
-    ("chain/bf16", "m1p3_long_bf16"): (1504.64e6 + 1095.88e6, "db8ddd8e6e5c2080"),
-    ("chunk_out/bf16", "m2p7_bf16"): (67.16e6 + 41.94e6, "db8ddd8e6e5c2080"),
-    ("chunk_out/f32", "m130_f32"): (43.13e6 + 30.59e6, "5ebdc37ac5a171d8"),
-    ("decode", "m2p7_decode_b1"): (2.72e6 + 2.63e6, "4f7d0aaaa5d6836c"),
-    ("decode", "m2p7_decode_b16"): (42.37e6 + 42.11e6, "4f7d0aaaa5d6836c"),
-    ("decode", "m2p7_decode_b64"): (169.10e6 + 168.43e6, "4f7d0aaaa5d6836c"),
-    ("conv1d", "conv_m2p7_bf16"): (49.20e6 + 44.07e6, "126ba24eb97486e5"),
-    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "126ba24eb97486e5"),
+    ("chain/bf16", "m1p3_long_bf16"): (1494.12e6 + 1096.80e6, "6cfe3e54207cd288"),
+    ("chunk_out/bf16", "m2p7_bf16"): (67.11e6 + 41.94e6, "6cfe3e54207cd288"),
+    ("chunk_out/f32", "m130_f32"): (43.13e6 + 30.60e6, "a69d264b603eff81"),
+    ("decode", "m2p7_decode_b1"): (2.72e6 + 2.63e6, "731634a88119e81c"),
+    ("decode", "m2p7_decode_b16"): (42.37e6 + 42.11e6, "731634a88119e81c"),
+    ("decode", "m2p7_decode_b64"): (169.10e6 + 168.43e6, "731634a88119e81c"),
+    ("conv1d", "conv_m2p7_bf16"): (49.20e6 + 44.07e6, "3367d563b506e53e"),
+    ("conv1d", "conv_m2p7_decode_b64"): (3.21e6 + 2.75e6, "3367d563b506e53e"),
 }
 COPY_CALIBRATION_BYTES = 1 << 30
 
