@@ -310,7 +310,7 @@ def bench_decode(ssd, torch, batch, steps_n, warmup):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for _ in range(max(1, warmup)):
+        for _ in range(max(1, min(warmup, 3))):   # eager passes before the capture
             body()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
@@ -657,7 +657,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="one decode batch size (default: 1, 16 and 64)")

@@ -1089,18 +1089,20 @@ void k_chunk_state_bf16(ScanArgs a) {
 // Chain kernel: one workgroup of 8 wavefronts per (b, h), chunks in order.
 // The float32 state [n][p] lives in matrix-core accumulators for the whole
 // sequence: wavefront w keeps n-tile w % (N/16) and P/16 / (8 / (N/16))
-// p-tiles of it; LDS holds only bf16(h) as the inter-chunk operand.  Per
-// chunk c:
-//   stage:   Delta/cum, x^T and bf16(h_{c-1}) into LDS, decay tables
-//   outputs: ChunkOut (inter-chunk term from the LDS copy)
-//   state:   S_c = sum_ks (B^T w)_bf16 x into a fresh accumulator, then
-//            h_c = fma(alpha_c, h_{c-1}, S_c)
-// Load order (memory counters retire loads in order, so a wait for a load
-// also waits for every older one): the next chunk's dt before the outputs;
-// the state step's B^T fragments, then the next chunk's x (consumed after
-// the next barrier); the next
-// chunk's first output-pass operands right after that barrier, so they fly
-// during the staging.
+// p-tiles of it; LDS holds only bf16(h) as the inter-chunk operand.  Delta
+// and its prefix sum run one chunk ahead, in double-buffered LDS, so a chunk
+// takes two barriers:
+//   stage:   x^T and bf16(h_{c-1}) into LDS; the first tile's C and S rows
+//            requested; chunk c's decay tables and state weights (from its
+//            prefix, formed during chunk c-1); stage 1 of chunk c+1's prefix
+//            sum (wavefronts 0-3); barrier
+//   then:    stage 2 of chunk c+1's prefix sum (wavefronts 0-3, into the
+//            other buffer); outputs (ChunkOut); S_c = sum_ks (B^T w)_bf16 x
+//            into a fresh accumulator, h_c = fma(alpha_c, h_{c-1}, S_c), the
+//            next chunk's x requested; barrier
+// Load order (memory counters retire loads in order): dt two chunks ahead
+// before the outputs; the state step's B^T fragments, then the next chunk's
+// x; the first output-pass operands before the first barrier.
 template <int P, int N, int LMAX, int VAR>
 __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void k_chain_bf16(ScanArgs a) {
@@ -1108,8 +1110,8 @@ void k_chain_bf16(ScanArgs a) {
   constexpr int TN = StateSplit<P, N>::TN, TPW = StateSplit<P, N>::TPW;
   constexpr int XTS = LMAX + 8, HS = N + 8;
   using Out = ChunkOut<P, N, LMAX, NW, VAR, false>;
-  __shared__ __attribute__((aligned(16))) float s_d[LMAX];
-  __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
+  __shared__ __attribute__((aligned(16))) float s_d[2][LMAX];
+  __shared__ __attribute__((aligned(16))) float s_cum[2][LMAX];
   __shared__ __attribute__((aligned(16))) float s_ws[LMAX];
   __shared__ float s_wsum[4];
   __shared__ __attribute__((aligned(16))) float s_w[tile_table_size(LMAX) + 4];
@@ -1125,7 +1127,14 @@ void k_chain_bf16(ScanArgs a) {
   const int64_t sbase = (b * a.H + h) * (int64_t)(P * N);
 
   const HeadConsts hc = head_consts(a, h);
-  float2 dtv = scan_thread ? chunk_dt_load(a, b, 0, h) : make_float2(0.f, 0.f);
+  // chunk 0's prefix into buffer 0; chunk 1's dt
+  {
+    DeltaScan ds{};
+    if (scan_thread) ds = chunk_scan_stage1(a, 0, hc, chunk_dt_load(a, b, 0, h), s_wsum);
+    __syncthreads();
+    if (scan_thread) chunk_scan_stage2(a, ds, s_wsum, s_d[0], s_cum[0]);
+  }
+  float2 dtv = scan_thread ? chunk_dt_load(a, b, a.Nc > 1 ? 1 : 0, h) : make_float2(0.f, 0.f);
   Out out(a, b, 0, h, g, chunk_len(a, 0));
   XStage<P, LMAX, NTH> xs;
   xs.load(a, b, 0, h);
@@ -1144,14 +1153,13 @@ void k_chain_bf16(ScanArgs a) {
       }
     }
   }
+  __syncthreads();   // chunk 0's prefix
 
   for (int64_t c = 0; c < a.Nc; ++c) {
     const int Lc = chunk_len(a, c);
+    const int buf = (int)(c & 1);
+    const bool next = c + 1 < a.Nc;   // uniform
     // ---- stage chunk c ----
-    DeltaScan ds{};
-    if (scan_thread) ds = chunk_scan_stage1(a, c, hc, dtv, s_wsum);
-    __syncthreads();   // every wavefront is done with chunk c-1's LDS; s_wsum published
-    if (scan_thread) chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
     xs.store(s_xt);
     {
       const int lane = Out::lane_opaque(), q = lane >> 4, r16 = lane & 15;
@@ -1163,23 +1171,23 @@ void k_chain_bf16(ScanArgs a) {
         st4b(s_h + (16 * (pt0 + ip) + r16) * HS + 16 * nt + 4 * q, v);
       }
     }
-    __syncthreads();
-    // this chunk's C and S rows, in flight during the tables (issued once the
-    // staging registers are free)
     out.c = c;
     out.Lc = Lc;
     out.prefetch();
-    tile_decay_table<VAR, NTH, LMAX>(Lc, s_d, s_cum, s_w);
-    state_weights<LMAX, NTH>(Lc, s_d, s_cum, s_ws);
-    const float alpha = fast_exp(s_cum[Lc - 1]);
+    tile_decay_table<VAR, NTH, LMAX>(Lc, s_d[buf], s_cum[buf], s_w);
+    state_weights<LMAX, NTH>(Lc, s_d[buf], s_cum[buf], s_ws);
+    const float alpha = fast_exp(s_cum[buf][Lc - 1]);
+    DeltaScan ds{};
+    if (scan_thread && next) ds = chunk_scan_stage1(a, c + 1, hc, dtv, s_wsum);
     __syncthreads();
+    if (scan_thread && next) chunk_scan_stage2(a, ds, s_wsum, s_d[buf ^ 1], s_cum[buf ^ 1]);
 
-    // the next chunk's dt (the last chunk re-reads itself), ahead of the
+    // dt two chunks ahead (the last chunks re-read the last), ahead of the
     // state step's loads so that the next staging does not wait behind them
-    if (scan_thread) dtv = chunk_dt_load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
+    if (scan_thread) dtv = chunk_dt_load(a, b, c + 2 < a.Nc ? c + 2 : a.Nc - 1, h);
 
     // ---- outputs of chunk c ----
-    out.run(s_d, s_cum, s_w, s_xt, s_h);
+    out.run(s_d[buf], s_cum[buf], s_w, s_xt, s_h);
 
     // ---- chunk summary state S_c, then h_c = fma(alpha, h_{c-1}, S_c) ----
     // the next chunk's x is issued right behind the state step's fragments
@@ -1187,7 +1195,7 @@ void k_chain_bf16(ScanArgs a) {
     {
       bf16x8 bt[LMAX / 32];
       state_bt_load<N, LMAX>(a, b, c, g, nt, Lc, bt);
-      xs.load(a, b, c + 1 < a.Nc ? c + 1 : c, h);
+      xs.load(a, b, next ? c + 1 : c, h);
       out.store_pending();
       f32x4 t[TPW];
       state_tiles<LMAX, TPW>(bt, pt0, Lc, s_xt, s_ws, t);
@@ -1196,6 +1204,7 @@ void k_chain_bf16(ScanArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc_h[ip][r] = __fmaf_rn(alpha, acc_h[ip][r], t[ip][r]);
     }
+    __syncthreads();   // every wavefront is done with s_xt, s_h, s_w, s_ws and buffer buf
   }
 
   if (a.final_state) {
