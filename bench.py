@@ -330,13 +330,49 @@ def bench_decode(ssd, torch, batch, steps_n, warmup):
     s_io = xs.element_size()
     bpt = decode_bytes_per_token(H, P, N, G, s_io)
     achieved = bpt * batch / (ms_step * 1e-3) / 1e9
+    copy_us = device_copy_us(torch, states, steps_n)
     return {"batch": batch, "steps": steps_n, "graph_replays": reps, "ms_per_step": ms_step,
+            "device_copy_us": copy_us,
             "tokens_per_s": batch / (ms_step * 1e-3), "state_buffers": nstates,
             "state_bytes_each": state_bytes,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                          "traffic": traffic_for("decode", f"m2p7_decode_b{batch}")},
             "bytes_per_token": bpt}
+
+
+def device_copy_us(torch, states, steps_n, reps=3):
+    """Time per step of torch's device copy of one state into another buffer
+    (the decode step's state bytes, read once and written once), replayed
+    from a HIP graph over the same rotation of buffers: a plain copy of the
+    step's bytes, for scale beside the step's own time."""
+    dst = [torch.empty_like(t) for t in states]
+    n = len(states)
+
+    def body():
+        for t in range(steps_n):
+            dst[t % n].copy_(states[t % n])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * steps_n)
+    del g, dst
+    return us
 
 
 def launch_floor_us(ssd, torch, n=1024):

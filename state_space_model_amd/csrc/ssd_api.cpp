@@ -318,7 +318,20 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   pl->NS = N > 64 ? (int32_t)(N / 64) : 1;
   const int64_t nbt = (int64_t)pl->NB * (pl->NB + 1) / 2;
   const int64_t bcg = Bt * Nc * G;
-  head_split(hpg, bcg * nbt, 768, &pl->HS, &pl->hpw);
+  // k_bwd_mix: as many head splits as fit in one round of resident
+  // workgroups (three per compute unit for bfloat16 rows of P <= 64, two
+  // otherwise, on 256 compute units), so that no second, nearly empty round
+  // follows; with more units than that, one split
+  {
+    const int64_t slots = 256 * ((d->io_dtype == SSD_BF16 && d->headdim <= 64) ? 3 : 2);
+    const int64_t units = bcg * nbt;
+    int64_t want = units > 0 ? slots / units : 1;
+    if (want < 1) want = 1;
+    if (want > hpg) want = hpg;
+    const int64_t p = (hpg + want - 1) / want;
+    pl->hpw = (int32_t)p;
+    pl->HS = (int32_t)((hpg + p - 1) / p);
+  }
   head_split(hpg, bcg * 2 * pl->NS * pl->NB, 512, &pl->HSD, &pl->hpwd);
 
   const size_t es = io_size(d->io_dtype);

@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
 // every partial sum has one writer, and the consumers add them in a fixed
 // order.
 template <typename T, int P>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_mix(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
@@ -360,7 +360,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
   // up to the order of its sums.  Otherwise they are staged as float32.
   constexpr bool kB = sizeof(T) == 2 && P % 32 == 0;
   using ST = typename std::conditional<kB, bf16, float>::type;
-  using VT = typename std::conditional<kB, uint4, float4>::type;
+  // native vectors (not HIP's struct vector types): the staging registers
+  // must stay in VGPRs across process(), and the struct types were kept on
+  // the stack
+  using VT = typename std::conditional<kB, bf16x8, f32x4>::type;
   constexpr int EPV = kB ? 8 : 4;                 // elements per 16-byte vector
   constexpr int XS = P + EPV;                     // padded LDS row
   constexpr int RQ = P / EPV;                     // vectors per row
@@ -373,8 +376,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
       const int row = rem / RQ, p4 = rem % RQ;
       const int grow = min((which ? 64 * J : 64 * I) + row, Lc - 1);
       const T* src = (which ? xg : dyg) + (int64_t)grow * xrs + h * P + EPV * p4;
-      if constexpr (kB) st[k] = *reinterpret_cast<const uint4*>(src);
-      else st[k] = ld4_io<T>(src, true);
+      if constexpr (kB) {
+        st[k] = *reinterpret_cast<const bf16x8*>(src);
+      } else {
+        const float4 v = ld4_io<T>(src, true);
+        st[k] = f32x4{v.x, v.y, v.z, v.w};
+      }
     }
   };
   auto store_stage = [&](int buf, const VT (&st)[SL]) {
@@ -385,17 +392,38 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
       *reinterpret_cast<VT*>(&s_op[buf][(which * 64 + row) * XS + EPV * p4]) = st[k];
     }
   };
+  // The prefix sums of the block's rows (I) and columns (J) and Delta of its
+  // columns go through LDS with the operand rows (a register copy per lane
+  // of its ten values, for this head and the next, held the kernel to two
+  // wavefronts per SIMD).  Every thread loads one of each (rows past the
+  // chunk read its last token); threads 0..127 store the prefix sums, 128..191
+  // the Deltas.
+  __shared__ double s_cum[2][128];
+  __shared__ float s_dj[2][64];
+  struct Tok {
+    double cv;
+    float wv;
+  };
+  auto load_tok = [&](int64_t h, Tok& o) {
+    const int rrow = tid < 64 ? 64 * I + tid : 64 * J + (tid & 63);
+    o.cv = cumg[(int64_t)min(rrow, Lc - 1) * a.H + h];
+    o.wv = wdg[(int64_t)min(64 * J + (tid & 63), Lc - 1) * a.H + h];   // masked with the decay
+  };
+  auto store_tok = [&](int buf, const Tok& o) {
+    if (tid < 128) s_cum[buf][tid] = o.cv;
+    else if (tid < 192) s_dj[buf][tid - 128] = o.wv;
+  };
   struct Dec {
     double ci[2][4], cj[2];
     float dj[2];
   };
-  auto load_dec = [&](int64_t h, Dec& o) {
+  auto read_dec = [&](int buf, Dec& o) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o.ci[s][r] = cumg[(int64_t)min(io[s][r], Lc - 1) * a.H + h];
-      o.cj[s] = cumg[(int64_t)min(jb[s], Lc - 1) * a.H + h];
-      o.dj[s] = wdg[(int64_t)min(jb[s], Lc - 1) * a.H + h];   // masked with the decay
+      for (int r = 0; r < 4; ++r) o.ci[s][r] = s_cum[buf][32 * wr + 16 * s + 4 * q + r];
+      o.cj[s] = s_cum[buf][64 + 32 * wc + 16 * s + r16];
+      o.dj[s] = s_dj[buf][32 * wc + 16 * s + r16];
     }
   };
   auto process = [&](int64_t h, const ST* so, const Dec& o) {
@@ -479,23 +507,27 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_mix(BwdArgs a) {
   };
   {
     VT st[SL];
-    Dec cur, nxt;
+    Tok tk;
     load_stage(hb, st);
-    load_dec(hb, cur);
+    load_tok(hb, tk);
     store_stage(0, st);
+    store_tok(0, tk);
     __syncthreads();
     int buf = 0;
+    // the next head's loads are issued on every path (the last head re-reads
+    // itself into the buffer nobody reads again): a conditional load kept
+    // the staging registers in scratch memory across process()
 #pragma unroll 1
     for (int64_t h = hb; h < he; ++h) {
-      const bool more = h + 1 < he;   // uniform
-      if (more) {
-        load_stage(h + 1, st);
-        load_dec(h + 1, nxt);
-      }
+      const int64_t hn = h + 1 < he ? h + 1 : h;   // uniform
+      load_stage(hn, st);
+      load_tok(hn, tk);
+      Dec cur;
+      read_dec(buf, cur);
       process(h, s_op[buf], cur);
-      if (more) store_stage(buf ^ 1, st);
+      store_stage(buf ^ 1, st);
+      store_tok(buf ^ 1, tk);
       __syncthreads();
-      cur = nxt;
       buf ^= 1;
     }
   }
@@ -597,35 +629,56 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
   constexpr int ZU = (P / 8 < 8 ? P / 8 : 8) - 1;   // swizzle mask of a [n][p] row's units
   __shared__ __attribute__((aligned(16))) float s_z[2][kB ? 4 : P * ZS];
   __shared__ __attribute__((aligned(16))) bf16 s_zt[2][kB ? 2 * NW * P : 8];
+  // Z's loads are issued on every path (a missing Z reads the forward states
+  // and is zeroed when stored): a load under a condition leaves a different
+  // number of loads in flight on each path, and the compiler's wait after the
+  // merge then also covers loads issued after the ones it needs
+  // kB: thread (g, cq) = (tid / ZQ, tid % ZQ) holds rows ZL g .. ZL g + ZL-1
+  // of column quad cq, so that each of its four columns goes to the
+  // transposed LDS copy as one packed store of ZL consecutive p; otherwise
+  // rows tid / ZQ + k kBwdThreads / ZQ
+  auto z_row = [&](int k) -> int {
+    if constexpr (kB) return ZL * (tid / ZQ) + k;
+    return min((tid + k * kBwdThreads) / ZQ, P - 1);
+  };
   auto load_z = [&](int64_t h, float4 (&zr)[ZL]) {
     const float* Z = zptr(h);
-    const bool zok = Z != nullptr;
-    const float* Zs = zok ? Z : a.fwd_state;   // a valid address either way
+    const float* Zs = Z != nullptr ? Z : a.fwd_state;   // a valid address either way
+    const int cq = tid % ZQ;
 #pragma unroll
-    for (int k = 0; k < ZL; ++k) {
-      const int e = tid + k * kBwdThreads, pr = min(e / ZQ, P - 1), cq = e % ZQ;
-      zr[k] = ld4_io<float>(Zs + (int64_t)pr * N + ns * NW + 4 * cq, zok);
-    }
+    for (int k = 0; k < ZL; ++k)
+      zr[k] = *reinterpret_cast<const float4*>(Zs + (int64_t)z_row(k) * N + ns * NW + 4 * cq);
   };
-  auto store_z = [&](int buf, const float4 (&zr)[ZL]) {
+  auto store_z = [&](int buf, int64_t h, float4 (&zr)[ZL]) {
+    if (zptr(h) == nullptr) {   // uniform
 #pragma unroll
-    for (int k = 0; k < ZL; ++k) {
-      const int e = tid + k * kBwdThreads, pr = e / ZQ, cq = e % ZQ;
-      if (e < P * ZQ) {
-        if constexpr (kB) {
-          const float v[4] = {zr[k].x, zr[k].y, zr[k].z, zr[k].w};
+      for (int k = 0; k < ZL; ++k) zr[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if constexpr (kB) {
+      // column n = 4 cq + cc: ZL consecutive p (one aligned run inside a
+      // 16-byte unit), hi and lo parts, one store each
+      using Pack = typename std::conditional<ZL == 2, bf16x2,
+                   typename std::conditional<ZL == 4, bf16x4, bf16x8>::type>::type;
+      const int cq = tid % ZQ, pr0 = z_row(0);
 #pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const int n = 4 * cq + cc;
-            const bf16 hi = (bf16)v[cc];
-            const bf16 lo = (bf16)__fsub_rn(v[cc], (float)hi);
-            const int at = n * P + 8 * ((pr >> 3) ^ ((n >> 2) & ZU)) + (pr & 7);
-            s_zt[buf][at] = hi;
-            s_zt[buf][NW * P + at] = lo;
-          }
-        } else {
-          *reinterpret_cast<float4*>(&s_z[buf][pr * ZS + 4 * cq]) = zr[k];
+      for (int cc = 0; cc < 4; ++cc) {
+        const int n = 4 * cq + cc;
+        Pack hi, lo;
+#pragma unroll
+        for (int k = 0; k < ZL; ++k) {
+          const float v = cc == 0 ? zr[k].x : cc == 1 ? zr[k].y : cc == 2 ? zr[k].z : zr[k].w;
+          hi[k] = (bf16)v;
+          lo[k] = (bf16)__fsub_rn(v, (float)hi[k]);
         }
+        const int at = n * P + 8 * ((pr0 >> 3) ^ ((n >> 2) & ZU)) + (pr0 & 7);
+        *reinterpret_cast<Pack*>(&s_zt[buf][at]) = hi;
+        *reinterpret_cast<Pack*>(&s_zt[buf][NW * P + at]) = lo;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < ZL; ++k) {
+        const int e = tid + k * kBwdThreads, pr = e / ZQ, cq = e % ZQ;
+        if (e < P * ZQ) *reinterpret_cast<float4*>(&s_z[buf][pr * ZS + 4 * cq]) = zr[k];
       }
     }
   };
@@ -639,7 +692,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
     RawA av[kB ? 1 : P / 16];
     bf16x8 avb[kB ? P / 32 : 1];
     double ci, clast, co[kB ? 4 : 1];
-    float dj, wn, djo[kB ? 4 : 1];
+    float dj, wn, Ah, djo[kB ? 4 : 1];
   };
   const T* amat = reinterpret_cast<const T*>(role ? a.x : a.dy);
   auto load_a = [&](int64_t h, Arow& o) {
@@ -662,7 +715,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
       o.dj = a.wd[rowi];
     }
     o.clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
-    o.wn = (role == 1 && c + 1 < a.Nc) ? a.wd[(b * a.T + t0 + L) * a.H + h] : 0.0f;
+    // Delta of the next chunk's first token (role 1; a valid row is read on
+    // every path and the value is dropped where it does not apply)
+    o.wn = a.wd[(b * a.T + min(t0 + L, a.T - 1)) * a.H + h];
+    // A of the head with the rest of its values: loaded where it is used, it
+    // was the newest load in flight, and its wait covered every load before it
+    o.Ah = a.A[h];
   };
   auto process_h = [&](int64_t h, const Arow& o, const float* sz, const bf16* szt) {
     f32x4 ah[KK];
@@ -683,7 +741,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
         }
       }
       // the row scale of output row io[r] (0 past the chunk)
-      const float gs = (role == 1 && c + 1 < a.Nc) ? expf(o.wn * a.A[h]) : 1.0f;
+      const float gs = (role == 1 && c + 1 < a.Nc) ? expf(o.wn * o.Ah) : 1.0f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = io[r] < Lc;
@@ -698,7 +756,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
       scale = iok ? fast_exp((float)o.ci) : 0.0f;
     } else {
       // abar of the next chunk's first token turns R1's entering state into Ghat_c
-      const float gs = c + 1 < a.Nc ? expf(o.wn * a.A[h]) : 1.0f;
+      const float gs = c + 1 < a.Nc ? expf(o.wn * o.Ah) : 1.0f;
       scale = iok ? gs * o.dj * fast_exp((float)(o.clast - o.ci)) : 0.0f;
     }
 #pragma unroll
@@ -751,18 +809,18 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
     Arow cur, nxt;
     load_z(hb, zr);
     load_a(hb, cur);
-    store_z(0, zr);
+    store_z(0, hb, zr);
     __syncthreads();
     int buf = 0;
+    // the next head's loads are issued on every path (the last head re-reads
+    // itself into the buffer nobody reads again)
 #pragma unroll 1
     for (int64_t h = hb; h < he; ++h) {
-      const bool more = h + 1 < he;   // uniform
-      if (more) {
-        load_z(h + 1, zr);
-        load_a(h + 1, nxt);
-      }
+      const int64_t hn = h + 1 < he ? h + 1 : h;   // uniform
+      load_z(hn, zr);
+      load_a(hn, nxt);
       process_h(h, cur, s_z[buf], s_zt[buf]);
-      if (more) store_z(buf ^ 1, zr);
+      store_z(buf ^ 1, hn, zr);
       __syncthreads();
       cur = nxt;
       buf ^= 1;
@@ -901,7 +959,13 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a, int sh) {
 // One workgroup per (b, c, h), one token per thread (L <= 256): dL/da_t from
 // the block sums of Q and the per-token u, v (prefix and suffix sums within
 // the chunk), the dt gradient, and this chunk's parts of dA, ddt_bias, dD.
+// Every global load is issued before the first value is used (rows, blocks
+// and splits that do not apply read a valid clamped address and are dropped
+// by a select), so the workgroup waits for memory once instead of once per
+// dependent step.
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
+  constexpr int kMaxNB = 4;   // 64-token blocks of a chunk (L <= 256)
+  constexpr int kMaxNS = 2;   // 64-column splits of N (N <= 128)
   __shared__ float s_w[kBwdThreads / 64];
   const int l = threadIdx.x;
   const int64_t u = blockIdx.x;
@@ -910,72 +974,109 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
   const int Lc = chunk_tokens(a, c);
   const int NB = a.NB, nbc = (Lc + 63) / 64;
   const bool ok = l < Lc;
-  const int64_t row = (b * a.T + t0 + (ok ? l : 0)) * a.H + h;
+  const int lc = ok ? l : 0;
+  const int64_t row = (b * a.T + t0 + lc) * a.H + h;
   const int64_t BtT = a.Bt * a.T;
+  const int64_t PN = (int64_t)a.P * a.N;
+
+  // per-token and per-head scalars
+  const float dt_raw = a.dt[row], wd_t = a.wd[row], ddin_t = a.ddin[row], dDp_t = a.dDp[row];
+  const float Ah = a.A[h];
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+  const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
+  const bool has_next = c + 1 < a.Nc;
+  const float wd_next = a.wd[(b * a.T + min(t0 + L, a.T - 1)) * a.H + h];
+  // Q's block row sums (blocks (K, Jb), Jb <= K) and column sums (blocks (Ib, K), K <= Ib < nbc)
+  const int K = lc >> 6, s = lc & 63;
+  const float* qr = a.qrow + ((b * a.Nc + c) * a.H + h) * (int64_t)NB * NB * 128;
+  const float* qc = a.qcol + ((b * a.Nc + c) * a.H + h) * (int64_t)NB * NB * 128;
+  float qrv[kMaxNB][2], qcv[kMaxNB][2];
+#pragma unroll
+  for (int k = 0; k < kMaxNB; ++k) {
+    const int jb = min(k, K);
+    const int ib = min(max(k, K), nbc - 1);
+    qrv[k][0] = qr[(K * NB + jb) * 128 + s];
+    qrv[k][1] = qr[(K * NB + jb) * 128 + 64 + s];
+    qcv[k][0] = qc[(ib * NB + K) * 128 + s];
+    qcv[k][1] = qc[(ib * NB + K) * 128 + 64 + s];
+  }
+  float uvv[kMaxNS][2];
+#pragma unroll
+  for (int k = 0; k < kMaxNS; ++k) {
+    const int ns = min(k, a.NS - 1);
+    uvv[k][0] = a.uv[((int64_t)ns * BtT + b * a.T + t0 + lc) * a.H + h];
+    uvv[k][1] = a.uv[((int64_t)(a.NS + ns) * BtT + b * a.T + t0 + lc) * a.H + h];
+  }
+  // e^{cum_last} <Ghat_c, H_c>: Ghat_c is R1's state at the next chunk (times
+  // that chunk's first abar) or dfinal for the last chunk; without either the
+  // term is 0 (the loads then read H_c twice)
+  const float* Hc = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
+  const float* Gh = has_next ? a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN
+                             : (a.dfinal ? a.dfinal + (b * a.H + h) * PN : nullptr);
+  const bool has_g = Gh != nullptr;
+  float sc = 0.0f;
+  {
+    // float4 vectors, eight of each operand in flight per thread; vectors past
+    // the state re-read its last one and are dropped
+    const float4* g4 = reinterpret_cast<const float4*>(has_g ? Gh : Hc);
+    const float4* h4 = reinterpret_cast<const float4*>(Hc);
+    const int n4 = (int)(PN / 4);
+    for (int e0 = 0; e0 < n4; e0 += 8 * kBwdThreads) {
+      float4 gv[8], hv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = min(e0 + k * kBwdThreads + l, n4 - 1);
+        gv[k] = g4[e];
+        hv[k] = h4[e];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (e0 + k * kBwdThreads + l < n4) {
+          sc = __fmaf_rn(gv[k].x, hv[k].x, sc);
+          sc = __fmaf_rn(gv[k].y, hv[k].y, sc);
+          sc = __fmaf_rn(gv[k].z, hv[k].z, sc);
+          sc = __fmaf_rn(gv[k].w, hv[k].w, sc);
+        }
+      }
+    }
+    if (!has_g) sc = 0.0f;
+  }
 
   float dv = 0.0f, uu = 0.0f, vv = 0.0f;
   if (ok) {
     // R_t = sum_{s<t} (column sum of s below the diagonal - row sum of s left of it)
-    const int K = l >> 6, s = l & 63;
-    const float* qr = a.qrow + ((b * a.Nc + c) * a.H + h) * (int64_t)NB * NB * 128;
-    const float* qc = a.qcol + ((b * a.Nc + c) * a.H + h) * (int64_t)NB * NB * 128;
     float rs = 0.0f, cs = 0.0f;
-    for (int Jb = 0; Jb <= K; ++Jb) rs += qr[(K * NB + Jb) * 128 + s] + qr[(K * NB + Jb) * 128 + 64 + s];
-    for (int Ib = K; Ib < nbc; ++Ib) cs += qc[(Ib * NB + K) * 128 + s] + qc[(Ib * NB + K) * 128 + 64 + s];
+#pragma unroll
+    for (int k = 0; k < kMaxNB; ++k) rs += k <= K ? qrv[k][0] + qrv[k][1] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < kMaxNB; ++k) cs += (k >= K && k < nbc) ? qcv[k][0] + qcv[k][1] : 0.0f;
     dv = cs - rs;
-    for (int ns = 0; ns < a.NS; ++ns) {
-      uu += a.uv[((int64_t)ns * BtT + b * a.T + t0 + l) * a.H + h];
-      vv += a.uv[((int64_t)(a.NS + ns) * BtT + b * a.T + t0 + l) * a.H + h];
+#pragma unroll
+    for (int k = 0; k < kMaxNS; ++k) {
+      uu += k < a.NS ? uvv[k][0] : 0.0f;
+      vv += k < a.NS ? uvv[k][1] : 0.0f;
     }
   }
   const float inc_d = block_inclusive_scan(dv, s_w);
   const float inc_v = block_inclusive_scan(vv, s_w);
   const float inc_u = block_inclusive_scan(uu, s_w);
   const float tot_u = block_sum(uu, s_w);
-
-  // e^{cum_last} <Ghat_c, H_c>
-  const int64_t PN = (int64_t)a.P * a.N;
-  const float* Hc = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
-  const float* Gh = nullptr;
-  float gs = 1.0f;
-  if (c + 1 < a.Nc) {
-    Gh = a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN;
-    gs = expf(a.wd[(b * a.T + t0 + L) * a.H + h] * a.A[h]);
-  } else if (a.dfinal) {
-    Gh = a.dfinal + (b * a.H + h) * PN;
-  }
-  float sc = 0.0f;
-  if (Gh) {
-    // float4 vectors, four in flight per thread (P N is a multiple of 256)
-    const float4* g4 = reinterpret_cast<const float4*>(Gh);
-    const float4* h4 = reinterpret_cast<const float4*>(Hc);
-    const int64_t n4 = PN / 4;
-#pragma unroll 4
-    for (int64_t e = l; e < n4; e += kBwdThreads) {
-      const float4 gv = g4[e], hv = h4[e];
-      sc = __fmaf_rn(gv.x, hv.x, sc);
-      sc = __fmaf_rn(gv.y, hv.y, sc);
-      sc = __fmaf_rn(gv.z, hv.z, sc);
-      sc = __fmaf_rn(gv.w, hv.w, sc);
-    }
-  }
   sc = block_sum(sc, s_w);
-  const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
+  const float gs = has_next ? expf(wd_next * Ah) : 1.0f;
   sc *= gs * (float)exp(clast);
 
   float pA = 0.0f, pB = 0.0f, pD = 0.0f;
   if (ok) {
     const float da = (inc_d - dv) + (tot_u - (inc_u - uu)) + (inc_v - vv) + sc;
-    const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-    const float z = a.dt[row] + bias;
+    const float z = dt_raw + bias;
     const float pre = a.softplus ? softplus_of(z) : z;   // as in delta_of: the same clip decision
     float gate = (pre >= a.dt_min && pre <= a.dt_max) ? 1.0f : 0.0f;
     if (a.softplus) gate *= 1.0f / (1.0f + expf(-z));
-    const float gd = __fmaf_rn(a.A[h], da, a.ddin[row]) * gate;
+    const float gd = __fmaf_rn(Ah, da, ddin_t) * gate;
     a.ddt[row] = gd;
-    pA = a.wd[row] * da;
+    pA = wd_t * da;
     pB = gd;
-    pD = a.dDp[row];
+    pD = dDp_t;
   }
   pA = block_sum(pA, s_w);
   pB = block_sum(pB, s_w);
