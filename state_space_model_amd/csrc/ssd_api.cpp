@@ -260,7 +260,7 @@ namespace {
 // Backward pass: descriptors of the three internal scans and the workspace.
 // ---------------------------------------------------------------------------
 enum BwdRegion {
-  kScanWs, kScanWsR1, kWd, kCum, kDtr1, kR1x, kR1b, kR1c, kR1h0, kR1y, kR1final, kMix, kQrow,
+  kScanWs, kScanWsR1, kWd, kCum, kRscale, kDtr1, kR1x, kR1b, kR1c, kR1h0, kR1y, kR1final, kMix, kQrow,
   kQcol, kUv, kDbcPart, kDdin, kDdp, kPart, kNumRegions
 };
 
@@ -277,9 +277,13 @@ struct BwdPlan {
 
 // Splits of a group's heads over workgroups: enough workgroups to fill the
 // device (`target`), each with at least one head.
-inline void head_split(int64_t hpg, int64_t units, int64_t target, int32_t* splits,
-                       int32_t* per) {
-  int64_t want = units > 0 ? (target + units - 1) / units : 1;
+// Heads of a group dealt to `splits` workgroups of `per` heads each: as many
+// splits as fit in one round of `slots` resident workgroups (so that no
+// second, nearly empty round follows), one split when the units alone fill
+// the round.
+inline void head_split_round(int64_t hpg, int64_t units, int64_t slots, int32_t* splits,
+                             int32_t* per) {
+  int64_t want = units > 0 ? slots / units : 1;
   if (want < 1) want = 1;
   if (want > hpg) want = hpg;
   const int64_t p = (hpg + want - 1) / want;
@@ -318,21 +322,13 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   pl->NS = N > 64 ? (int32_t)(N / 64) : 1;
   const int64_t nbt = (int64_t)pl->NB * (pl->NB + 1) / 2;
   const int64_t bcg = Bt * Nc * G;
-  // k_bwd_mix: as many head splits as fit in one round of resident
-  // workgroups (three per compute unit for bfloat16 rows of P <= 64, two
-  // otherwise, on 256 compute units), so that no second, nearly empty round
-  // follows; with more units than that, one split
-  {
-    const int64_t slots = 256 * ((d->io_dtype == SSD_BF16 && d->headdim <= 64) ? 3 : 2);
-    const int64_t units = bcg * nbt;
-    int64_t want = units > 0 ? slots / units : 1;
-    if (want < 1) want = 1;
-    if (want > hpg) want = hpg;
-    const int64_t p = (hpg + want - 1) / want;
-    pl->hpw = (int32_t)p;
-    pl->HS = (int32_t)((hpg + p - 1) / p);
-  }
-  head_split(hpg, bcg * 2 * pl->NS * pl->NB, 512, &pl->HSD, &pl->hpwd);
+  // k_bwd_mix: three resident workgroups per compute unit (of 256) for
+  // bfloat16 rows of P <= 64, two otherwise (LDS and registers);
+  // k_bwd_dcdb: the same, three workgroups per compute unit at P <= 64
+  head_split_round(hpg, bcg * nbt, 256 * ((d->io_dtype == SSD_BF16 && d->headdim <= 64) ? 3 : 2),
+                   &pl->HS, &pl->hpw);
+  head_split_round(hpg, bcg * 2 * pl->NS * pl->NB, 256 * (d->headdim <= 64 ? 3 : 2), &pl->HSD,
+                   &pl->hpwd);
 
   const size_t es = io_size(d->io_dtype);
   const size_t nst = (size_t)s0.n_state, nbc = (size_t)s0.n_bc;
@@ -344,6 +340,7 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   sizes[kScanWsR1] = pl->scan_ws_r1;
   sizes[kWd] = ndt * 4;
   sizes[kCum] = ndt * 8;
+  sizes[kRscale] = 2 * ndt * 4;
   sizes[kDtr1] = ndt1 * 4;
   sizes[kR1x] = nx1 * es;
   sizes[kR1b] = nbc1 * es;
@@ -649,7 +646,8 @@ ssd_status ssd_chunk_scan_backward(const ssd_scan_desc* d, const void* x, const 
   a.x = x; a.dt = dt; a.dt_bias = dt_bias; a.A = A; a.B = B; a.C = C; a.D = D;
   a.h0 = initial_state; a.dy = dy; a.dfinal = dfinal_state;
   const bool bf = d->io_dtype == SSD_BF16;
-  a.wd = atf(kWd); a.cum = reinterpret_cast<double*>(w + pl.off[kCum]); a.dtr1 = atf(kDtr1);
+  a.wd = atf(kWd); a.cum = reinterpret_cast<double*>(w + pl.off[kCum]);
+  a.rscale = atf(kRscale); a.dtr1 = atf(kDtr1);
   a.r1_x = at(kR1x); a.r1_b = at(kR1b); a.r1_c = at(kR1c); a.r1_h0 = atf(kR1h0);
   a.r1_y = at(kR1y); a.r1_final = atf(kR1final);
   a.fwd_state = atf(kScanWs);

@@ -276,6 +276,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
     if (l < Lc) a.cum[row] = v;
     carry = __shfl(v, 63, 64);
   }
+  // the row scales of the dC / dB inter-chunk products (the same float
+  // operations the products' kernel would apply to the prefix sums)
+  const double clast = carry;
+  const int64_t n = a.Bt * a.T * a.H;
+  for (int l = lane; l < Lc; l += 64) {
+    const int64_t row = (b * a.T + t0 + l) * a.H + h;
+    const double cv = a.cum[row];   // this lane's own store above
+    a.rscale[row] = fast_exp((float)cv);
+    a.rscale[n + row] = a.wd[row] * fast_exp((float)(clast - cv));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -555,7 +565,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 //   intra-chunk part: M B (role 0, j <= i) or M^T C (role 1, i >= j), its 16-token
 //     blocks dealt out over the head splits.
 template <typename T, int P, int KK>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_bwd_dcdb(BwdArgs a) {
   constexpr int NW = 16 * KK;
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -691,10 +701,11 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
   struct Arow {
     RawA av[kB ? 1 : P / 16];
     bf16x8 avb[kB ? P / 32 : 1];
-    double ci, clast, co[kB ? 4 : 1];
-    float dj, wn, Ah, djo[kB ? 4 : 1];
+    float sc[kB ? 4 : 1];   // the row scale of the role (output rows io[r], or row ia)
+    float wn, Ah;
   };
   const T* amat = reinterpret_cast<const T*>(role ? a.x : a.dy);
+  const float* rsc = a.rscale + (role ? a.Bt * a.T * a.H : 0);
   auto load_a = [&](int64_t h, Arow& o) {
     const int64_t rowi = (b * a.T + t0 + iac) * a.H + h;
     const T* arow = amat + rowi * P;
@@ -705,16 +716,13 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t ro = (b * a.T + t0 + min(io[r], Lc - 1)) * a.H + h;
-        o.co[r] = a.cum[ro];
-        o.djo[r] = a.wd[ro];
+        o.sc[r] = rsc[ro];
       }
     } else {
 #pragma unroll
       for (int pb = 0; pb < P / 16; ++pb) o.av[pb] = *reinterpret_cast<const RawA*>(arow + 16 * pb + 4 * q);
-      o.ci = a.cum[rowi];
-      o.dj = a.wd[rowi];
+      o.sc[0] = rsc[rowi];
     }
-    o.clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
     // Delta of the next chunk's first token (role 1; a valid row is read on
     // every path and the value is dropped where it does not apply)
     o.wn = a.wd[(b * a.T + min(t0 + L, a.T - 1)) * a.H + h];
@@ -745,19 +753,18 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const bool ok = io[r] < Lc;
-        const float sc = role == 0 ? (ok ? fast_exp((float)o.co[r]) : 0.0f)
-                                   : (ok ? gs * o.djo[r] * fast_exp((float)(o.clast - o.co[r])) : 0.0f);
+        const float sc = ok ? (role == 0 ? o.sc[r] : gs * o.sc[r]) : 0.0f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) ah[kk][r] *= sc;
       }
     } else {
     float scale;
     if (role == 0) {
-      scale = iok ? fast_exp((float)o.ci) : 0.0f;
+      scale = iok ? o.sc[0] : 0.0f;
     } else {
       // abar of the next chunk's first token turns R1's entering state into Ghat_c
       const float gs = c + 1 < a.Nc ? expf(o.wn * o.Ah) : 1.0f;
-      scale = iok ? gs * o.dj * fast_exp((float)(o.clast - o.ci)) : 0.0f;
+      scale = iok ? gs * o.sc[0] : 0.0f;
     }
 #pragma unroll
     for (int pb = 0; pb < P / 16; ++pb) {

@@ -82,6 +82,8 @@ struct BwdArgs {
   // (in the io type: R1 runs the scan kernels of that type)
   float* wd;                // [Bt,T,H] Delta
   double* cum;              // [Bt,T,H] sum of Delta A from the chunk start to the token (inclusive)
+  float* rscale;            // [2,Bt,T,H] row scales of the dC / dB inter-chunk products:
+                            // e^{cum_t} and Delta_t e^{cum_last - cum_t}
   float* dtr1;              // [Bt,T+pad,H] Delta' of R1: d_t at reversed position pad+T-t
   void* r1_x;               // [Bt,T+pad,H,P] io  reversed dy_t / Delta_{t+1}
   void* r1_b;               // [Bt,T+pad,G,N] io  reversed C
