@@ -96,6 +96,30 @@ __device__ __forceinline__ void ldk(const T* p, bool ok, float (&v)[KK]) {
   }
 }
 
+// 16 bytes of io elements (8 bfloat16 or 4 float32) as float32, and back.
+template <typename T>
+__device__ __forceinline__ void ld16_io(const T* p, float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const bf16x8 w = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = (float)w[k];
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st16_io(T* p, const float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    bf16x8 w;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = (bf16)v[k];
+    *reinterpret_cast<bf16x8*>(p) = w;
+  }
+}
+
 // Four consecutive elements to memory in the io type (aligned to 4 elements).
 template <typename T>
 __device__ __forceinline__ void st4_io(T* p, float4 v) {
@@ -184,6 +208,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_delta(BwdArgs a) {
 // io type (R1 runs the scan kernels of that type).  `sh` = log2(P/4).
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_x(BwdArgs a, int sh) {
+  constexpr int EPT = 16 / sizeof(T);   // elements per thread: one 16-byte vector
   const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
   const uint32_t row32 = e >> sh, pq = e & ((1u << sh) - 1u);
   if ((int64_t)row32 >= a.Bt * a.T * a.H) return;
@@ -192,14 +217,16 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_x(BwdArgs a, int sh) {
   const int64_t h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
   const int64_t T1 = a.T + a.pad, tr1 = a.pad + (a.T - 1 - t);
   const int P = a.P;
-  const int64_t rp = (int64_t)row32 * P + 4 * pq;
+  const int64_t rp = (int64_t)row32 * P + EPT * pq;
   const bool has_next = t + 1 < a.T;
   const float wn = a.wd[has_next ? row32 + (uint32_t)a.H : row32];   // a valid row either way
-  const float dn = has_next ? wn : 1.0f;
-  const float4 v = ld4_io<T>(reinterpret_cast<const T*>(a.dy) + rp, true);
-  const float4 r = has_next ? make_float4(v.x / dn, v.y / dn, v.z / dn, v.w / dn)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
-  st4_io<T>(reinterpret_cast<T*>(a.r1_x) + ((b * T1 + tr1) * a.H + h) * P + 4 * pq, r);
+  // dy_t / Delta_{t+1}, as dy_t times the reciprocal (one division per row)
+  const float rn = has_next ? 1.0f / wn : 0.0f;
+  float v[EPT];
+  ld16_io<T>(reinterpret_cast<const T*>(a.dy) + rp, v);
+#pragma unroll
+  for (int k = 0; k < EPT; ++k) v[k] *= rn;
+  st16_io<T>(reinterpret_cast<T*>(a.r1_x) + ((b * T1 + tr1) * a.H + h) * P + EPT * pq, v);
 }
 
 // One thread per four state columns of a (b, t, g) row: R1's B and C (C and
@@ -255,6 +282,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_init_states(BwdArgs a) {
 // Chunk-local inclusive prefix sum of Delta A, in double: one wavefront per
 // (b, c, h).  (Runs after k_bwd_delta, which writes Delta.)
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
+  constexpr int kMaxBlocks = 4;   // 64-token blocks of a chunk (L <= 256)
   const int64_t w = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (w >= a.Bt * a.Nc * a.H) return;
@@ -262,29 +290,39 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
   const int64_t t0 = c * a.L;
   const int Lc = chunk_tokens(a, c);
   const double Ah = (double)a.A[h];
+  // every Delta of the chunk first (tokens past it re-read its last one)
+  float wdv[kMaxBlocks];
+#pragma unroll
+  for (int k = 0; k < kMaxBlocks; ++k)
+    wdv[k] = a.wd[(b * a.T + t0 + min(64 * k + lane, Lc - 1)) * a.H + h];
+  double cv[kMaxBlocks];
   double carry = 0.0;
-  for (int l0 = 0; l0 < Lc; l0 += 64) {
-    const int l = l0 + lane;
-    const int64_t row = (b * a.T + t0 + l) * a.H + h;
-    double v = l < Lc ? (double)a.wd[row] * Ah : 0.0;
+#pragma unroll
+  for (int k = 0; k < kMaxBlocks; ++k) {
+    const int l = 64 * k + lane;
+    double v = l < Lc ? (double)wdv[k] * Ah : 0.0;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const double o = __shfl_up(v, off, 64);
       if (lane >= off) v += o;
     }
     v += carry;
-    if (l < Lc) a.cum[row] = v;
+    cv[k] = v;
+    if (l < Lc) a.cum[(b * a.T + t0 + l) * a.H + h] = v;
     carry = __shfl(v, 63, 64);
   }
   // the row scales of the dC / dB inter-chunk products (the same float
   // operations the products' kernel would apply to the prefix sums)
   const double clast = carry;
   const int64_t n = a.Bt * a.T * a.H;
-  for (int l = lane; l < Lc; l += 64) {
-    const int64_t row = (b * a.T + t0 + l) * a.H + h;
-    const double cv = a.cum[row];   // this lane's own store above
-    a.rscale[row] = fast_exp((float)cv);
-    a.rscale[n + row] = a.wd[row] * fast_exp((float)(clast - cv));
+#pragma unroll
+  for (int k = 0; k < kMaxBlocks; ++k) {
+    const int l = 64 * k + lane;
+    if (l < Lc) {
+      const int64_t row = (b * a.T + t0 + l) * a.H + h;
+      a.rscale[row] = fast_exp((float)cv[k]);
+      a.rscale[n + row] = wdv[k] * fast_exp((float)(clast - cv[k]));
+    }
   }
 }
 
@@ -926,6 +964,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb_reduce(BwdArgs a) {
 // Delta gradient (x . G B) and the per-token part of dD.  `sh` = log2(P/4).
 template <typename T>
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a, int sh) {
+  constexpr int EPT = 16 / sizeof(T);   // elements per thread: one 16-byte vector of each input
   const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
   const uint32_t row32 = e >> sh, pq = e & ((1u << sh) - 1u);
   const bool ok = (int64_t)row32 < a.Bt * a.T * a.H;
@@ -936,24 +975,26 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a, int sh) {
   const int P = a.P;
   const float d = a.wd[rowc];
   const float Dh = a.D ? a.D[h] : 0.0f;
-  const int64_t rp = (int64_t)rowc * P + 4 * pq;
-  const int64_t rpr1 = ((b * (a.T + a.pad) + (a.pad + a.T - 1 - t)) * a.H + h) * P + 4 * pq;
+  const int64_t rp = (int64_t)rowc * P + EPT * pq;
+  const int64_t rpr1 = ((b * (a.T + a.pad) + (a.pad + a.T - 1 - t)) * a.H + h) * P + EPT * pq;
   // threads past the last row read row 0 and store nothing
-  const float4 xv = ld4_io<T>(reinterpret_cast<const T*>(a.x) + rp, true);
-  const float4 dyv = ld4_io<T>(reinterpret_cast<const T*>(a.dy) + rp, true);
-  const float4 gb = ld4_io<T>(reinterpret_cast<const T*>(a.r1_y) + rpr1, true);   // sum_n G[p,n] B_t[n]
-  if (ok)
-    *reinterpret_cast<float4*>(a.dx + rp) =
-        make_float4(__fmaf_rn(Dh, dyv.x, d * gb.x), __fmaf_rn(Dh, dyv.y, d * gb.y),
-                    __fmaf_rn(Dh, dyv.z, d * gb.z), __fmaf_rn(Dh, dyv.w, d * gb.w));
-  float s_din = xv.x * gb.x;
-  s_din = __fmaf_rn(xv.y, gb.y, s_din);
-  s_din = __fmaf_rn(xv.z, gb.z, s_din);
-  s_din = __fmaf_rn(xv.w, gb.w, s_din);
-  float s_dd = dyv.x * xv.x;
-  s_dd = __fmaf_rn(dyv.y, xv.y, s_dd);
-  s_dd = __fmaf_rn(dyv.z, xv.z, s_dd);
-  s_dd = __fmaf_rn(dyv.w, xv.w, s_dd);
+  float xv[EPT], dyv[EPT], gb[EPT];   // gb = sum_n G[p,n] B_t[n]
+  ld16_io<T>(reinterpret_cast<const T*>(a.x) + rp, xv);
+  ld16_io<T>(reinterpret_cast<const T*>(a.dy) + rp, dyv);
+  ld16_io<T>(reinterpret_cast<const T*>(a.r1_y) + rpr1, gb);
+  if (ok) {
+#pragma unroll
+    for (int k = 0; k < EPT; k += 4)
+      *reinterpret_cast<float4*>(a.dx + rp + k) =
+          make_float4(__fmaf_rn(Dh, dyv[k], d * gb[k]), __fmaf_rn(Dh, dyv[k + 1], d * gb[k + 1]),
+                      __fmaf_rn(Dh, dyv[k + 2], d * gb[k + 2]), __fmaf_rn(Dh, dyv[k + 3], d * gb[k + 3]));
+  }
+  float s_din = xv[0] * gb[0];
+#pragma unroll
+  for (int k = 1; k < EPT; ++k) s_din = __fmaf_rn(xv[k], gb[k], s_din);
+  float s_dd = dyv[0] * xv[0];
+#pragma unroll
+  for (int k = 1; k < EPT; ++k) s_dd = __fmaf_rn(dyv[k], xv[k], s_dd);
   const int width = 1 << sh;
   s_din = group_sum(s_din, width);
   s_dd = group_sum(s_dd, width);
@@ -1155,8 +1196,9 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
     case 0:
       hipLaunchKernelGGL(k_bwd_delta, dim3(blocks_of(rows, kBwdThreads)), dim3(kBwdThreads), 0, s,
                          a);
-      hipLaunchKernelGGL(k_bwd_prep_x<T>, dim3(blocks_of(rows * (a.P / 4), kBwdThreads)),
-                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / 4));
+      hipLaunchKernelGGL(k_bwd_prep_x<T>,
+                         dim3(blocks_of(rows * (a.P / (16 / (int)sizeof(T))), kBwdThreads)),
+                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / (16 / (int)sizeof(T))));
       hipLaunchKernelGGL(k_bwd_prep_bc<T>,
                          dim3(blocks_of(a.Bt * a.T * a.G * (int64_t)(a.N / 4), kBwdThreads)),
                          dim3(kBwdThreads), 0, s, a, log2_of(a.N / 4));
@@ -1182,8 +1224,9 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
         default: e = hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_bwd_dx<T>, dim3(blocks_of(rows * (a.P / 4), kBwdThreads)),
-                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / 4));
+      hipLaunchKernelGGL(k_bwd_dx<T>,
+                         dim3(blocks_of(rows * (a.P / (16 / (int)sizeof(T))), kBwdThreads)),
+                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / (16 / (int)sizeof(T))));
       hipLaunchKernelGGL(k_bwd_assemble, dim3((unsigned)(a.Bt * a.Nc * a.H)), dim3(kBwdThreads),
                          0, s, a);
       hipLaunchKernelGGL(k_bwd_reduce_heads, dim3(blocks_of(a.H, kBwdThreads)), dim3(kBwdThreads),
