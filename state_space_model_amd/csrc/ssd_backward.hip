@@ -186,23 +186,6 @@ __device__ __forceinline__ float block_sum(float v, float* wsum) {
 // Phase 0
 // ---------------------------------------------------------------------------
 
-// One thread per (b, t, h) row: Delta and R1's Delta' (d_t at R1 position
-// pad + T - t; the pad and position pad get 0).
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_delta(BwdArgs a) {
-  const uint32_t row32 = blockIdx.x * kBwdThreads + threadIdx.x;
-  if ((int64_t)row32 >= a.Bt * a.T * a.H) return;
-  // rows fit 32 bits (checked on the host): 32-bit divisions
-  const uint32_t H32 = (uint32_t)a.H, T32 = (uint32_t)a.T;
-  const uint32_t bt32 = row32 / H32;
-  const int64_t h = row32 - bt32 * H32, t = bt32 % T32, b = bt32 / T32;
-  const int64_t T1 = a.T + a.pad;
-  const float d = delta_at(a, b, t, h);
-  a.wd[row32] = d;
-  if (t >= 1) a.dtr1[(b * T1 + (a.pad + a.T - t)) * a.H + h] = d;
-  else
-    for (int64_t k = 0; k <= a.pad; ++k) a.dtr1[(b * T1 + k) * a.H + h] = 0.0f;
-}
-
 // One thread per four head columns of a (b, t, h) row: R1's input
 // dy_t / Delta_{t+1} (0 for the last token) at R1 position pad + T-1-t, in the
 // io type (R1 runs the scan kernels of that type).  `sh` = log2(P/4).
@@ -232,8 +215,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_x(BwdArgs a, int sh) {
 // One thread per four state columns of a (b, t, g) row: R1's B and C (C and
 // B, reversed), copied in the io type.  `sh` = log2(N/4).
 template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_bc(BwdArgs a, int sh) {
-  const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
+__device__ __forceinline__ void bwd_prep_bc(const BwdArgs& a, int sh, int64_t bid) {
+  const uint32_t e = (uint32_t)bid * kBwdThreads + threadIdx.x;
   const uint32_t row32 = e >> sh, nq = e & ((1u << sh) - 1u);
   if ((int64_t)row32 >= a.Bt * a.T * a.G) return;
   const uint32_t G32 = (uint32_t)a.G, T32 = (uint32_t)a.T;
@@ -252,8 +235,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_prep_bc(BwdArgs a, int sh) 
 
 // The pad positions of R1 (reversed positions 0 .. pad-1) hold no token.
 template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_zero_pad(BwdArgs a, int64_t per_b) {
-  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+__device__ __forceinline__ void bwd_zero_pad(const BwdArgs& a, int64_t per_b, int64_t bid) {
+  const int64_t e = bid * kBwdThreads + threadIdx.x;
   if (e >= a.Bt * per_b) return;
   const int64_t b = e / per_b, r = e % per_b;
   const int64_t T1 = a.T + a.pad;
@@ -267,8 +250,8 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_zero_pad(BwdArgs a, int64_t
 
 // Initial state of R1: dfinal + dy_{T-1} (x) C_{T-1}.
 template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_init_states(BwdArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+__device__ __forceinline__ void bwd_init_states(const BwdArgs& a, int64_t bid) {
+  const int64_t e = bid * kBwdThreads + threadIdx.x;
   const int P = a.P, N = a.N;
   if (e >= a.Bt * a.H * P * N) return;
   const int64_t n = e % N, p = (e / N) % P, bh = e / ((int64_t)P * N);
@@ -279,51 +262,103 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_init_states(BwdArgs a) {
   a.r1_h0[e] = __fmaf_rn(dyv, cv, a.dfinal ? a.dfinal[e] : 0.0f);
 }
 
-// Chunk-local inclusive prefix sum of Delta A, in double: one wavefront per
-// (b, c, h).  (Runs after k_bwd_delta, which writes Delta.)
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_cum(BwdArgs a) {
-  constexpr int kMaxBlocks = 4;   // 64-token blocks of a chunk (L <= 256)
-  const int64_t w = (int64_t)blockIdx.x * (kBwdThreads / 64) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (w >= a.Bt * a.Nc * a.H) return;
-  const int64_t h = w % a.H, bc = w / a.H, c = bc % a.Nc, b = bc / a.Nc;
-  const int64_t t0 = c * a.L;
+// Delta and R1's Delta' (d_t at R1 position pad + T - t; the pad and
+// position pad get 0), then the chunk-local inclusive prefix sum of Delta A
+// in double and the row scales of the dC / dB inter-chunk products.  One
+// workgroup per (b, c, block of 16 heads): thread (g, hh) forms Delta of
+// tokens 16g .. 16g+15 of head hb + hh and their serial prefix sum (the 16
+// heads of a token are adjacent in memory, so every access is a 64-byte run),
+// then adds the totals of the token groups before it, in order, from LDS.
+__device__ __forceinline__ void bwd_cum_delta(const BwdArgs& a, int64_t bid) {
+  constexpr int kHB = 16, kTG = kBwdThreads / kHB;   // heads per block, token groups (L <= 256)
+  __shared__ double s_tot[kTG][kHB];
+  __shared__ double s_last[kHB];
+  const int hh = threadIdx.x % kHB, g = threadIdx.x / kHB;
+  const int64_t nhb = (a.H + kHB - 1) / kHB;
+  const int64_t hb = (bid % nhb) * kHB, bc = bid / nhb, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t h = min(hb + hh, (int64_t)a.H - 1);   // heads past H repeat the last and store nothing
+  const bool hok = hb + hh < a.H;
+  const int64_t t0 = c * a.L, T1 = a.T + a.pad;
   const int Lc = chunk_tokens(a, c);
   const double Ah = (double)a.A[h];
-  // every Delta of the chunk first (tokens past it re-read its last one)
-  float wdv[kMaxBlocks];
+  float wdv[16];   // tokens past the chunk repeat its last one and store nothing
 #pragma unroll
-  for (int k = 0; k < kMaxBlocks; ++k)
-    wdv[k] = a.wd[(b * a.T + t0 + min(64 * k + lane, Lc - 1)) * a.H + h];
-  double cv[kMaxBlocks];
-  double carry = 0.0;
+  for (int k = 0; k < 16; ++k) wdv[k] = delta_at(a, b, t0 + min(16 * g + k, Lc - 1), h);
 #pragma unroll
-  for (int k = 0; k < kMaxBlocks; ++k) {
-    const int l = 64 * k + lane;
-    double v = l < Lc ? (double)wdv[k] * Ah : 0.0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const double o = __shfl_up(v, off, 64);
-      if (lane >= off) v += o;
+  for (int k = 0; k < 16; ++k) {
+    const int l = 16 * g + k;
+    if (hok && l < Lc) {
+      const int64_t t = t0 + l;
+      a.wd[(b * a.T + t) * a.H + h] = wdv[k];
+      if (t >= 1) {
+        a.dtr1[(b * T1 + (a.pad + a.T - t)) * a.H + h] = wdv[k];
+      } else {
+        for (int64_t z = 0; z <= a.pad; ++z) a.dtr1[(b * T1 + z) * a.H + h] = 0.0f;
+      }
     }
-    v += carry;
-    cv[k] = v;
-    if (l < Lc) a.cum[(b * a.T + t0 + l) * a.H + h] = v;
-    carry = __shfl(v, 63, 64);
   }
-  // the row scales of the dC / dB inter-chunk products (the same float
-  // operations the products' kernel would apply to the prefix sums)
-  const double clast = carry;
+  double cv[16];
+  double run = 0.0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    run += 16 * g + k < Lc ? (double)wdv[k] * Ah : 0.0;
+    cv[k] = run;
+  }
+  s_tot[g][hh] = run;
+  __syncthreads();
+  double off = 0.0;
+  for (int j = 0; j < g; ++j) off += s_tot[j][hh];
+  const int last = Lc - 1;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    cv[k] += off;
+    const int l = 16 * g + k;
+    if (hok && l < Lc) a.cum[(b * a.T + t0 + l) * a.H + h] = cv[k];
+    if (l == last) s_last[hh] = cv[k];
+  }
+  __syncthreads();
+  // the row scales (the same float operations the products' kernel would
+  // apply to the prefix sums)
+  const double clast = s_last[hh];
   const int64_t n = a.Bt * a.T * a.H;
 #pragma unroll
-  for (int k = 0; k < kMaxBlocks; ++k) {
-    const int l = 64 * k + lane;
-    if (l < Lc) {
+  for (int k = 0; k < 16; ++k) {
+    const int l = 16 * g + k;
+    if (hok && l < Lc) {
       const int64_t row = (b * a.T + t0 + l) * a.H + h;
       a.rscale[row] = fast_exp((float)cv[k]);
       a.rscale[n + row] = wdv[k] * fast_exp((float)(clast - cv[k]));
     }
   }
+}
+
+// Phase 0 but R1's input rows: the blocks of one launch are dealt, in order,
+// to Delta and its prefix sums, R1's B and C, R1's pad rows and R1's initial
+// state (independent work; fewer launches).
+struct Prep0Grid {
+  int64_t n_cd, n_bc, n_pad;
+  int64_t per_b;
+  int sh_bc;
+};
+template <typename T>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_prep0(BwdArgs a, Prep0Grid pg) {
+  int64_t bid = blockIdx.x;
+  if (bid < pg.n_cd) {
+    bwd_cum_delta(a, bid);
+    return;
+  }
+  bid -= pg.n_cd;
+  if (bid < pg.n_bc) {
+    bwd_prep_bc<T>(a, pg.sh_bc, bid);
+    return;
+  }
+  bid -= pg.n_bc;
+  if (bid < pg.n_pad) {
+    bwd_zero_pad<T>(a, pg.per_b, bid);
+    return;
+  }
+  bid -= pg.n_pad;
+  bwd_init_states<T>(a, bid);
 }
 
 // ---------------------------------------------------------------------------
@@ -948,9 +983,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
 }
 
 // dC, dB: sums over the head splits of their parts (fixed order).
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb_reduce(BwdArgs a) {
+__device__ __forceinline__ void bwd_dcdb_reduce(const BwdArgs& a, int64_t bid) {
   const int64_t n = a.Bt * a.T * a.G * a.N;
-  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+  const int64_t e = bid * kBwdThreads + threadIdx.x;
   if (e >= 2 * n) return;
   const int role = e >= n ? 1 : 0;
   const int64_t k = e - role * n;
@@ -963,9 +998,9 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_dcdb_reduce(BwdArgs a) {
 // row are adjacent lanes of one wavefront): dx, the input-scale part of the
 // Delta gradient (x . G B) and the per-token part of dD.  `sh` = log2(P/4).
 template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dx(BwdArgs a, int sh) {
+__device__ __forceinline__ void bwd_dx(const BwdArgs& a, int sh, int64_t bid) {
   constexpr int EPT = 16 / sizeof(T);   // elements per thread: one 16-byte vector of each input
-  const uint32_t e = blockIdx.x * kBwdThreads + threadIdx.x;
+  const uint32_t e = (uint32_t)bid * kBwdThreads + threadIdx.x;
   const uint32_t row32 = e >> sh, pq = e & ((1u << sh) - 1u);
   const bool ok = (int64_t)row32 < a.Bt * a.T * a.H;
   const uint32_t rowc = ok ? row32 : 0u;
@@ -1138,26 +1173,52 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
 }
 
 // dA, ddt_bias, dD: sums over the batch and the chunks of the parts (fixed order).
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_reduce_heads(BwdArgs a) {
-  const int64_t h = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+__device__ __forceinline__ void bwd_reduce_heads(const BwdArgs& a, int64_t bid) {
+  const int64_t h = bid * kBwdThreads + threadIdx.x;
   if (h >= a.H) return;
   const int64_t n = a.Bt * a.Nc;
   float s[3] = {0.0f, 0.0f, 0.0f};
-  for (int64_t k = 0; k < n; ++k)
-    for (int m = 0; m < 3; ++m) s[m] += a.part[(m * n + k) * a.H + h];
+  // 16 parts of each sum in flight, added in order (rows past n re-read the last)
+  for (int64_t k0 = 0; k0 < n; k0 += 16) {
+    float v[3][16];
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[m][k] = a.part[(m * n + min(k0 + k, n - 1)) * a.H + h];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k0 + k < n)
+#pragma unroll
+        for (int m = 0; m < 3; ++m) s[m] += v[m][k];
+  }
   a.dA[h] = s[0];
   if (a.ddt_bias_out) a.ddt_bias_out[h] = s[1];
   if (a.dD) a.dD[h] = s[2];
 }
 
 // dh0 = abar_0 * (final state of R1).
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dh0(BwdArgs a) {
-  const int64_t e = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+__device__ __forceinline__ void bwd_dh0(const BwdArgs& a, int64_t bid) {
+  const int64_t e = bid * kBwdThreads + threadIdx.x;
   const int64_t PN = (int64_t)a.P * a.N;
   if (e >= a.Bt * a.H * PN) return;
   const int64_t bh = e / PN, h = bh % a.H, b = bh / a.H;
   const float ab0 = expf(a.wd[(b * a.T) * a.H + h] * a.A[h]);
   a.dh0[e] = ab0 * a.r1_final[e];
+}
+
+// Independent element-wise work in one launch each: dx (with the per-token
+// parts of the Delta and D gradients) beside the sum of the dC / dB head-split
+// parts; the per-head sums beside d(initial state).
+template <typename T>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dx_reduce(BwdArgs a, int sh, int64_t n_dx) {
+  const int64_t bid = blockIdx.x;
+  if (bid < n_dx) bwd_dx<T>(a, sh, bid);
+  else bwd_dcdb_reduce(a, bid - n_dx);
+}
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_finish(BwdArgs a, int64_t n_heads) {
+  const int64_t bid = blockIdx.x;
+  if (bid < n_heads) bwd_reduce_heads(a, bid);
+  else bwd_dh0(a, bid - n_heads);
 }
 
 inline unsigned blocks_of(int64_t n, int64_t per) { return (unsigned)((n + per - 1) / per); }
@@ -1182,10 +1243,6 @@ hipError_t launch_mix_dcdb(const BwdArgs& a, hipStream_t s) {
     case 128: hipLaunchKernelGGL((k_bwd_dcdb<T, P, 4>), grid, dim3(kBwdThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  if (a.HSD > 1)
-    hipLaunchKernelGGL(k_bwd_dcdb_reduce,
-                       dim3(blocks_of(2 * a.Bt * a.T * a.G * (int64_t)a.N, kBwdThreads)),
-                       dim3(kBwdThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -1193,27 +1250,23 @@ template <typename T>
 hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
   const int64_t rows = a.Bt * a.T * a.H;
   switch (phase) {
-    case 0:
-      hipLaunchKernelGGL(k_bwd_delta, dim3(blocks_of(rows, kBwdThreads)), dim3(kBwdThreads), 0, s,
-                         a);
+    case 0: {
+      Prep0Grid pg;
+      pg.n_cd = a.Bt * a.Nc * ((a.H + 15) / 16);
+      pg.n_bc = blocks_of(a.Bt * a.T * a.G * (int64_t)(a.N / 4), kBwdThreads);
+      pg.sh_bc = log2_of(a.N / 4);
+      const int64_t hp = a.pad * a.H * a.P, gn = a.pad * a.G * a.N;
+      pg.per_b = hp > gn ? hp : gn;
+      pg.n_pad = a.pad > 0 ? blocks_of(a.Bt * pg.per_b, kBwdThreads) : 0;
+      const int64_t n_init = blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads);
+      hipLaunchKernelGGL(k_bwd_prep0<T>, dim3((unsigned)(pg.n_cd + pg.n_bc + pg.n_pad + n_init)),
+                         dim3(kBwdThreads), 0, s, a, pg);
+      // R1's input rows read Delta of the next token
       hipLaunchKernelGGL(k_bwd_prep_x<T>,
                          dim3(blocks_of(rows * (a.P / (16 / (int)sizeof(T))), kBwdThreads)),
                          dim3(kBwdThreads), 0, s, a, log2_of(a.P / (16 / (int)sizeof(T))));
-      hipLaunchKernelGGL(k_bwd_prep_bc<T>,
-                         dim3(blocks_of(a.Bt * a.T * a.G * (int64_t)(a.N / 4), kBwdThreads)),
-                         dim3(kBwdThreads), 0, s, a, log2_of(a.N / 4));
-      if (a.pad > 0) {
-        const int64_t hp = a.pad * a.H * a.P, gn = a.pad * a.G * a.N;
-        const int64_t per_b = hp > gn ? hp : gn;
-        hipLaunchKernelGGL(k_bwd_zero_pad<T>, dim3(blocks_of(a.Bt * per_b, kBwdThreads)),
-                           dim3(kBwdThreads), 0, s, a, per_b);
-      }
-      hipLaunchKernelGGL(k_bwd_init_states<T>,
-                         dim3(blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads)),
-                         dim3(kBwdThreads), 0, s, a);
-      hipLaunchKernelGGL(k_bwd_cum, dim3(blocks_of(a.Bt * a.Nc * a.H, kBwdThreads / 64)),
-                         dim3(kBwdThreads), 0, s, a);
       break;
+    }
     case 1: {
       hipError_t e;
       switch (a.P) {
@@ -1224,16 +1277,20 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
         default: e = hipErrorInvalidValue;
       }
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(k_bwd_dx<T>,
-                         dim3(blocks_of(rows * (a.P / (16 / (int)sizeof(T))), kBwdThreads)),
-                         dim3(kBwdThreads), 0, s, a, log2_of(a.P / (16 / (int)sizeof(T))));
+      {
+        const int64_t n_dx = blocks_of(rows * (a.P / (16 / (int)sizeof(T))), kBwdThreads);
+        const int64_t n_red = a.HSD > 1 ? blocks_of(2 * a.Bt * a.T * a.G * (int64_t)a.N, kBwdThreads) : 0;
+        hipLaunchKernelGGL(k_bwd_dx_reduce<T>, dim3((unsigned)(n_dx + n_red)), dim3(kBwdThreads), 0,
+                           s, a, log2_of(a.P / (16 / (int)sizeof(T))), n_dx);
+      }
       hipLaunchKernelGGL(k_bwd_assemble, dim3((unsigned)(a.Bt * a.Nc * a.H)), dim3(kBwdThreads),
                          0, s, a);
-      hipLaunchKernelGGL(k_bwd_reduce_heads, dim3(blocks_of(a.H, kBwdThreads)), dim3(kBwdThreads),
-                         0, s, a);
-      if (a.dh0)
-        hipLaunchKernelGGL(k_bwd_dh0, dim3(blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads)),
-                           dim3(kBwdThreads), 0, s, a);
+      {
+        const int64_t n_heads = blocks_of(a.H, kBwdThreads);
+        const int64_t n_dh0 = a.dh0 ? blocks_of(a.Bt * a.H * (int64_t)a.P * a.N, kBwdThreads) : 0;
+        hipLaunchKernelGGL(k_bwd_finish, dim3((unsigned)(n_heads + n_dh0)), dim3(kBwdThreads), 0, s,
+                           a, n_heads);
+      }
       break;
     }
     default:
