@@ -355,7 +355,7 @@ ssd_status plan_backward(const ssd_scan_desc* d, BwdPlan* pl) {
   sizes[kDbcPart] = pl->HSD > 1 ? 2 * (size_t)pl->HSD * nbc * 4 : 0;
   sizes[kDdin] = ndt * 4;
   sizes[kDdp] = ndt * 4;
-  sizes[kPart] = 3 * (size_t)(Bt * Nc * H) * 4;
+  sizes[kPart] = 4 * (size_t)(Bt * Nc * H) * 4;
   size_t at = 0;
   for (int k = 0; k < kNumRegions; ++k) {
     pl->off[k] = at;

@@ -684,7 +684,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
   const int64_t he = min(hb + (int64_t)a.hpwd, (g + 1) * hpg);
   const int64_t PN = (int64_t)P * N;
   const int64_t BtT = a.Bt * a.T;
-  float* uvo = a.uv + ((int64_t)(role * a.NS + ns) * BtT + b * a.T + t0) * a.H;
+  // u / v are stored token-contiguous per (b, h): [2][NS][Bt,H,T]
+  float* uvo = a.uv + (int64_t)(role * a.NS + ns) * BtT * a.H + b * a.H * a.T + t0;
   // Z = H_c (role 0) or Ghat_c / abar (role 1; null for the last chunk without dfinal)
   auto zptr = [&](int64_t h) -> const float* {
     if (role == 0) return a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
@@ -879,7 +880,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     if (r16 == 0) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (io[r] < Lc) uvo[(int64_t)io[r] * a.H + h] = ds[r];
+        if (io[r] < Lc) uvo[h * a.T + io[r]] = ds[r];
     }
 #pragma unroll
     for (int k = 0; k < KK; ++k) acc[k] += ah[k];
@@ -916,7 +917,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
     if (role == 0) {
       // dC_i += sum_{j <= i} M[i][j] B_j
       const int kb1 = min(4 * (rb + 1), kend);
-#pragma unroll 4
       for (int kb = hsd; kb < kb1; kb += a.HSD) {
         float4 m4 = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int s = 0; s < a.HS; ++s) {
@@ -941,7 +941,6 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3))
       }
     } else {
       // dB_j += sum_{i >= j} M[i][j] C_i
-#pragma unroll 4
       for (int kb = 4 * rb + hsd; kb < kend; kb += a.HSD) {
         float m4[4] = {0.f, 0.f, 0.f, 0.f};
         for (int s = 0; s < a.HS; ++s) {
@@ -1034,8 +1033,10 @@ __device__ __forceinline__ void bwd_dx(const BwdArgs& a, int sh, int64_t bid) {
   s_din = group_sum(s_din, width);
   s_dd = group_sum(s_dd, width);
   if (ok && pq == 0) {
-    a.ddin[row32] = s_din;
-    a.dDp[row32] = s_dd;
+    // token-contiguous per (b, h), as the assembly reads them
+    const int64_t o = (b * a.H + h) * a.T + t;
+    a.ddin[o] = s_din;
+    a.dDp[o] = s_dd;
   }
 }
 
@@ -1045,7 +1046,7 @@ __device__ __forceinline__ void bwd_dx(const BwdArgs& a, int sh, int64_t bid) {
 // Every global load is issued before the first value is used (rows, blocks
 // and splits that do not apply read a valid clamped address and are dropped
 // by a select), so the workgroup waits for memory once instead of once per
-// dependent step.
+// dependent step; the chunk-boundary dot <Ghat_c, H_c> comes formed.
 __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
   constexpr int kMaxNB = 4;   // 64-token blocks of a chunk (L <= 256)
   constexpr int kMaxNS = 2;   // 64-column splits of N (N <= 128)
@@ -1060,10 +1061,10 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
   const int lc = ok ? l : 0;
   const int64_t row = (b * a.T + t0 + lc) * a.H + h;
   const int64_t BtT = a.Bt * a.T;
-  const int64_t PN = (int64_t)a.P * a.N;
 
   // per-token and per-head scalars
-  const float dt_raw = a.dt[row], wd_t = a.wd[row], ddin_t = a.ddin[row], dDp_t = a.dDp[row];
+  const int64_t rowt = (b * a.H + h) * a.T + t0 + lc;   // the token-contiguous buffers
+  const float dt_raw = a.dt[row], wd_t = a.wd[row], ddin_t = a.ddin[rowt], dDp_t = a.dDp[rowt];
   const float Ah = a.A[h];
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   const double clast = a.cum[(b * a.T + t0 + Lc - 1) * a.H + h];
@@ -1087,44 +1088,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < kMaxNS; ++k) {
     const int ns = min(k, a.NS - 1);
-    uvv[k][0] = a.uv[((int64_t)ns * BtT + b * a.T + t0 + lc) * a.H + h];
-    uvv[k][1] = a.uv[((int64_t)(a.NS + ns) * BtT + b * a.T + t0 + lc) * a.H + h];
+    uvv[k][0] = a.uv[(int64_t)ns * BtT * a.H + rowt];
+    uvv[k][1] = a.uv[(int64_t)(a.NS + ns) * BtT * a.H + rowt];
   }
-  // e^{cum_last} <Ghat_c, H_c>: Ghat_c is R1's state at the next chunk (times
-  // that chunk's first abar) or dfinal for the last chunk; without either the
-  // term is 0 (the loads then read H_c twice)
-  const float* Hc = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
-  const float* Gh = has_next ? a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN
-                             : (a.dfinal ? a.dfinal + (b * a.H + h) * PN : nullptr);
-  const bool has_g = Gh != nullptr;
-  float sc = 0.0f;
-  {
-    // float4 vectors, eight of each operand in flight per thread; vectors past
-    // the state re-read its last one and are dropped
-    const float4* g4 = reinterpret_cast<const float4*>(has_g ? Gh : Hc);
-    const float4* h4 = reinterpret_cast<const float4*>(Hc);
-    const int n4 = (int)(PN / 4);
-    for (int e0 = 0; e0 < n4; e0 += 8 * kBwdThreads) {
-      float4 gv[8], hv[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int e = min(e0 + k * kBwdThreads + l, n4 - 1);
-        gv[k] = g4[e];
-        hv[k] = h4[e];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (e0 + k * kBwdThreads + l < n4) {
-          sc = __fmaf_rn(gv[k].x, hv[k].x, sc);
-          sc = __fmaf_rn(gv[k].y, hv[k].y, sc);
-          sc = __fmaf_rn(gv[k].z, hv[k].z, sc);
-          sc = __fmaf_rn(gv[k].w, hv[k].w, sc);
-        }
-      }
-    }
-    if (!has_g) sc = 0.0f;
-  }
-
+  // <Ghat_c, H_c>, formed beside dx (bwd_ghat_dot)
+  const int64_t nbch = a.Bt * a.Nc * a.H;
+  float sc = a.part[3 * nbch + (b * a.Nc + c) * a.H + h];
   float dv = 0.0f, uu = 0.0f, vv = 0.0f;
   if (ok) {
     // R_t = sum_{s<t} (column sum of s below the diagonal - row sum of s left of it)
@@ -1144,7 +1113,6 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_assemble(BwdArgs a) {
   const float inc_v = block_inclusive_scan(vv, s_w);
   const float inc_u = block_inclusive_scan(uu, s_w);
   const float tot_u = block_sum(uu, s_w);
-  sc = block_sum(sc, s_w);
   const float gs = has_next ? expf(wd_next * Ah) : 1.0f;
   sc *= gs * (float)exp(clast);
 
@@ -1206,12 +1174,63 @@ __device__ __forceinline__ void bwd_dh0(const BwdArgs& a, int64_t bid) {
   a.dh0[e] = ab0 * a.r1_final[e];
 }
 
-// Independent element-wise work in one launch each: dx (with the per-token
-// parts of the Delta and D gradients) beside the sum of the dC / dB head-split
-// parts; the per-head sums beside d(initial state).
+// <Ghat_c, H_c> of one (b, c, h), for the assembly of the decay gradient:
+// Ghat_c is R1's state at the next chunk (times that chunk's first abar, which
+// the assembly applies) or dfinal for the last chunk; without either the term
+// is 0 (the loads then read H_c twice).  Stored after the three parts.
+__device__ __forceinline__ void bwd_ghat_dot(const BwdArgs& a, int64_t bid) {
+  __shared__ float s_w[kBwdThreads / 64];
+  const int l = threadIdx.x;
+  const int64_t h = bid % a.H, bc = bid / a.H, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t PN = (int64_t)a.P * a.N;
+  const bool has_next = c + 1 < a.Nc;
+  const float* Hc = a.fwd_state + ((b * a.H + h) * a.Nc + c) * PN;
+  const float* Gh = has_next ? a.r1_state + ((b * a.H + h) * a.Nc + (a.Nc - 1 - c)) * PN
+                             : (a.dfinal ? a.dfinal + (b * a.H + h) * PN : nullptr);
+  const bool has_g = Gh != nullptr;
+  float sc = 0.0f;
+  {
+    // float4 vectors, eight of each operand in flight per thread; vectors past
+    // the state re-read its last one and are dropped
+    const float4* g4 = reinterpret_cast<const float4*>(has_g ? Gh : Hc);
+    const float4* h4 = reinterpret_cast<const float4*>(Hc);
+    const int n4 = (int)(PN / 4);
+    for (int e0 = 0; e0 < n4; e0 += 8 * kBwdThreads) {
+      float4 gv[8], hv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int e = min(e0 + k * kBwdThreads + l, n4 - 1);
+        gv[k] = g4[e];
+        hv[k] = h4[e];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (e0 + k * kBwdThreads + l < n4) {
+          sc = __fmaf_rn(gv[k].x, hv[k].x, sc);
+          sc = __fmaf_rn(gv[k].y, hv[k].y, sc);
+          sc = __fmaf_rn(gv[k].z, hv[k].z, sc);
+          sc = __fmaf_rn(gv[k].w, hv[k].w, sc);
+        }
+      }
+    }
+    if (!has_g) sc = 0.0f;
+  }
+  sc = block_sum(sc, s_w);
+  if (l == 0) a.part[3 * a.Bt * a.Nc * a.H + bid] = sc;
+}
+
+// Independent work in one launch each: the chunk-boundary dots, dx (with the
+// per-token parts of the Delta and D gradients) and the sum of the dC / dB
+// head-split parts; the per-head sums beside d(initial state).
 template <typename T>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_dx_reduce(BwdArgs a, int sh, int64_t n_dx) {
-  const int64_t bid = blockIdx.x;
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_dx_reduce(BwdArgs a, int sh, int64_t n_dot,
+                                                               int64_t n_dx) {
+  int64_t bid = blockIdx.x;
+  if (bid < n_dot) {
+    bwd_ghat_dot(a, bid);
+    return;
+  }
+  bid -= n_dot;
   if (bid < n_dx) bwd_dx<T>(a, sh, bid);
   else bwd_dcdb_reduce(a, bid - n_dx);
 }
@@ -1280,8 +1299,10 @@ hipError_t launch_phase(const BwdArgs& a, int phase, hipStream_t s) {
       {
         const int64_t n_dx = blocks_of(rows * (a.P / (16 / (int)sizeof(T))), kBwdThreads);
         const int64_t n_red = a.HSD > 1 ? blocks_of(2 * a.Bt * a.T * a.G * (int64_t)a.N, kBwdThreads) : 0;
-        hipLaunchKernelGGL(k_bwd_dx_reduce<T>, dim3((unsigned)(n_dx + n_red)), dim3(kBwdThreads), 0,
-                           s, a, log2_of(a.P / (16 / (int)sizeof(T))), n_dx);
+        const int64_t n_dot = a.Bt * a.Nc * a.H;
+        hipLaunchKernelGGL(k_bwd_dx_reduce<T>, dim3((unsigned)(n_dot + n_dx + n_red)),
+                           dim3(kBwdThreads), 0, s, a, log2_of(a.P / (16 / (int)sizeof(T))), n_dot,
+                           n_dx);
       }
       hipLaunchKernelGGL(k_bwd_assemble, dim3((unsigned)(a.Bt * a.Nc * a.H)), dim3(kBwdThreads),
                          0, s, a);

@@ -99,11 +99,11 @@ struct BwdArgs {
   float* mix;               // [Bt,Nc,G,HS,LP,LP] per head split: sum_h (dy x^T) o decay o Delta_j
   float* qrow;              // [Bt,Nc,H,NB,NB,2,64] row sums of the decay-gradient products
   float* qcol;              // [Bt,Nc,H,NB,NB,2,64] column sums of the same
-  float* uv;                // [2][NS][Bt,T,H] per-token state terms of the decay gradient
+  float* uv;                // [2][NS][Bt,H,T] per-token state terms of the decay gradient
   float* dbc_part;          // [2][HSD][Bt,T,G,N] head-split parts of dC, dB (HSD > 1)
-  float* ddin;              // [Bt,T,H]  x_t . (sum_n G B)
-  float* dDp;               // [Bt,T,H]  dy_t . x_t
-  float* part;              // [3][Bt,Nc,H] parts of dA, ddt_bias, dD
+  float* ddin;              // [Bt,H,T]  x_t . (sum_n G B)
+  float* dDp;               // [Bt,H,T]  dy_t . x_t
+  float* part;              // [4][Bt,Nc,H] parts of dA, ddt_bias, dD; <Ghat_c, H_c>
   // gradients
   float* dx;                // [Bt,T,H,P]
   float* ddt;               // [Bt,T,H]
