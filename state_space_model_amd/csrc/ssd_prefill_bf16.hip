@@ -79,6 +79,35 @@ __device__ __forceinline__ void pin(bf16x8& v) {
 }
 __device__ __forceinline__ void st8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 __device__ __forceinline__ bf16x4 ld4b(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+
+// x of a chunk sits in LDS row-major, x[token][p] with row stride P + 8, and
+// the matrix-core operands that contract over tokens (x^T rows p, k = token)
+// are read with the transposing LDS read ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane j addresses 4 elements and receives element j % 4
+// of the vectors addressed by lanes j / 4, 4 + j / 4, 8 + j / 4, 12 + j / 4
+// (checked on gfx950 with an in-bounds probe of every lane).  So when lane j
+// of group q addresses x[t + j / 4][p0 + 4 (j % 4)], it receives
+// x[t .. t+3][p0 + j]: the operand layout of lane (row p0 + j, k-slots of
+// group q).
+constexpr int x_row_stride(int P) { return P + 8; }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+// x^T[p0 + j][t .. t+3] for lane j of its 16-lane group (t: the group's first token)
+template <int P>
+__device__ __forceinline__ bf16x4 xt_frag4(const bf16* s_x, int t, int p0, int lane) {
+  const int j = lane & 15;
+  return lds_read_tr4(s_x + (t + (j >> 2)) * x_row_stride(P) + p0 + 4 * (j & 3));
+}
+// x^T[p0 + j][t .. t+7] (the 8 k-slots of a 32-deep operand)
+template <int P>
+__device__ __forceinline__ bf16x8 xt_frag8(const bf16* s_x, int t, int p0, int lane) {
+  const bf16x4 lo = xt_frag4<P>(s_x, t, p0, lane), hi = xt_frag4<P>(s_x, t + 4, p0, lane);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
 __device__ __forceinline__ void st4b(bf16* p, bf16x4 v) { *reinterpret_cast<bf16x4*>(p) = v; }
 
 __device__ __forceinline__ bf16x8 cat(bf16x4 lo, bf16x4 hi) {
@@ -164,9 +193,8 @@ inline int cb_tiles(const ScanArgs& a) {
 // x of one chunk, in blocks of 8 token rows x CW head columns (CW = 8, or 4
 // when the workgroup has threads enough for the smaller blocks): block id ->
 // token block id / (P/CW), column block id % (P/CW).  NXB blocks per thread
-// cover LMAX rows.  Rows past the chunk's end read its last row and are
-// zeroed when stored: a select on loaded data right after the loads would
-// make the compiler wait for them there.
+// cover LMAX rows.  Rows past the chunk's end repeat its last row (finite
+// values: they meet only zero scores and zero state weights).
 template <int P, int LMAX, int NTH = kThreads>
 struct XStage {
   static constexpr int CW = (LMAX / 8) * (P / 8) >= NTH ? 8 : 4;
@@ -177,14 +205,11 @@ struct XStage {
   vrow v[NXB][8];
   int Lc = 0;
 
-  static_assert((LMAX / 8) % 8 == 0, "token blocks in groups of 8");
-  // block id -> (token block, column block): 8 consecutive ids take 8
-  // consecutive token blocks of one column block, so the 8 lanes the LDS
-  // serves together store x^T rows' 16-byte units side by side (all banks)
+  // block id -> (token block, column block), column blocks fastest: the
+  // lanes of a token block load and store whole rows
   __device__ __forceinline__ static void block_of(int id, int& lb, int& cb) {
-    const int g8 = id >> 3;
-    cb = g8 % NCB;
-    lb = (g8 / NCB) * 8 + (id & 7);
+    cb = id % NCB;
+    lb = id / NCB;
   }
 
   __device__ __forceinline__ void load(const ScanArgs& a, int64_t b, int64_t c, int64_t h) {
@@ -203,9 +228,9 @@ struct XStage {
             off32(xg, (uint32_t)min(8 * lb + r, Lc - 1) * xs + CW * cb));
     }
   }
-  // x^T[p][l] into s_xt (row stride XTS), zero past the chunk
-  __device__ __forceinline__ void store(bf16* s_xt) {
-    constexpr int XTS = LMAX + 8;
+  // x[l][p] into s_x (row stride x_row_stride(P))
+  __device__ __forceinline__ void store(bf16* s_x) {
+    constexpr int XRS = x_row_stride(P);
     const int tid = opaque_tid();
 #pragma unroll
     for (int i = 0; i < NXB; ++i) {
@@ -213,16 +238,8 @@ struct XStage {
       if (id < NBLK) {
         int lb, cb;
         block_of(id, lb, cb);
-        bool in[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) in[r] = 8 * lb + r < Lc;
-#pragma unroll
-        for (int cc = 0; cc < CW; ++cc) {
-          bf16x8 col;
-#pragma unroll
-          for (int r = 0; r < 8; ++r) col[r] = in[r] ? v[i][r][cc] : (bf16)0.0f;
-          st8(s_xt + (CW * cb + cc) * XTS + 8 * lb, col);
-        }
+        for (int r = 0; r < 8; ++r) *reinterpret_cast<vrow*>(s_x + (8 * lb + r) * XRS + CW * cb) = v[i][r];
       }
     }
   }
@@ -338,7 +355,7 @@ __device__ __forceinline__ int col_tile_of(int wave, int k) {
 // a 16-key remainder and the diagonal tile through v_mfma_f32_16x16x16_bf16
 // (lane: keys 4q ..).
 //   s_h   bf16(h_{c-1})[p][n] (row stride N + 8): the inter-chunk operand
-//   s_xt  bf16 x^T[p][j]     (row stride LMAX + 8), zero past the chunk
+//   s_xt  bf16 x[j][p]       (row stride P + 8), read transposed (xt_frag4/8)
 //   s_d, s_cum, s_w: Delta, cum and the per-tile decay tables of the chunk
 // S (C B^T, bfloat16) and C come from global memory (L2: shared by all heads
 // of a group).  The S rows of every 32-key step a wavefront needs are
@@ -358,7 +375,7 @@ struct ChunkOut {
   // 32-key steps before the wavefront's tiles: tile w has w/2, and with a
   // second tile 2NW-1-w the two add up to NW-1
   static constexpr int NS = CT == 2 ? NW - 1 : (NW - 1) / 2;
-  static constexpr int XTS = LMAX + 8, HS = N + 8;
+  static constexpr int HS = N + 8;
 
   const ScanArgs& a;
   int64_t b, c, h, g;
@@ -532,7 +549,7 @@ struct ChunkOut {
           m[7] = (bf16)__fmul_rn((float)st[7], w1.w);
 #pragma unroll
           for (int pt = 0; pt < TP; ++pt)
-            acc[pt] = mma(ld8(s_xt + (16 * pt + r16) * XTS + k0), m, acc[pt]);
+            acc[pt] = mma(xt_frag8<P>(s_xt, 32 * ks + 8 * q, 16 * pt, lane), m, acc[pt]);
         }
       }
       if (I & 1) {   // the key tile just before the diagonal one
@@ -546,7 +563,7 @@ struct ChunkOut {
         m[3] = (bf16)__fmul_rn((float)st[3], w.w);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-          acc[pt] = mma16(ld4b(s_xt + (16 * pt + r16) * XTS + k0), m, acc[pt]);
+          acc[pt] = mma16(xt_frag4<P>(s_xt, k0, 16 * pt, lane), m, acc[pt]);
       }
       // decay from the reference token to the query
       const float cum_i = s_cum[ri];
@@ -582,7 +599,7 @@ struct ChunkOut {
         m[3] = dec(mk[3], (float)st[3], cj.w, dj.w);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
-          const bf16x4 xd = ld4b(s_xt + (16 * pt + r16) * XTS + j0);
+          const bf16x4 xd = xt_frag4<P>(s_xt, j0, 16 * pt, lane);
           acc[pt] = mma16(xd, m, acc[pt]);
           // the skip term D x of the tile's own tokens, on the same x^T fragment
           acc[pt] = mma16(xd, e1, acc[pt]);
@@ -802,13 +819,13 @@ __device__ __forceinline__ void chunk_delta_cumsum_wide(const ScanArgs& a, int64
 template <int P, int N, int LMAX, int VAR>
 __global__ __launch_bounds__(2 * LMAX) __attribute__((amdgpu_waves_per_eu(LMAX <= 256 ? 4 : 2)))
 void k_chunk_out_bf16(ScanArgs a) {
-  constexpr int XTS = LMAX + 8, HS = N + 8;
+  constexpr int HS = N + 8;
   constexpr int NTH = 2 * LMAX, NW = NTH / 64;
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
   __shared__ float s_wsum[4];
   __shared__ __attribute__((aligned(16))) float s_w[tile_table_size(LMAX) + 4];
-  __shared__ __attribute__((aligned(16))) bf16 s_xt[P * XTS];
+  __shared__ __attribute__((aligned(16))) bf16 s_xt[LMAX * x_row_stride(P)];
   __shared__ __attribute__((aligned(16))) bf16 s_h[P * HS];
 
   const int tid = threadIdx.x;
@@ -1010,11 +1027,11 @@ __device__ __forceinline__ void state_bt_load(const ScanArgs& a, int64_t b, int6
   for (int ks = 0; ks < LMAX / 32; ++ks) bt[ks] = ld8(off32(btc, row + 32 * min(ks, nks - 1)));
 }
 
-template <int LMAX, int TPW>
+template <int P, int LMAX, int TPW>
 __device__ __forceinline__ void state_tiles(const bf16x8 (&bt)[LMAX / 32], int pt0, int Lc,
                                             const bf16* s_xt, const float* s_ws,
                                             f32x4 (&t)[TPW]) {
-  constexpr int NKS = LMAX / 32, XTS = LMAX + 8;
+  constexpr int NKS = LMAX / 32;
   const int nks = (Lc + 31) / 32;
   const int lane = opaque_tid() & 63, q = lane >> 4, r16 = lane & 15;
 #pragma unroll
@@ -1026,7 +1043,7 @@ __device__ __forceinline__ void state_tiles(const bf16x8 (&bt)[LMAX / 32], int p
       const bf16x8 bw = scale8(bt[ks], ld4(&s_ws[l0]), ld4(&s_ws[l0 + 4]));
 #pragma unroll
       for (int ip = 0; ip < TPW; ++ip)
-        t[ip] = mma(bw, ld8(s_xt + (16 * (pt0 + ip) + r16) * XTS + l0), t[ip]);
+        t[ip] = mma(bw, xt_frag8<P>(s_xt, l0, 16 * (pt0 + ip), lane), t[ip]);
     }
   }
 }
@@ -1048,13 +1065,13 @@ struct StateSplit {
 template <int P, int N>
 __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void k_chunk_state_bf16(ScanArgs a) {
-  constexpr int LMAX = 256, NTH = kOutThreads, XTS = LMAX + 8;
+  constexpr int LMAX = 256, NTH = kOutThreads;
   using SP = StateSplit<P, N>;
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[LMAX];
   __shared__ __attribute__((aligned(16))) float s_ws[LMAX];
   __shared__ float s_wsum[4];
-  __shared__ __attribute__((aligned(16))) bf16 s_xt[P * XTS];
+  __shared__ __attribute__((aligned(16))) bf16 s_xt[LMAX * x_row_stride(P)];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1076,7 +1093,7 @@ void k_chunk_state_bf16(ScanArgs a) {
   __syncthreads();
 
   f32x4 t[SP::TPW];
-  state_tiles<LMAX, SP::TPW>(bt, pt0, Lc, s_xt, s_ws, t);
+  state_tiles<P, LMAX, SP::TPW>(bt, pt0, Lc, s_xt, s_ws, t);
   // lane holds S[n = 16 nt + 4q + r][p = 16 (pt0 + ip) + r16]: 4 consecutive n of one p
   const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
   float* out = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
@@ -1108,14 +1125,14 @@ __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4))
 void k_chain_bf16(ScanArgs a) {
   constexpr int NTH = kOutThreads, NW = kOutWaves;
   constexpr int TN = StateSplit<P, N>::TN, TPW = StateSplit<P, N>::TPW;
-  constexpr int XTS = LMAX + 8, HS = N + 8;
+  constexpr int HS = N + 8;
   using Out = ChunkOut<P, N, LMAX, NW, VAR, false>;
   __shared__ __attribute__((aligned(16))) float s_d[2][LMAX];
   __shared__ __attribute__((aligned(16))) float s_cum[2][LMAX];
   __shared__ __attribute__((aligned(16))) float s_ws[LMAX];
   __shared__ float s_wsum[4];
   __shared__ __attribute__((aligned(16))) float s_w[tile_table_size(LMAX) + 4];
-  __shared__ __attribute__((aligned(16))) bf16 s_xt[P * XTS];
+  __shared__ __attribute__((aligned(16))) bf16 s_xt[LMAX * x_row_stride(P)];
   __shared__ __attribute__((aligned(16))) bf16 s_h[P * HS];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1198,7 +1215,7 @@ void k_chain_bf16(ScanArgs a) {
       xs.load(a, b, next ? c + 1 : c, h);
       out.store_pending();
       f32x4 t[TPW];
-      state_tiles<LMAX, TPW>(bt, pt0, Lc, s_xt, s_ws, t);
+      state_tiles<P, LMAX, TPW>(bt, pt0, Lc, s_xt, s_ws, t);
 #pragma unroll
       for (int ip = 0; ip < TPW; ++ip)
 #pragma unroll
