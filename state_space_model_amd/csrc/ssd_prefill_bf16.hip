@@ -80,7 +80,7 @@ __device__ __forceinline__ void pin(bf16x8& v) {
 __device__ __forceinline__ void st8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
 __device__ __forceinline__ bf16x4 ld4b(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
 
-// x of a chunk sits in LDS row-major, x[token][p] with row stride P + 8, and
+// x of a chunk sits in LDS row-major, x[token][p] with row stride P + 16, and
 // the matrix-core operands that contract over tokens (x^T rows p, k = token)
 // are read with the transposing LDS read ds_read_b64_tr_b16: within each
 // group of 16 lanes, lane j addresses 4 elements and receives element j % 4
@@ -89,7 +89,7 @@ __device__ __forceinline__ bf16x4 ld4b(const bf16* p) { return *reinterpret_cast
 // of group q addresses x[t + j / 4][p0 + 4 (j % 4)], it receives
 // x[t .. t+3][p0 + j]: the operand layout of lane (row p0 + j, k-slots of
 // group q).
-constexpr int x_row_stride(int P) { return P + 8; }
+constexpr int x_row_stride(int P) { return P + 16; }
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -355,7 +355,7 @@ __device__ __forceinline__ int col_tile_of(int wave, int k) {
 // a 16-key remainder and the diagonal tile through v_mfma_f32_16x16x16_bf16
 // (lane: keys 4q ..).
 //   s_h   bf16(h_{c-1})[p][n] (row stride N + 8): the inter-chunk operand
-//   s_xt  bf16 x[j][p]       (row stride P + 8), read transposed (xt_frag4/8)
+//   s_xt  bf16 x[j][p]       (row stride P + 16), read transposed (xt_frag4/8)
 //   s_d, s_cum, s_w: Delta, cum and the per-tile decay tables of the chunk
 // S (C B^T, bfloat16) and C come from global memory (L2: shared by all heads
 // of a group).  The S rows of every 32-key step a wavefront needs are
