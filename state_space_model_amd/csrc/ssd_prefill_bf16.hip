@@ -37,6 +37,7 @@
 // an 8 x 8 block (8 rows of 16 bytes) and writes it back as 8 columns of 16
 // bytes.
 #include "ssd_prefill_common.h"
+#include <type_traits>
 
 namespace ssd {
 namespace prefill {
@@ -1059,12 +1060,16 @@ struct StateSplit {
 };
 
 // Phased schedule, phase 1 for the chain shapes (chain_variant, L <= 256):
-// chunk summary states S_c, one workgroup of 8 wavefronts per (b, c, h), from
-// the pre-pass's B^T (k_cb_and_bt_bf16, which also forms C B^T).  Stored as
+// chunk summary states S_c from the pre-pass's B^T (k_cb_and_bt_bf16, which
+// also forms C B^T), one workgroup of 8 wavefronts per (b, c, g) and run of
+// `per` consecutive heads of group g.  The wavefront's B^T fragments are the
+// same for every head of the group and stay in registers; the next head's x
+// and dt are requested before the current head's products, so their latency
+// hides behind them (the last head, peeled, requests nothing).  Stored as
 // [p][n] to ws_state; exp(cum_last) to ws_alpha.
 template <int P, int N>
 __global__ __launch_bounds__(kOutThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void k_chunk_state_bf16(ScanArgs a) {
+void k_chunk_state_bf16(ScanArgs a, int per, int splits) {
   constexpr int LMAX = 256, NTH = kOutThreads;
   using SP = StateSplit<P, N>;
   __shared__ __attribute__((aligned(16))) float s_d[LMAX];
@@ -1074,33 +1079,57 @@ void k_chunk_state_bf16(ScanArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 s_xt[LMAX * x_row_stride(P)];
 
   const int tid = threadIdx.x;
+  const bool scan_thread = tid < kThreads;   // Delta and its prefix sum
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nt = wave % SP::TN, pt0 = (wave / SP::TN) * SP::TPW;
+  // the runs of one (b, c, g) are consecutive: they share an XCD and B^T in its L2
   const int64_t u = xcd_remap(blockIdx.x, gridDim.x);
-  const int64_t h = u % a.H, bc = u / a.H, c = bc % a.Nc, b = bc / a.Nc;
-  const int64_t g = h / (a.H / a.G);
+  const int64_t sp = u % splits, bcg = u / splits;
+  const int64_t g = bcg % a.G, bc = bcg / a.G, c = bc % a.Nc, b = bc / a.Nc;
+  const int64_t hpg = a.H / a.G;
+  const int64_t h_lo = g * hpg + sp * per;
+  const int64_t h_hi = min<int64_t>(h_lo + per, (g + 1) * hpg);
   const int Lc = chunk_len(a, c);
+  const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
 
-  // every global load is issued before the first wait: B^T, x, dt
+  // every global load of the first head is issued before the first wait
   bf16x8 bt[LMAX / 32];
   state_bt_load<N, LMAX>(a, b, c, g, nt, Lc, bt);
+  float2 dtv = scan_thread ? chunk_dt_load(a, b, c, h_lo) : make_float2(0.f, 0.f);
+  HeadConsts hc = head_consts(a, h_lo);
   XStage<P, LMAX, NTH> xs;
-  xs.load(a, b, c, h);
-  chunk_delta_cumsum_wide(a, b, c, h, s_d, s_cum, s_wsum);  // ends with a barrier
-  xs.store(s_xt);
-  state_weights<LMAX, NTH>(Lc, s_d, s_cum, s_ws);
-  if (tid == 0) a.ws_alpha[(b * a.H + h) * a.Nc + c] = fast_exp(s_cum[Lc - 1]);
-  __syncthreads();
+  xs.load(a, b, c, h_lo);
 
-  f32x4 t[SP::TPW];
-  state_tiles<P, LMAX, SP::TPW>(bt, pt0, Lc, s_xt, s_ws, t);
-  // lane holds S[n = 16 nt + 4q + r][p = 16 (pt0 + ip) + r16]: 4 consecutive n of one p
-  const int lane = tid & 63, q = lane >> 4, r16 = lane & 15;
-  float* out = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
+  auto head = [&](int64_t h, auto more) {
+    DeltaScan ds{};
+    if (scan_thread) ds = chunk_scan_stage1(a, c, hc, dtv, s_wsum);
+    __syncthreads();
+    if (scan_thread) chunk_scan_stage2(a, ds, s_wsum, s_d, s_cum);
+    __syncthreads();
+    xs.store(s_xt);
+    state_weights<LMAX, NTH>(Lc, s_d, s_cum, s_ws);
+    if (tid == 0) a.ws_alpha[(b * a.H + h) * a.Nc + c] = fast_exp(s_cum[Lc - 1]);
+    __syncthreads();
+    if constexpr (decltype(more)::value) {
+      // the next head's operands, behind this head's products
+      if (scan_thread) dtv = chunk_dt_load(a, b, c, h + 1);
+      hc = head_consts(a, h + 1);
+      xs.load(a, b, c, h + 1);
+    }
+    f32x4 t[SP::TPW];
+    state_tiles<P, LMAX, SP::TPW>(bt, pt0, Lc, s_xt, s_ws, t);
+    // lane holds S[n = 16 nt + 4q + r][p = 16 (pt0 + ip) + r16]: 4 consecutive n of one p
+    float* out = a.ws_state + ((b * a.H + h) * a.Nc + c) * (int64_t)(P * N);
 #pragma unroll
-  for (int ip = 0; ip < SP::TPW; ++ip)
-    st4(out + (16 * (pt0 + ip) + r16) * N + 16 * nt + 4 * q,
-        make_float4(t[ip][0], t[ip][1], t[ip][2], t[ip][3]));
+    for (int ip = 0; ip < SP::TPW; ++ip)
+      st4(out + (16 * (pt0 + ip) + r16) * N + 16 * nt + 4 * q,
+          make_float4(t[ip][0], t[ip][1], t[ip][2], t[ip][3]));
+    // s_d, s_cum and s_wsum are next written after the next head's stage-1
+    // barrier, s_xt and s_ws after its stage-2 one: every wavefront has left
+    // this head's products by then
+  };
+  for (int64_t h = h_lo; h + 1 < h_hi; ++h) head(h, std::true_type{});
+  head(h_hi - 1, std::false_type{});
 }
 
 // Chain kernel: one workgroup of 8 wavefronts per (b, h), chunks in order.
@@ -1238,6 +1267,28 @@ void k_chain_bf16(ScanArgs a) {
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
+// Heads per chunk-state workgroup.  The heads of a compute unit run one after
+// another whether they share a workgroup or not, so the unit with the most
+// heads sets the time: with `per` heads per workgroup and the workgroups dealt
+// round-robin over the 256 compute units, that is ceil(workgroups / 256) *
+// per heads.  The smallest such load wins, and of equal loads the longest
+// runs (B^T loaded once per run, each head's loads behind the previous head's
+// products): on the 2.7B shape (16 chunks x 80 heads) 5 heads per workgroup,
+// 256 workgroups, 32.5 -> 29 us against one head per workgroup.
+inline void state_runs(int64_t bcg, int64_t hpg, int& per, int& splits) {
+  constexpr int64_t kCUs = 256;
+  int64_t best = -1;
+  for (int64_t p = 1; p <= hpg; ++p) {
+    const int64_t sp = (hpg + p - 1) / p;
+    const int64_t load = (bcg * sp + kCUs - 1) / kCUs * p;
+    if (best < 0 || load <= best) {
+      best = load;
+      per = (int)p;
+      splits = (int)sp;
+    }
+  }
+}
+
 template <int P, int N>
 hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) {
   hipError_t e;
@@ -1249,8 +1300,10 @@ hipError_t launch_phased(const ScanArgs& a, hipStream_t stream, hipEvent_t* ev) 
     if ((e = launch_prepass<N>(a, stream)) != hipSuccess) return e;
     if ((e = rec(1)) != hipSuccess) return e;
     if constexpr (chain_variant(P, N)) {
-      hipLaunchKernelGGL((k_chunk_state_bf16<P, N>), dim3((unsigned)units), dim3(kOutThreads), 0,
-                         stream, a);
+      int per = 1, splits = 1;
+      state_runs(a.Bt * a.Nc * a.G, a.H / a.G, per, splits);
+      hipLaunchKernelGGL((k_chunk_state_bf16<P, N>), dim3((unsigned)(a.Bt * a.Nc * a.G * splits)),
+                         dim3(kOutThreads), 0, stream, a, per, splits);
     }
   } else {
     if ((e = rec(1)) != hipSuccess) return e;
