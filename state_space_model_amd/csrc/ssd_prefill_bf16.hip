@@ -452,19 +452,28 @@ struct ChunkOut {
   // Stores and loads share one in-order completion counter, so a store issued
   // ahead of a load makes every wait for that load wait for the store too:
   // each tile's store is issued after the next tile's loads, and the last
-  // one by the caller, after the loads it issues next.
+  // one by the caller, after the loads it issues next.  The stores are issued
+  // on every path, also by lanes with no row to store (rows past the chunk,
+  // or no tile run): a store issued on some paths only is counted as absent
+  // by the waits that follow it, so a wait for a load issued just before it
+  // would wait for the store too.  Those lanes write their meaningless values
+  // into the chunk's C B^T tile (0, L/16 - 1), strictly above the diagonal,
+  // which the scan never writes or reads (all of their stores to one place).
   __device__ __forceinline__ void store_pending() {
-    const int lane = lane_opaque(), q = lane >> 4;
-    if (yrow < Lc) {
-      bf16* yg = reinterpret_cast<bf16*>(a.y) + ((b * a.T + c * a.L) * a.H + h) * P;
-      const uint32_t rowy = (uint32_t)yrow * (uint32_t)(a.H * P) + 4 * q;
+    const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
+    const bool ok = yrow < Lc;
+    bf16* yg = reinterpret_cast<bf16*>(a.y) + ((b * a.T + c * a.L) * a.H + h) * P;
+    bf16* tg = reinterpret_cast<bf16*>(a.ws_cb) + ((b * a.Nc + c) * a.G + g) * a.L * a.L;
+    const uint32_t ry = (uint32_t)yrow * (uint32_t)(a.H * P) + 4 * q;
+    const uint32_t rt = (uint32_t)r16 * (uint32_t)a.L + (uint32_t)(a.L - 16) + 4 * q;
+    bf16* dst = ok ? off32(yg, ry) : off32(tg, rt);
+    const uint32_t step = ok ? 16u : 0u;
 #pragma unroll
-      for (int pt = 0; pt < TP; ++pt) {
-        bf16x4 o;
+    for (int pt = 0; pt < TP; ++pt) {
+      bf16x4 o;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = (bf16)yacc[pt][r];
-        st4b(off32(yg, rowy + 16 * pt), o);
-      }
+      for (int r = 0; r < 4; ++r) o[r] = (bf16)yacc[pt][r];
+      st4b(off32(dst, step * pt), o);
     }
   }
 
