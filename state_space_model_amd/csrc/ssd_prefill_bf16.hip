@@ -97,16 +97,24 @@ __device__ __forceinline__ bf16x4 lds_read_tr4(const bf16* p) {
       (__attribute__((address_space(3))) s16x4*)(const_cast<bf16*>(p)));
   return __builtin_bit_cast(bf16x4, v);
 }
-// x^T[p0 + j][t .. t+3] for lane j of its 16-lane group (t: the group's first token)
-template <int P>
-__device__ __forceinline__ bf16x4 xt_frag4(const bf16* s_x, int t, int p0, int lane) {
-  const int j = lane & 15;
-  return lds_read_tr4(s_x + (t + (j >> 2)) * x_row_stride(P) + p0 + 4 * (j & 3));
+// The lane's part of a transposed read: x[j / 4 + QM q][4 (j % 4)] for lane j
+// of 16-lane group q, whose first token is QM q past the fragment's.  Reads
+// then add only the fragment's uniform token and column offsets (immediate
+// offsets where those are compile-time constants).
+template <int P, int QM>
+__device__ __forceinline__ const bf16* xt_lane(const bf16* s_x, int lane) {
+  const int j = lane & 15, q = lane >> 4;
+  return s_x + ((j >> 2) + QM * q) * x_row_stride(P) + 4 * (j & 3);
 }
-// x^T[p0 + j][t .. t+7] (the 8 k-slots of a 32-deep operand)
+// x^T[p0 + j][t + QM q .. + 3] for lane j of group q (base from xt_lane)
 template <int P>
-__device__ __forceinline__ bf16x8 xt_frag8(const bf16* s_x, int t, int p0, int lane) {
-  const bf16x4 lo = xt_frag4<P>(s_x, t, p0, lane), hi = xt_frag4<P>(s_x, t + 4, p0, lane);
+__device__ __forceinline__ bf16x4 xt_at4(const bf16* base, int t, int p0) {
+  return lds_read_tr4(base + t * x_row_stride(P) + p0);
+}
+// x^T[p0 + j][t + QM q .. + 7] (the 8 k-slots of a 32-deep operand)
+template <int P>
+__device__ __forceinline__ bf16x8 xt_at8(const bf16* base, int t, int p0) {
+  const bf16x4 lo = xt_at4<P>(base, t, p0), hi = xt_at4<P>(base, t + 4, p0);
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 __device__ __forceinline__ void st4b(bf16* p, bf16x4 v) { *reinterpret_cast<bf16x4*>(p) = v; }
@@ -483,6 +491,8 @@ struct ChunkOut {
                                       const bf16* s_xt, const bf16* s_h) {
     const int lane = lane_opaque(), q = lane >> 4, r16 = lane & 15;
     const int wave = wave_id(), n_rt = nrt();
+    const bf16* xb8 = xt_lane<P, 8>(s_xt, lane);   // 32-key steps: 8 tokens per group
+    const bf16* xb4 = xt_lane<P, 4>(s_xt, lane);   // 16-key steps: 4 tokens per group
     yrow = Lc;   // nothing pending unless a tile runs
     // skip-term operands: D = d1 + d2 + d3 exactly (bfloat16 parts of the
     // float32 value and of its remainders), on the diagonal of a 16 x 16 block
@@ -541,13 +551,13 @@ struct ChunkOut {
 
       // ---- earlier key tiles: 32-key steps, then the odd 16-key one ----
       const float* wI = s_w + 8 * I * (I - 1);
+      const float* wq = wI + 8 * q;
       const int nfull = I >> 1;
 #pragma unroll
       for (int ks = 0; ks < NS; ++ks) {
         if (ks < nfull) {
           const bf16x8 st = sf[k == 0 ? ks : NS - 1 - ks];
-          const int k0 = 32 * ks + 8 * q;
-          const float4 w0 = ld4(wI + k0), w1 = ld4(wI + k0 + 4);
+          const float4 w0 = ld4(wq + 32 * ks), w1 = ld4(wq + 32 * ks + 4);
           bf16x8 m;
           m[0] = (bf16)__fmul_rn((float)st[0], w0.x);
           m[1] = (bf16)__fmul_rn((float)st[1], w0.y);
@@ -559,7 +569,7 @@ struct ChunkOut {
           m[7] = (bf16)__fmul_rn((float)st[7], w1.w);
 #pragma unroll
           for (int pt = 0; pt < TP; ++pt)
-            acc[pt] = mma(xt_frag8<P>(s_xt, 32 * ks + 8 * q, 16 * pt, lane), m, acc[pt]);
+            acc[pt] = mma(xt_at8<P>(xb8, 32 * ks, 16 * pt), m, acc[pt]);
         }
       }
       if (I & 1) {   // the key tile just before the diagonal one
@@ -573,7 +583,7 @@ struct ChunkOut {
         m[3] = (bf16)__fmul_rn((float)st[3], w.w);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt)
-          acc[pt] = mma16(xt_frag4<P>(s_xt, k0, 16 * pt, lane), m, acc[pt]);
+          acc[pt] = mma16(xt_at4<P>(xb4, 16 * (I - 1), 16 * pt), m, acc[pt]);
       }
       // decay from the reference token to the query
       const float cum_i = s_cum[ri];
@@ -609,7 +619,7 @@ struct ChunkOut {
         m[3] = dec(mk[3], (float)st[3], cj.w, dj.w);
 #pragma unroll
         for (int pt = 0; pt < TP; ++pt) {
-          const bf16x4 xd = xt_frag4<P>(s_xt, j0, 16 * pt, lane);
+          const bf16x4 xd = xt_at4<P>(xb4, 16 * I, 16 * pt);
           acc[pt] = mma16(xd, m, acc[pt]);
           // the skip term D x of the tile's own tokens, on the same x^T fragment
           acc[pt] = mma16(xd, e1, acc[pt]);
@@ -1043,17 +1053,18 @@ __device__ __forceinline__ void state_tiles(const bf16x8 (&bt)[LMAX / 32], int p
                                             f32x4 (&t)[TPW]) {
   constexpr int NKS = LMAX / 32;
   const int nks = (Lc + 31) / 32;
-  const int lane = opaque_tid() & 63, q = lane >> 4, r16 = lane & 15;
+  const int lane = opaque_tid() & 63, q = lane >> 4;
+  const bf16* xb8 = xt_lane<P, 8>(s_xt, lane);
+  const float* wq = s_ws + 8 * q;
 #pragma unroll
   for (int ip = 0; ip < TPW; ++ip) t[ip] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     if (ks < nks) {
-      const int l0 = 32 * ks + 8 * q;
-      const bf16x8 bw = scale8(bt[ks], ld4(&s_ws[l0]), ld4(&s_ws[l0 + 4]));
+      const bf16x8 bw = scale8(bt[ks], ld4(wq + 32 * ks), ld4(wq + 32 * ks + 4));
 #pragma unroll
       for (int ip = 0; ip < TPW; ++ip)
-        t[ip] = mma(bw, xt_frag8<P>(s_xt, l0, 16 * (pt0 + ip), lane), t[ip]);
+        t[ip] = mma(bw, xt_at8<P>(xb8, 32 * ks, 16 * (pt0 + ip)), t[ip]);
     }
   }
 }
