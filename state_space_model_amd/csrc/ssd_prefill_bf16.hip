@@ -364,7 +364,7 @@ __device__ __forceinline__ int col_tile_of(int wave, int k) {
 // a 16-key remainder and the diagonal tile through v_mfma_f32_16x16x16_bf16
 // (lane: keys 4q ..).
 //   s_h   bf16(h_{c-1})[p][n] (row stride N + 8): the inter-chunk operand
-//   s_xt  bf16 x[j][p]       (row stride P + 16), read transposed (xt_frag4/8)
+//   s_xt  bf16 x[j][p]       (row stride P + 16), read transposed (xt_at4/8)
 //   s_d, s_cum, s_w: Delta, cum and the per-tile decay tables of the chunk
 // S (C B^T, bfloat16) and C come from global memory (L2: shared by all heads
 // of a group).  The S rows of every 32-key step a wavefront needs are
