@@ -25,11 +25,18 @@ namespace {
 
 constexpr int kBatch = 16;
 
-template <bool BF16_OUT>
+// Every memory operation of a batch is issued on every path: the counter that
+// tracks loads and stores together is then counted exactly, and the wait for
+// chunk k's state waits for that load alone.  (With the stores of the last,
+// partial batch and of the optional float32 copy under runtime conditions,
+// the compiler counted them as absent and each step waited for the stores
+// before it as well.)  Whole batches first, the last Nc % 16 chunks one at
+// a time.
+template <bool BF16_OUT, bool KEEP_F32>
 __global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const float* ws_alpha,
                                                          bf16* ws_hb, const float* h0,
                                                          float* final_state, int64_t BH,
-                                                         int64_t Nc, int PN, int keep_f32) {
+                                                         int64_t Nc, int PN) {
   const int PN4 = PN / 4;
   const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (gid >= BH * PN4) return;
@@ -41,36 +48,34 @@ __global__ __launch_bounds__(kThreads) void k_state_pass(float* ws_state, const 
   const float* al = ws_alpha + bh * Nc;
   float4 hc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (h0) hc = reinterpret_cast<const float4*>(h0 + bh * PN)[e4];
-  for (int64_t c0 = 0; c0 < Nc; c0 += kBatch) {
-    const int n = (int)min<int64_t>(kBatch, Nc - c0);
-    // every load of the batch is issued unconditionally (indices clamped in range)
+  // h_{c-1} to chunk c's slots, then h_c = fma(alpha_c, h_{c-1}, S_c)
+  auto step = [&](int64_t c, float4 sc, float a) {
+    if constexpr (BF16_OUT) {
+      bf16x4 v;
+      v[0] = (bf16)hc.x; v[1] = (bf16)hc.y; v[2] = (bf16)hc.z; v[3] = (bf16)hc.w;
+      hb[c * PN4] = v;
+      if constexpr (KEEP_F32) st[c * PN4] = hc;   // S_c is already loaded
+    } else {
+      st[c * PN4] = hc;
+    }
+    hc.x = __fmaf_rn(a, hc.x, sc.x);
+    hc.y = __fmaf_rn(a, hc.y, sc.y);
+    hc.z = __fmaf_rn(a, hc.z, sc.z);
+    hc.w = __fmaf_rn(a, hc.w, sc.w);
+  };
+  int64_t c0 = 0;
+  for (; c0 + kBatch <= Nc; c0 += kBatch) {
     float4 s[kBatch];
     float al_c[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int64_t cc = min<int64_t>(c0 + k, Nc - 1);
-      s[k] = st[cc * PN4];
-      al_c[k] = al[cc];
+      s[k] = st[(c0 + k) * PN4];
+      al_c[k] = al[c0 + k];
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      if (k < n) {
-        if constexpr (BF16_OUT) {
-          bf16x4 v;
-          v[0] = (bf16)hc.x; v[1] = (bf16)hc.y; v[2] = (bf16)hc.z; v[3] = (bf16)hc.w;
-          hb[(c0 + k) * PN4] = v;
-          if (keep_f32) st[(c0 + k) * PN4] = hc;   // this batch's S_c are already loaded
-        } else {
-          st[(c0 + k) * PN4] = hc;
-        }
-        const float a = al_c[k];
-        hc.x = __fmaf_rn(a, hc.x, s[k].x);
-        hc.y = __fmaf_rn(a, hc.y, s[k].y);
-        hc.z = __fmaf_rn(a, hc.z, s[k].z);
-        hc.w = __fmaf_rn(a, hc.w, s[k].w);
-      }
-    }
+    for (int k = 0; k < kBatch; ++k) step(c0 + k, s[k], al_c[k]);
   }
+  for (; c0 < Nc; ++c0) step(c0, st[c0 * PN4], al[c0]);
   if (final_state) reinterpret_cast<float4*>(final_state + bh * PN)[e4] = hc;
 }
 
@@ -81,15 +86,18 @@ hipError_t launch_state_pass(const ScanArgs& a, int P, int N, hipStream_t stream
   const int PN = P * N;
   const int64_t threads = a.Bt * a.H * (PN / 4);
   const int64_t blocks = (threads + prefill::kThreads - 1) / prefill::kThreads;
-  if (bf16_out) {
-    hipLaunchKernelGGL(prefill::k_state_pass<true>, dim3((unsigned)blocks), dim3(prefill::kThreads),
-                       0, stream, a.ws_state, (const float*)a.ws_alpha,
-                       reinterpret_cast<bf16*>(a.ws_hb), a.h0, a.final_state, a.Bt * a.H, a.Nc,
-                       PN, a.keep_f32_states);
+  const dim3 grid((unsigned)blocks), block(prefill::kThreads);
+  const float* alpha = a.ws_alpha;
+  bf16* hb = reinterpret_cast<bf16*>(a.ws_hb);
+  if (bf16_out && a.keep_f32_states) {
+    hipLaunchKernelGGL((prefill::k_state_pass<true, true>), grid, block, 0, stream, a.ws_state,
+                       alpha, hb, a.h0, a.final_state, a.Bt * a.H, a.Nc, PN);
+  } else if (bf16_out) {
+    hipLaunchKernelGGL((prefill::k_state_pass<true, false>), grid, block, 0, stream, a.ws_state,
+                       alpha, hb, a.h0, a.final_state, a.Bt * a.H, a.Nc, PN);
   } else {
-    hipLaunchKernelGGL(prefill::k_state_pass<false>, dim3((unsigned)blocks),
-                       dim3(prefill::kThreads), 0, stream, a.ws_state, (const float*)a.ws_alpha,
-                       nullptr, a.h0, a.final_state, a.Bt * a.H, a.Nc, PN, 0);
+    hipLaunchKernelGGL((prefill::k_state_pass<false, false>), grid, block, 0, stream, a.ws_state,
+                       alpha, nullptr, a.h0, a.final_state, a.Bt * a.H, a.Nc, PN);
   }
   return hipGetLastError();
 }
