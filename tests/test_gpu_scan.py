@@ -47,6 +47,29 @@ def test_scan_workload_full(name):
     assert ey <= TOL[w.io_dtype] and ef <= TOL[w.io_dtype]
 
 
+# The phased bf16 chunk states run several heads per workgroup (the count
+# chosen from the number of chunks and heads); at 4097 tokens the last chunk
+# holds one token and the heads of a group split into runs of 6 with a
+# shorter last run, with one and with two groups (a run starting inside the
+# second group's heads).
+@pytest.mark.parametrize("G", [1, 2])
+def test_scan_phased_head_runs(G):
+    """2.7B-shaped bf16 prefill at 4097 tokens (phased: 80 chains), every
+    (b, h) sequence against the oracle."""
+    need_gpu()
+    import state_space_model_amd as ssd
+    w = make_tiny(1, 4097, 80, 64, 128, G, 256, "bf16", seed=5100 + G)
+    inp = make_inputs(w)
+    d = to_dev(inp)
+    assert ssd.ssd_chunk_scan_schedule(d["x"], d["B"], 256) == ssd.SSD_SCHEDULE_PHASED
+    announce(f"scan head runs 1x4097 H80 G{G} bf16")
+    y, fin = run_gpu(inp, w)
+    y_ref, f_ref = oracle_scan(inp, w)
+    ey, ef = y_err(y, y_ref), state_err(fin, f_ref)
+    print(f"head runs G={G}: y err {ey:.3e}  final-state err {ef:.3e}")
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"]
+
+
 def test_scan_long_batched_full():
     """1.3B-shaped batched long prefill (8 x 16384, H=64, bf16) at chunk
     128, 256 and 512, each run whole on the GPU in the benchmark's launch
