@@ -44,19 +44,25 @@ __device__ __forceinline__ void st_stream(float4* p, float4 v) {
 // spaces out the stores.  Measured at the 2.7B shape: exact waits took batch
 // 64 from 57.8 to 56.1 us and batch 1 from 4.74 to 4.28 us; at batch 16 the
 // spaced stores are faster (15.4 against 17.1 us).
-template <typename T, int THREADS, int BATCH, bool EXACT>
+//
+// PS workgroups share one (b, h) slice, each taking P / PS consecutive rows:
+// the rows are independent (row p needs x[p] and the whole of B and C), so the
+// split changes no arithmetic and every element is computed exactly as with
+// one workgroup per slice.
+template <typename T, int THREADS, int BATCH, bool EXACT, int PS = 1>
 __global__ __launch_bounds__(THREADS) void k_step(StepArgs a) {
-  const int64_t bh = blockIdx.x;
-  const int P = a.P, N = a.N, NQ = N / 4;
+  const int64_t bh = blockIdx.x / PS;
+  const int ps = (int)(blockIdx.x % PS);
+  const int P = a.P / PS, N = a.N, NQ = N / 4;   // P: rows of this workgroup
   const int nq_shift = __builtin_ctz(NQ);   // N / 4 is a power of two
   const int tid = threadIdx.x;
-  const int total = P * NQ;  // float4 elements of the slice, a multiple of 64
-  float4* st = reinterpret_cast<float4*>(a.state + bh * (int64_t)P * N);
+  const int total = P * NQ;  // float4 elements of the rows, a multiple of 64
+  float4* st = reinterpret_cast<float4*>(a.state + (bh * PS + ps) * (int64_t)P * N);
   const int64_t b = bh / a.H, h = bh % a.H, g = h / (a.H / a.G);
-  const T* xg = reinterpret_cast<const T*>(a.x) + bh * P;
+  const T* xg = reinterpret_cast<const T*>(a.x) + (bh * PS + ps) * P;
   const T* Bg = reinterpret_cast<const T*>(a.B) + (b * a.G + g) * N;
   const T* Cg = reinterpret_cast<const T*>(a.C) + (b * a.G + g) * N;
-  T* yg = reinterpret_cast<T*>(a.y) + bh * P;
+  T* yg = reinterpret_cast<T*>(a.y) + (bh * PS + ps) * P;
   // the n-quad of this lane is the same for every row it visits (NQ | THREADS)
   const int n4 = tid % NQ;
 
@@ -134,13 +140,17 @@ __global__ __launch_bounds__(kThreads) void k_copy_or_zero(float4* dst, const fl
 template <typename T>
 hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
   const int64_t slices = a.Bt * a.H;
-  // shapes measured at the 2.7B shape (P N = 8192): 512 x 4 at batch 64,
-  // 256 x 8 at batch 16, 1024 x 2 at batch 1 (80 slices: fewer, wider
-  // workgroups put more of the state in flight at once)
-  if (a.P * a.N >= 8192 && slices >= 2048) {
-    hipLaunchKernelGGL((k_step<T, 512, 4, true>), dim3((unsigned)slices), dim3(512), 0, stream, a);
-  } else if (a.P * a.N >= 8192 && slices < 512) {
-    hipLaunchKernelGGL((k_step<T, 1024, 2, true>), dim3((unsigned)slices), dim3(1024), 0, stream, a);
+  // Shapes measured at the 2.7B shape (P N = 8192, 1024 steps from one HIP
+  // graph).  Batch 1 (80 slices) and batch 64: each slice's rows split over
+  // four workgroups of 256 lanes, two vectors each (batch 1: 4.05 -> 3.54 us,
+  // more compute units streaming at once; batch 64: 56.6 -> 55.5 us).  Batch
+  // 16 (1280 slices): one workgroup of 256 lanes x 8 vectors per slice with
+  // spaced stores (16.0 us; every split or exact-wait shape tried was
+  // 16.2-18.8 us).  P N >= 8192 makes every split's rows a multiple of 64
+  // vectors and a whole number of 512-vector passes.
+  if (a.P * a.N >= 8192 && (slices >= 2048 || slices < 512)) {
+    hipLaunchKernelGGL((k_step<T, 256, 2, true, 4>), dim3((unsigned)(slices * 4)), dim3(256), 0,
+                       stream, a);
   } else {
     hipLaunchKernelGGL((k_step<T, 256, 8, false>), dim3((unsigned)slices), dim3(256), 0, stream, a);
   }
