@@ -31,6 +31,7 @@ STEP_CASES = [
     (4, 4, 64, 128, 1, "bf16"),
     (1, 6, 16, 16, 2, "bf16"),
     (2, 2, 128, 128, 1, "bf16"),
+    (32, 64, 128, 64, 2, "f32"),      # 2048 slices: the row-split shape of large batches
 ]
 
 
