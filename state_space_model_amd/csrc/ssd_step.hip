@@ -147,8 +147,10 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream) {
   // 16 (1280 slices): one workgroup of 256 lanes x 8 vectors per slice with
   // spaced stores (16.0 us; every split or exact-wait shape tried was
   // 16.2-18.8 us).  P N >= 8192 makes every split's rows a multiple of 64
-  // vectors and a whole number of 512-vector passes.
-  if (a.P * a.N >= 8192 && (slices >= 2048 || slices < 512)) {
+  // vectors and a whole number of 512-vector passes.  The split grid must
+  // also fit the 32-bit grid dimension (the whole-slice grid always does: the
+  // ABI refuses more than INT32_MAX slices).
+  if (a.P * a.N >= 8192 && (slices >= 2048 || slices < 512) && slices <= INT32_MAX / 4) {
     hipLaunchKernelGGL((k_step<T, 256, 2, true, 4>), dim3((unsigned)(slices * 4)), dim3(256), 0,
                        stream, a);
   } else {
