@@ -66,9 +66,9 @@ TRAFFIC = {
     ("chain/bf16", "m1p3_long_bf16"): (1566.49e6 + 1096.93e6, "a4525c742d855750"),
     ("chunk_out/bf16", "m2p7_bf16"): (67.05e6 + 41.94e6, "a4525c742d855750"),
     ("chunk_out/f32", "m130_f32"): (43.13e6 + 30.60e6, "a69d264b603eff81"),
-    ("decode", "m2p7_decode_b1"): (2.76e6 + 2.63e6, "94d91e67f09c7a75"),
-    ("decode", "m2p7_decode_b16"): (42.37e6 + 42.11e6, "94d91e67f09c7a75"),
-    ("decode", "m2p7_decode_b64"): (171.07e6 + 168.43e6, "94d91e67f09c7a75"),
+    ("decode", "m2p7_decode_b1"): (2.76e6 + 2.63e6, "f187b92f35e363d9"),
+    ("decode", "m2p7_decode_b16"): (42.37e6 + 42.11e6, "f187b92f35e363d9"),
+    ("decode", "m2p7_decode_b64"): (171.07e6 + 168.43e6, "f187b92f35e363d9"),
     ("conv1d", "conv_m2p7_bf16"): (49.20e6 + 44.07e6, "8b295ccdaccd2f32"),
     ("conv1d", "conv_m2p7_decode_b64"): (3.64e6 + 2.75e6, "8b295ccdaccd2f32"),
 }

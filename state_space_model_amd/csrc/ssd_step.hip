@@ -8,15 +8,15 @@
 //
 // Per (b, h):  d = clip(softplus(dt + dt_bias)),  alpha = exp(d A[h])
 //   h'[p,n] = alpha h[p,n] + d x[p] B[n];   y[p] = sum_n C[n] h'[p,n] + D[h] x[p]
-// One workgroup streams the (b, h) state slice: every lane moves 16-byte
-// vectors, a wavefront instruction covers 1 KB of contiguous state, each
-// element is read once and written once, and the row sums over n are reduced
-// across the N/4 lanes that hold one row.  The state is touched exactly once
+// A workgroup streams the (b, h) state slice, or a run of its rows: every
+// lane moves 16-byte vectors, a wavefront instruction covers 1 KB of
+// contiguous state, each element is read once and written once, and the row
+// sums over n are reduced across the N/4 lanes that hold one row.  The state is touched exactly once
 // per step, so its loads and stores are non-temporal (no cache allocation for
 // a stream that will not be re-read before it is evicted); this alone raised
 // the measured rate at batch 64 from 53% to 65% of the HBM peak.  The
-// workgroup shape (threads x vectors per lane) is chosen per batch size from
-// measurements (launch_step).
+// workgroup shape (threads x vectors per lane, workgroups per slice) is
+// chosen per batch size from measurements (launch_step).
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
